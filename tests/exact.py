@@ -1,0 +1,142 @@
+"""Exact-arithmetic brute force used to pin the oracle.
+
+Nothing here calls the oracle or the GPU library.  Values are carried as exact
+rationals (``fractions.Fraction``) and rounded to IEEE binary32 by an explicit
+round-to-nearest-even routine written from the format's definition, so a slip
+in the oracle's C code (a fused multiply-add, a wrong association, round-to-even
+instead of half-away, a dropped or transposed term) shows up as a mismatch.
+Only for tiny inputs: everything is pure Python.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import mpmath
+import numpy as np
+
+F32_MIN_EXP = -126          # exponent of the smallest normal binary32
+F32_MANT = 23               # fraction bits of binary32
+F32_MAX = Fraction((2 ** 24 - 1) * 2 ** (127 - 23))
+
+
+def f32_round(v: Fraction) -> float:
+    """Round an exact rational to binary32, nearest, ties to even."""
+    if v == 0:
+        return 0.0
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    # fix e so that 2^e <= a < 2^(e+1) exactly
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, F32_MIN_EXP) - F32_MANT)
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    r = fl * quantum
+    if r > F32_MAX:
+        return sign * math.inf
+    return float(sign * r)
+
+
+def fr(x) -> Fraction:
+    return Fraction(float(x))
+
+
+def f32(x) -> float:
+    """Check that x is a binary32 value and return it as a Python float."""
+    xf = float(np.float32(x))
+    assert xf == float(x)
+    return xf
+
+
+def half_away(v: Fraction) -> int:
+    """Round to the nearest integer, halves away from zero."""
+    a = abs(v)
+    n = math.floor(a + Fraction(1, 2))
+    return n if v >= 0 else -n
+
+
+def quantize_row(x) -> tuple[list[int], float]:
+    """Per-token quantisation by brute force: s = RN(amax / 127), q = clamp(half_away(RN(x / s)))."""
+    xs = [fr(v) for v in np.asarray(x, np.float32).tolist()]
+    amax = max((abs(v) for v in xs), default=Fraction(0))
+    s = f32_round(amax / 127)
+    if s == 0:
+        return [0] * len(xs), 0.0
+    q = []
+    for v in xs:
+        r = half_away(Fraction(f32_round(v / fr(s))))
+        q.append(max(-127, min(127, r)))
+    return q, s
+
+
+def epilogue(acc: int, ws, a_scale) -> float:
+    """RN( RN(acc) * RN(ws * as) ) evaluated exactly then rounded."""
+    c = f32_round(Fraction(acc))
+    sc = f32_round(fr(ws) * fr(a_scale))
+    return f32_round(fr(c) * fr(sc))
+
+
+def gemv(W, ws, q, a_scale) -> list[float]:
+    W = np.asarray(W, np.int64)
+    qv = np.asarray(q, np.int64)
+    acc = W @ qv
+    return [epilogue(int(acc[n]), ws[n], a_scale) for n in range(W.shape[0])]
+
+
+def stack_token(weights, scales, x) -> tuple[list[float], list[list[float]]]:
+    """One token through the stack, composed from the brute-force pieces.
+
+    Returns the final activation and, per layer, the seven projection outputs
+    concatenated (q, k, v, o, gate, up, down)."""
+    h = [float(v) for v in np.asarray(x, np.float32)]
+    per_layer = []
+    for wl, sl in zip(weights, scales):
+        a, sa = quantize_row(np.array(h, np.float32))
+        outs = [gemv(wl[j], sl[j], a, sa) for j in range(6)]
+        b, sb = quantize_row(np.array(outs[5], np.float32))
+        down = gemv(wl[6], sl[6], b, sb)
+        per_layer.append(sum(outs, []) + down)
+        h = down
+    return h, per_layer
+
+
+def seq_sum_products(w, x) -> float:
+    """acc = 0; for k ascending acc = RN(acc + RN(w_k * x_k))."""
+    acc = 0.0
+    for a, b in zip(w, x):
+        p = f32_round(fr(a) * fr(b))
+        acc = f32_round(fr(acc) + fr(p))
+    return acc
+
+
+def exp_cr(x: float) -> float:
+    """Correctly rounded binary32 exp via 80-digit mpmath then exact rounding."""
+    if x == -math.inf:
+        return 0.0
+    with mpmath.workdps(80):
+        y = mpmath.exp(mpmath.mpf(x))
+        # exact rational of the 80-digit value (its error is far below any
+        # binary32 rounding boundary distance for these inputs)
+        man, exp = mpmath.mpf(y).man_exp
+    v = Fraction(int(man)) * (Fraction(2) ** int(exp))
+    return f32_round(v)
+
+
+def softmax_topk(logits, k) -> tuple[list[int], list[float], list[float]]:
+    """Brute-force softmax + top-k: returns (ids, weights, all p)."""
+    ls = [float(v) for v in np.asarray(logits, np.float32)]
+    m = max(ls)
+    z = [exp_cr(f32_round(fr(v) - fr(m))) for v in ls]
+    S = 0.0
+    for v in z:
+        S = f32_round(fr(S) + fr(v))
+    p = [f32_round(fr(v) / fr(S)) for v in z]
+    order = sorted(range(len(p)), key=lambda e: (-p[e], e))[:k]
+    return order, [p[e] for e in order], p
