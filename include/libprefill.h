@@ -1,0 +1,192 @@
+/* libprefill.h — C ABI of the batched int8-weight prefill library (MI355X, gfx950).
+ *
+ * The problem (from the pages on the subject):
+ *   "Batched Prefill" (cellm), §The Problem and §The arithmetic: running a prompt
+ *   one token at a time performs one GEMV per token and re-reads every weight once
+ *   per prompt token, so prefill is bound by weight traffic.
+ *   Same page, §The Solution: run each linear projection as one int8 GEMM over a
+ *   chunk of tokens, quantising the chunk's activations once, so each weight byte
+ *   is read once per chunk and does chunk-many multiply-accumulates.
+ *   Same page, §Correctness: the batched result must equal the per-token result
+ *   byte for byte, and a runtime switch must select either path.
+ *   "Single-pass prefill" (SipLLM), "The fix": sweep every prompt position
+ *   through a layer while that layer's weights are loaded, layer after layer.
+ *   "Red Lite dev24", "What changed": mixture-of-experts prefill of a 512-token
+ *   chunk routes every token (softmax top-10), takes the union of the selected
+ *   experts and runs the experts on their token groups.
+ *
+ * Conventions (all entry points):
+ *   - Array arguments are DEVICE pointers owned by the caller, 16-byte aligned.
+ *     Host-side descriptors (pf_stack, pf_layer, pf_moe, pf_stack_stats) are
+ *     read during the call only.
+ *   - Layouts are row-major.  A weight W is [N][K] (K contiguous); activations
+ *     and outputs are token-major: x [M][K], y [M][N].
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream); results are ready once the stream is synchronised.  Device faults
+ *     surface at that synchronisation.
+ *   - Arguments are validated on the host before any device work is queued;
+ *     a rejected call returns a negative status and touches nothing.
+ *   - Outputs are fully overwritten, never accumulated into.
+ *   - The library allocates no device memory inside calls.  Calls that need
+ *     scratch memory take a caller-owned workspace whose size comes from the
+ *     matching *_workspace() query.  A workspace must be zero-filled once
+ *     before its first use (pf_workspace_clear, or any zero fill); each call
+ *     returns the parts that must start at zero (split-K accumulators and
+ *     their counters) to zero before it ends, so later calls need no clearing.
+ *     Calls that share one workspace must be ordered (same stream); calls that
+ *     overlap on one workspace race.
+ *   - Input activations must be finite; results for NaN or Inf inputs are
+ *     unspecified.
+ *   - K of every product must be a positive multiple of 64 and at most 131072,
+ *     which keeps every int32 accumulator exact (131072 * 127 * 127 < 2^31).
+ *
+ * Arithmetic (bit-exact with the plain per-token CPU definition):
+ *   quantise:  amax = max_k |x_k|; s = fl(amax / 127); q_k = clamp(roundf(fl(x_k / s)),
+ *              -127, 127) with roundf rounding halves away from zero; s = 0 -> q = 0.
+ *   product:   acc[t][n] = sum_k W[n][k] * q[t][k] in exact int32;
+ *              y[t][n] = fl( fl((float)acc) * fl(w_scale[n] * a_scale[t]) ).
+ */
+#ifndef LIBPREFILL_H
+#define LIBPREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int pf_status;
+#define PF_OK          0
+#define PF_EINVAL     -1  /* bad argument: null, size, alignment, overlap       */
+#define PF_ENODEV     -2  /* no HIP device, or the current device is not gfx950 */
+#define PF_ELAUNCH    -3  /* a HIP launch or runtime call failed                 */
+#define PF_EWORKSPACE -4  /* workspace missing or smaller than required          */
+#define PF_EINTERNAL  -5  /* unexpected internal error                           */
+
+/* Human-readable name of a status code (static string). */
+const char* pf_status_string(pf_status status);
+
+/* Checks that a gfx950 device is current.  Every entry point calls it on first
+ * use; calling it first only moves the cost.  PF_ENODEV without a device. */
+pf_status pf_init(void);
+
+/* Zero-fills `bytes` of workspace on `stream` (a fill kernel, no memset node). */
+pf_status pf_workspace_clear(void* workspace, size_t bytes, void* stream);
+
+/* Per-token symmetric int8 quantisation of a chunk, done once per chunk
+ * ("Batched Prefill", §The Solution, "quantize activations once per batch").
+ * x [M][ldx] f32 (first K of each row used) -> xq [M][K] int8, a_scale [M] f32.
+ * M = 0 is a no-op.  ldx >= K, ldx % 4 == 0. */
+pf_status pf_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx,
+                          int8_t* xq, float* a_scale, void* stream);
+
+/* Workspace bytes pf_gemm_i8_chunk may use to split K across workgroups
+ * (0 is always accepted; a larger workspace only adds parallelism). */
+size_t pf_gemm_i8_chunk_workspace(int64_t N, int64_t K, int64_t M);
+
+/* One projection over a chunk of M tokens ("Batched Prefill", §The Solution:
+ * each weight row is loaded once and dotted against every token column).
+ * W [N][K] int8, w_scale [N] f32, xq [M][K] int8, a_scale [M] f32 -> y [M][N]
+ * f32 (token-major).  Chooses an MFMA kernel by M (skinny M <= 64, tiled above).
+ * workspace may be NULL with ws_bytes 0. */
+pf_status pf_gemm_i8_chunk(const int8_t* W, const float* w_scale, int64_t N, int64_t K,
+                           const int8_t* xq, const float* a_scale, int64_t M, float* y,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* The per-token baseline ("Batched Prefill", §The Problem: one GEMV per token,
+ * every weight re-read per token): y [N] = product of W with one token xq [K]. */
+pf_status pf_gemv_i8(const int8_t* W, const float* w_scale, int64_t N, int64_t K,
+                     const int8_t* xq, const float* a_scale, float* y, void* stream);
+
+/* Projection set of one layer, in this order: q, k, v, o, gate, up, down.
+ * Shapes: q, k, v, o [H][H]; gate, up [F][H]; down [H][F]; w_scale[j] has one
+ * f32 per weight row. */
+#define PF_NPROJ 7
+typedef struct {
+    const int8_t* W[PF_NPROJ];
+    const float* w_scale[PF_NPROJ];
+} pf_layer;
+
+typedef struct {
+    int64_t n_layers;
+    int64_t hidden;          /* H */
+    int64_t ffn;             /* F */
+    const pf_layer* layers;  /* host array of n_layers */
+} pf_stack;
+
+typedef struct {
+    int64_t chunks;          /* chunks processed (the last may be ragged)       */
+    int64_t tail_tokens;     /* tokens in the last chunk                       */
+    int64_t launches;        /* kernel launches queued                         */
+    double alg_bytes;        /* weight + scale + activation bytes, algorithmic  */
+    double elapsed_ms;       /* device time between first and last launch      */
+    int per_token_mode;      /* 1 if the per-token GEMV path ran                */
+} pf_stack_stats;
+
+/* Workspace bytes for pf_prefill_stack with this stack and chunk size. */
+size_t pf_prefill_stack_workspace(const pf_stack* stack, int64_t chunk);
+
+/* Sweeps a prompt of P tokens through every layer's projection set, one chunk
+ * of `chunk` tokens at a time, the last chunk ragged ("Single-pass prefill",
+ * "The fix"; "Batched Prefill", §The Solution).  Per chunk and layer, with h the
+ * layer input (x for layer 0):
+ *   (a, sa) = quantise(h); q, k, v, o, gate, up = products with a;
+ *   (b, sb) = quantise(up); down = product with b; the next layer's h = down.
+ * x [P][H] f32 -> y [P][H] f32 (the last layer's down).  proj, when not NULL,
+ * receives every projection output: proj [L][P][5H + 2F] f32, each row holding
+ * q, k, v, o, gate, up, down concatenated.  With the environment variable
+ * PF_BATCHED_PREFILL=0 the same call runs one GEMV per token and projection
+ * instead (the per-token baseline); the bytes of y and proj are identical
+ * ("Batched Prefill", §Correctness).  stats, when not NULL, is filled in and the
+ * call then synchronises the stream. */
+pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int64_t chunk,
+                           float* y, float* proj, void* workspace, size_t ws_bytes,
+                           pf_stack_stats* stats, void* stream);
+
+/* Mixture-of-experts layer ("Red Lite dev24", What changed):
+ *   W_router [E][H] f32; W_gate, W_up [E][I][H] int8; W_down [E][H][I] int8;
+ *   s_gate, s_up [E][I] f32; s_down [E][H] f32. */
+typedef struct {
+    int64_t n_experts;   /* E */
+    int64_t top_k;       /* experts per token */
+    int64_t hidden;      /* H */
+    int64_t inter;       /* I */
+    const float* W_router;
+    const int8_t* W_gate;
+    const int8_t* W_up;
+    const int8_t* W_down;
+    const float* s_gate;
+    const float* s_up;
+    const float* s_down;
+} pf_moe;
+
+/* Workspace bytes for pf_moe_chunk with T tokens. */
+size_t pf_moe_chunk_workspace(const pf_moe* moe, int64_t T);
+
+/* Expert prefill of one chunk of T tokens x [T][H] f32, all on the device:
+ *   logits[t][e] = sum over k ascending of fl(W_router[e][k] * x[t][k]) (f32,
+ *     each product and sum rounded on its own);
+ *   p = softmax(logits[t]) with correctly rounded expf, normaliser summed in
+ *     ascending e; ids[t] = the top_k experts by descending p, ties to the lower
+ *     id; weights[t][j] = p[ids[t][j]] (not renormalised);
+ *   tokens are grouped by expert (the union of selected experts, tokens in
+ *     ascending order within an expert) and each expert runs as int8 products
+ *     over its group: g = gate(xq), u = up(xq), r = fl(g * u), (hq, hs) =
+ *     quantise(r) per (token, expert) row, y_e = down(hq);
+ *   out[t] = +0 then, over the selected experts in ascending id,
+ *     out[t][j] = fl(out[t][j] + fl(weights_e * y_e[j])).
+ * ids [T][top_k] int32, weights [T][top_k] f32, out [T][H] f32.
+ * Limits: T * top_k <= 65536, E <= 1024, top_k <= 32, E * ceil(T / 32) <= 12288. */
+pf_status pf_moe_chunk(const pf_moe* moe, const float* x, int64_t T, int32_t* ids,
+                       float* weights, float* out, void* workspace, size_t ws_bytes,
+                       void* stream);
+
+/* The correctly rounded binary32 exp used by the softmax above, applied
+ * elementwise to x [n] -> y [n] (exposed so that it can be checked). */
+pf_status pf_expf_cr(const float* x, int64_t n, float* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

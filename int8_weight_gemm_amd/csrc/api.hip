@@ -1,0 +1,610 @@
+// api.hip — the C ABI of libprefill (include/libprefill.h): argument checks,
+// workspace carving, kernel choice and launch order.  No device memory is
+// allocated here; every call queues work on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/libprefill.h"
+#include "kernels.hpp"
+
+using namespace pf;
+
+namespace {
+
+constexpr int64_t kMaxK = 131072;
+constexpr size_t kAlign = 256;
+constexpr int kTargetWorkgroups = 512;   // two per compute unit
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, -1 other.
+std::atomic<int> g_arch[64];
+
+pf_status check_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return PF_ENODEV;
+    }
+    int v = g_arch[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return PF_ENODEV;
+        }
+        v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        g_arch[dev].store(v, std::memory_order_relaxed);
+    }
+    return v == 1 ? PF_OK : PF_ENODEV;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+bool valid_k(int64_t K) { return K > 0 && K % 64 == 0 && K <= kMaxK; }
+
+pf_status launched(hipError_t e)
+{
+    if (e == hipSuccess) return PF_OK;
+    (void)hipGetLastError();
+    return PF_ELAUNCH;
+}
+
+// ---------------------------------------------------------------------------
+// Split plan of the skinny product: 64-row bands x K slices, enough
+// workgroups to cover the chip twice, every slice at least 4 k-blocks long.
+struct SkinnyPlan {
+    int tiles_n, splits, kb_per_split;
+};
+
+SkinnyPlan plan_skinny(int64_t N, int64_t K, int64_t total_bands)
+{
+    SkinnyPlan p;
+    p.tiles_n = (int)((N + 63) / 64);
+    const int nkb = (int)(K / 64);
+    int s = 1;
+    while (total_bands * s * 2 <= kTargetWorkgroups && nkb / (s * 2) >= 4) s *= 2;
+    p.kb_per_split = (nkb + s - 1) / s;
+    p.splits = (nkb + p.kb_per_split - 1) / p.kb_per_split;
+    return p;
+}
+
+size_t split_bytes(int64_t N, int64_t M, const SkinnyPlan& p)
+{
+    if (p.splits <= 1) return 0;
+    return round_up((size_t)M * (size_t)N * 4, kAlign) + round_up((size_t)p.tiles_n * 4, kAlign);
+}
+
+int token_blocks(int64_t M) { return (int)((M + 15) / 16); }
+
+// Fills a skinny problem.  With a split plan its int32 accumulator ([m_alloc][N],
+// m_alloc >= M) and counters are carved from `scratch`, which then advances.
+void make_skinny(GemmProb& g, const int8_t* W, const float* ws, int64_t N, int64_t K,
+                 const int8_t* X, int64_t ldx, const float* xs, int64_t M, float* Y, int64_t ldy,
+                 const SkinnyPlan& p, char*& scratch, int64_t m_alloc)
+{
+    std::memset(&g, 0, sizeof(g));
+    g.W = W; g.ws = ws; g.X = X; g.xs = xs; g.Y = Y;
+    g.ldx = ldx; g.ldy = ldy;
+    g.N = (int)N; g.K = (int)K; g.M = (int)M;
+    g.tiles_n = p.tiles_n; g.tiles_m = 1;
+    g.splits = p.splits; g.kb_per_split = p.kb_per_split;
+    if (p.splits > 1) {
+        g.acc = reinterpret_cast<int*>(scratch);
+        scratch += round_up((size_t)m_alloc * (size_t)N * 4, kAlign);
+        g.cnt = reinterpret_cast<unsigned*>(scratch);
+        scratch += round_up((size_t)p.tiles_n * 4, kAlign);
+    }
+}
+
+void make_tiled(GemmProb& g, const int8_t* W, const float* ws, int64_t N, int64_t K,
+                const int8_t* X, int64_t ldx, const float* xs, int64_t M, float* Y, int64_t ldy)
+{
+    std::memset(&g, 0, sizeof(g));
+    g.W = W; g.ws = ws; g.X = X; g.xs = xs; g.Y = Y;
+    g.ldx = ldx; g.ldy = ldy;
+    g.N = (int)N; g.K = (int)K; g.M = (int)M;
+    g.tiles_n = (int)((N + 127) / 128);
+    g.tiles_m = (int)((M + 127) / 128);
+    g.splits = 1; g.kb_per_split = (int)(K / 64);
+}
+
+void finish_set(GemmSet& set, int kind)  // kind 0 gemv, 1 skinny, 2 tiled
+{
+    int begin = 0;
+    for (int i = 0; i < set.nprob; ++i) {
+        GemmProb& g = set.p[i];
+        g.tile_begin = begin;
+        if (kind == 0) begin += (g.N + 15) / 16;
+        else if (kind == 1) begin += g.tiles_n * g.splits;
+        else begin += g.tiles_n * g.tiles_m;
+    }
+    set.total_tiles = begin;
+}
+
+// Runs a set of products that share M (skinny for M <= 64, tiled above).
+pf_status run_products(GemmSet& set, int64_t M, hipStream_t s)
+{
+    if (M <= 64) {
+        finish_set(set, 1);
+        return launched(launch_gemm_skinny(set, token_blocks(M), s));
+    }
+    finish_set(set, 2);
+    return launched(launch_gemm_tiled(set, s));
+}
+
+// ---------------------------------------------------------------------------
+// Stack workspace layout (per chunk): quantised input a [chunk][H], quantised
+// up b [chunk][F], their scales, the projection rows [chunk][5H+2F] when the
+// caller keeps none, and the split-K scratch of the seven products.
+struct StackLayout {
+    size_t a, b, sa, sb, proj, split, total;
+    SkinnyPlan plan[PF_NPROJ];
+};
+
+StackLayout stack_layout(int64_t H, int64_t F, int64_t chunk)
+{
+    StackLayout L{};
+    size_t o = 0;
+    L.a = o; o += round_up((size_t)chunk * H, kAlign);
+    L.b = o; o += round_up((size_t)chunk * F, kAlign);
+    L.sa = o; o += round_up((size_t)chunk * 4, kAlign);
+    L.sb = o; o += round_up((size_t)chunk * 4, kAlign);
+    L.proj = o; o += round_up((size_t)chunk * (5 * H + 2 * F) * 4, kAlign);
+    L.split = o;
+    const int64_t rows[PF_NPROJ] = {H, H, H, H, F, F, H};
+    int64_t bands_a = 0;
+    for (int j = 0; j < 6; ++j) bands_a += (rows[j] + 63) / 64;
+    size_t split = 0;
+    if (chunk <= 64) {
+        for (int j = 0; j < PF_NPROJ; ++j) {
+            const int64_t K = j < 6 ? H : F;
+            L.plan[j] = plan_skinny(rows[j], K, j < 6 ? bands_a : (H + 63) / 64);
+            split += split_bytes(rows[j], chunk, L.plan[j]);
+        }
+    }
+    L.total = o + split;
+    return L;
+}
+
+pf_status validate_stack(const pf_stack* st)
+{
+    if (!st || !st->layers || st->n_layers <= 0 || st->hidden <= 0 || st->ffn <= 0)
+        return PF_EINVAL;
+    if (!valid_k(st->hidden) || !valid_k(st->ffn)) return PF_EINVAL;
+    for (int64_t l = 0; l < st->n_layers; ++l)
+        for (int j = 0; j < PF_NPROJ; ++j) {
+            const pf_layer& ly = st->layers[l];
+            if (!ly.W[j] || !ly.w_scale[j] || !aligned16(ly.W[j]) || !aligned16(ly.w_scale[j]))
+                return PF_EINVAL;
+        }
+    return PF_OK;
+}
+
+bool per_token_mode()
+{
+    const char* v = std::getenv("PF_BATCHED_PREFILL");
+    return v && v[0] == '0' && v[1] == '\0';
+}
+
+// ---------------------------------------------------------------------------
+// MoE workspace layout.
+struct MoeLayout {
+    size_t xq, xs, logits, off, pair_tok, comb_row, comb_w, r, hq, hs, ypair, total;
+};
+
+MoeLayout moe_layout(const pf_moe* m, int64_t T)
+{
+    MoeLayout L{};
+    const size_t P = (size_t)T * m->top_k;
+    size_t o = 0;
+    L.xq = o; o += round_up((size_t)T * m->hidden, kAlign);
+    L.xs = o; o += round_up((size_t)T * 4, kAlign);
+    L.logits = o; o += round_up((size_t)T * m->n_experts * 4, kAlign);
+    L.off = o; o += round_up((size_t)(m->n_experts + 1) * 4, kAlign);
+    L.pair_tok = o; o += round_up(P * 4, kAlign);
+    L.comb_row = o; o += round_up(P * 4, kAlign);
+    L.comb_w = o; o += round_up(P * 4, kAlign);
+    L.r = o; o += round_up(P * m->inter * 4, kAlign);
+    L.hq = o; o += round_up(P * m->inter, kAlign);
+    L.hs = o; o += round_up(P * 4, kAlign);
+    L.ypair = o; o += round_up(P * m->hidden * 4, kAlign);
+    L.total = o;
+    return L;
+}
+
+pf_status validate_moe(const pf_moe* m)
+{
+    if (!m) return PF_EINVAL;
+    if (m->n_experts <= 0 || m->n_experts > 1024 || m->top_k <= 0 || m->top_k > 32 ||
+        m->top_k > m->n_experts)
+        return PF_EINVAL;
+    if (!valid_k(m->hidden) || !valid_k(m->inter)) return PF_EINVAL;
+    const void* ptrs[] = {m->W_router, m->W_gate, m->W_up, m->W_down, m->s_gate, m->s_up, m->s_down};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return PF_EINVAL;
+    return PF_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+extern "C" {
+
+const char* pf_status_string(pf_status s)
+{
+    switch (s) {
+        case PF_OK: return "PF_OK";
+        case PF_EINVAL: return "PF_EINVAL: invalid argument";
+        case PF_ENODEV: return "PF_ENODEV: no gfx950 device is current";
+        case PF_ELAUNCH: return "PF_ELAUNCH: a HIP launch failed";
+        case PF_EWORKSPACE: return "PF_EWORKSPACE: workspace missing or too small";
+        case PF_EINTERNAL: return "PF_EINTERNAL: internal error";
+        default: return "unknown pf_status";
+    }
+}
+
+pf_status pf_init(void)
+{
+    try {
+        return check_device();
+    } catch (...) {
+        return PF_EINTERNAL;
+    }
+}
+
+pf_status pf_workspace_clear(void* workspace, size_t bytes, void* stream)
+{
+    try {
+        if (bytes == 0) return PF_OK;
+        if (!workspace || !aligned16(workspace)) return PF_EINVAL;
+        if (pf_status st = check_device()) return st;
+        return launched(launch_fill_zero(workspace, bytes, (hipStream_t)stream));
+    } catch (...) {
+        return PF_EINTERNAL;
+    }
+}
+
+pf_status pf_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* xq,
+                          float* a_scale, void* stream)
+{
+    try {
+        if (M < 0 || K <= 0 || K % 4 != 0 || ldx < K || ldx % 4 != 0 || M > INT32_MAX)
+            return PF_EINVAL;
+        if (M == 0) return PF_OK;
+        if (!x || !xq || !a_scale || !aligned16(x) || !aligned16(xq) || !aligned16(a_scale))
+            return PF_EINVAL;
+        const size_t xb = (size_t)((M - 1) * ldx + K) * 4;
+        if (overlap(x, xb, xq, (size_t)M * K) || overlap(x, xb, a_scale, (size_t)M * 4) ||
+            overlap(xq, (size_t)M * K, a_scale, (size_t)M * 4))
+            return PF_EINVAL;
+        if (pf_status st = check_device()) return st;
+        return launched(launch_quantize(x, ldx, (int)M, (int)K, xq, a_scale, (hipStream_t)stream));
+    } catch (...) {
+        return PF_EINTERNAL;
+    }
+}
+
+size_t pf_gemm_i8_chunk_workspace(int64_t N, int64_t K, int64_t M)
+{
+    if (N <= 0 || !valid_k(K) || M <= 0 || M > 64) return 0;
+    const SkinnyPlan p = plan_skinny(N, K, (N + 63) / 64);
+    return split_bytes(N, M, p);
+}
+
+pf_status pf_gemm_i8_chunk(const int8_t* W, const float* w_scale, int64_t N, int64_t K,
+                           const int8_t* xq, const float* a_scale, int64_t M, float* y,
+                           void* workspace, size_t ws_bytes, void* stream)
+{
+    try {
+        if (N <= 0 || N > INT32_MAX || !valid_k(K) || M < 0 || M > INT32_MAX) return PF_EINVAL;
+        if (M == 0) return PF_OK;
+        if (!W || !w_scale || !xq || !a_scale || !y) return PF_EINVAL;
+        if (!aligned16(W) || !aligned16(w_scale) || !aligned16(xq) || !aligned16(a_scale) ||
+            !aligned16(y))
+            return PF_EINVAL;
+        const size_t yb = (size_t)M * N * 4;
+        if (overlap(y, yb, W, (size_t)N * K) || overlap(y, yb, w_scale, (size_t)N * 4) ||
+            overlap(y, yb, xq, (size_t)M * K) || overlap(y, yb, a_scale, (size_t)M * 4))
+            return PF_EINVAL;
+        if (workspace && !aligned16(workspace)) return PF_EINVAL;
+        if (pf_status st = check_device()) return st;
+        GemmSet set;
+        std::memset(&set, 0, sizeof(set));
+        set.nprob = 1;
+        if (M <= 64) {
+            SkinnyPlan p = plan_skinny(N, K, (N + 63) / 64);
+            if (!workspace || ws_bytes < split_bytes(N, M, p)) {
+                p.splits = 1;
+                p.kb_per_split = (int)(K / 64);
+            }
+            if (workspace && overlap(workspace, ws_bytes, y, yb)) return PF_EINVAL;
+            char* scratch = static_cast<char*>(workspace);
+            make_skinny(set.p[0], W, w_scale, N, K, xq, K, a_scale, M, y, N, p, scratch, M);
+        } else {
+            make_tiled(set.p[0], W, w_scale, N, K, xq, K, a_scale, M, y, N);
+        }
+        return run_products(set, M, (hipStream_t)stream);
+    } catch (...) {
+        return PF_EINTERNAL;
+    }
+}
+
+pf_status pf_gemv_i8(const int8_t* W, const float* w_scale, int64_t N, int64_t K,
+                     const int8_t* xq, const float* a_scale, float* y, void* stream)
+{
+    try {
+        if (N <= 0 || N > INT32_MAX || !valid_k(K)) return PF_EINVAL;
+        if (!W || !w_scale || !xq || !a_scale || !y) return PF_EINVAL;
+        if (!aligned16(W) || !aligned16(w_scale) || !aligned16(xq) || !aligned16(a_scale) ||
+            !aligned16(y))
+            return PF_EINVAL;
+        const size_t yb = (size_t)N * 4;
+        if (overlap(y, yb, W, (size_t)N * K) || overlap(y, yb, w_scale, yb) ||
+            overlap(y, yb, xq, (size_t)K) || overlap(y, yb, a_scale, 4))
+            return PF_EINVAL;
+        if (pf_status st = check_device()) return st;
+        GemmSet set;
+        std::memset(&set, 0, sizeof(set));
+        set.nprob = 1;
+        char* none = nullptr;
+        const SkinnyPlan p{(int)((N + 63) / 64), 1, (int)(K / 64)};
+        make_skinny(set.p[0], W, w_scale, N, K, xq, K, a_scale, 1, y, N, p, none, 1);
+        finish_set(set, 0);
+        return launched(launch_gemv(set, (hipStream_t)stream));
+    } catch (...) {
+        return PF_EINTERNAL;
+    }
+}
+
+size_t pf_prefill_stack_workspace(const pf_stack* stack, int64_t chunk)
+{
+    if (!stack || stack->hidden <= 0 || stack->ffn <= 0 || chunk <= 0) return 0;
+    return stack_layout(stack->hidden, stack->ffn, chunk).total;
+}
+
+pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int64_t chunk,
+                           float* y, float* proj, void* workspace, size_t ws_bytes,
+                           pf_stack_stats* stats, void* stream)
+{
+    try {
+        if (pf_status st = validate_stack(stack)) return st;
+        if (P < 0 || chunk <= 0 || chunk > INT32_MAX || P > INT32_MAX) return PF_EINVAL;
+        const int64_t L = stack->n_layers, H = stack->hidden, F = stack->ffn;
+        const int64_t NT = 5 * H + 2 * F;
+        if (P == 0) {
+            if (stats) std::memset(stats, 0, sizeof(*stats));
+            return PF_OK;
+        }
+        if (!x || !y || !aligned16(x) || !aligned16(y) || (proj && !aligned16(proj)))
+            return PF_EINVAL;
+        const size_t xb = (size_t)P * H * 4, pb = proj ? (size_t)L * P * NT * 4 : 0;
+        if (overlap(x, xb, y, xb) || overlap(proj, pb, x, xb) || overlap(proj, pb, y, xb))
+            return PF_EINVAL;
+        const int64_t ch = std::min(chunk, P);
+        const StackLayout lay = stack_layout(H, F, ch);
+        if (!workspace || ws_bytes < lay.total) return PF_EWORKSPACE;
+        if (!aligned16(workspace)) return PF_EINVAL;
+        if (overlap(workspace, ws_bytes, x, xb) || overlap(workspace, ws_bytes, y, xb) ||
+            overlap(workspace, ws_bytes, proj, pb))
+            return PF_EINVAL;
+        if (pf_status st = check_device()) return st;
+        hipStream_t s = (hipStream_t)stream;
+        char* ws = static_cast<char*>(workspace);
+        int8_t* a = reinterpret_cast<int8_t*>(ws + lay.a);
+        int8_t* b = reinterpret_cast<int8_t*>(ws + lay.b);
+        float* sa = reinterpret_cast<float*>(ws + lay.sa);
+        float* sb = reinterpret_cast<float*>(ws + lay.sb);
+        float* pscratch = reinterpret_cast<float*>(ws + lay.proj);
+        const int64_t rows[PF_NPROJ] = {H, H, H, H, F, F, H};
+        int64_t offs[PF_NPROJ + 1] = {0};
+        for (int j = 0; j < PF_NPROJ; ++j) offs[j + 1] = offs[j] + rows[j];
+        const bool per_token = per_token_mode();
+
+        hipEvent_t ev0 = nullptr, ev1 = nullptr;
+        if (stats) {
+            if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess)
+                return PF_ELAUNCH;
+            if (hipEventRecord(ev0, s) != hipSuccess) return PF_ELAUNCH;
+        }
+        int64_t launches = 0;
+        double alg = 0.0;
+        pf_status st = PF_OK;
+        const int64_t step = per_token ? 1 : ch;
+        for (int64_t c0 = 0; c0 < P && st == PF_OK; c0 += step) {
+            const int64_t M = std::min(step, P - c0);
+            for (int64_t l = 0; l < L && st == PF_OK; ++l) {
+                const pf_layer& ly = stack->layers[l];
+                float* prow = proj ? proj + ((size_t)l * P + c0) * NT : pscratch;
+                // input of this layer: x for layer 0, else the previous down output
+                const float* hin;
+                int64_t ldh;
+                if (l == 0) {
+                    hin = x + c0 * H;
+                    ldh = H;
+                } else {
+                    hin = (proj ? proj + ((size_t)(l - 1) * P + c0) * NT : pscratch) + offs[6];
+                    ldh = NT;
+                }
+                st = launched(launch_quantize(hin, ldh, (int)M, (int)H, a, sa, s));
+                ++launches;
+                alg += (double)M * H * 4 + (double)M * H + M * 4.0;
+                if (st) break;
+                GemmSet set;
+                std::memset(&set, 0, sizeof(set));
+                set.nprob = 6;
+                char* scratch = ws + lay.split;
+                for (int j = 0; j < 6; ++j) {
+                    SkinnyPlan p = lay.plan[j];
+                    if (per_token) p = SkinnyPlan{(int)((rows[j] + 63) / 64), 1, (int)(H / 64)};
+                    if (per_token || M <= 64) {
+                        make_skinny(set.p[j], ly.W[j], ly.w_scale[j], rows[j], H, a, H, sa, M,
+                                    prow + offs[j], NT, p, scratch, ch);
+                    } else {
+                        make_tiled(set.p[j], ly.W[j], ly.w_scale[j], rows[j], H, a, H, sa, M,
+                                   prow + offs[j], NT);
+                    }
+                    alg += (double)rows[j] * H + rows[j] * 4.0 + (double)M * H + (double)M * rows[j] * 4;
+                }
+                if (per_token) {
+                    finish_set(set, 0);
+                    st = launched(launch_gemv(set, s));
+                } else {
+                    st = run_products(set, M, s);
+                }
+                ++launches;
+                if (st) break;
+                st = launched(launch_quantize(prow + offs[5], NT, (int)M, (int)F, b, sb, s));
+                ++launches;
+                alg += (double)M * F * 4 + (double)M * F + M * 4.0;
+                if (st) break;
+                GemmSet dn;
+                std::memset(&dn, 0, sizeof(dn));
+                dn.nprob = 1;
+                SkinnyPlan p = lay.plan[6];
+                if (per_token) p = SkinnyPlan{(int)((H + 63) / 64), 1, (int)(F / 64)};
+                if (per_token || M <= 64)
+                    make_skinny(dn.p[0], ly.W[6], ly.w_scale[6], H, F, b, F, sb, M, prow + offs[6], NT,
+                                p, scratch, ch);
+                else
+                    make_tiled(dn.p[0], ly.W[6], ly.w_scale[6], H, F, b, F, sb, M, prow + offs[6], NT);
+                if (l == L - 1) {
+                    dn.p[0].Y2 = y + c0 * H;
+                    dn.p[0].ldy2 = H;
+                }
+                alg += (double)H * F + H * 4.0 + (double)M * F + (double)M * H * 4;
+                if (per_token) {
+                    finish_set(dn, 0);
+                    st = launched(launch_gemv(dn, s));
+                } else {
+                    st = run_products(dn, M, s);
+                }
+                ++launches;
+            }
+        }
+        if (st != PF_OK) {
+            if (ev0) (void)hipEventDestroy(ev0);
+            if (ev1) (void)hipEventDestroy(ev1);
+            return st;
+        }
+        if (stats) {
+            std::memset(stats, 0, sizeof(*stats));
+            float ms = 0.0f;
+            if (hipEventRecord(ev1, s) != hipSuccess || hipEventSynchronize(ev1) != hipSuccess ||
+                hipEventElapsedTime(&ms, ev0, ev1) != hipSuccess)
+                st = PF_ELAUNCH;
+            (void)hipEventDestroy(ev0);
+            (void)hipEventDestroy(ev1);
+            stats->chunks = per_token ? P : (P + ch - 1) / ch;
+            stats->tail_tokens = per_token ? 1 : P - (stats->chunks - 1) * ch;
+            stats->launches = launches;
+            stats->alg_bytes = alg;
+            stats->elapsed_ms = ms;
+            stats->per_token_mode = per_token ? 1 : 0;
+        }
+        return st;
+    } catch (...) {
+        return PF_EINTERNAL;
+    }
+}
+
+size_t pf_moe_chunk_workspace(const pf_moe* moe, int64_t T)
+{
+    if (validate_moe(moe) != PF_OK || T <= 0) return 0;
+    return moe_layout(moe, T).total;
+}
+
+pf_status pf_moe_chunk(const pf_moe* moe, const float* x, int64_t T, int32_t* ids,
+                       float* weights, float* out, void* workspace, size_t ws_bytes,
+                       void* stream)
+{
+    try {
+        if (pf_status st = validate_moe(moe)) return st;
+        if (T < 0 || T * moe->top_k > 65536) return PF_EINVAL;
+        if (T == 0) return PF_OK;
+        const int64_t E = moe->n_experts, k = moe->top_k, H = moe->hidden, I = moe->inter;
+        if ((size_t)E * ((T + 31) / 32) > 12288) return PF_EINVAL;   // grouping bitmap in LDS
+        if (!x || !ids || !weights || !out) return PF_EINVAL;
+        if (!aligned16(x) || !aligned16(ids) || !aligned16(weights) || !aligned16(out))
+            return PF_EINVAL;
+        const size_t xb = (size_t)T * H * 4, ib = (size_t)T * k * 4;
+        if (overlap(x, xb, out, xb) || overlap(ids, ib, weights, ib) || overlap(ids, ib, out, xb) ||
+            overlap(weights, ib, out, xb) || overlap(x, xb, ids, ib) || overlap(x, xb, weights, ib))
+            return PF_EINVAL;
+        const MoeLayout lay = moe_layout(moe, T);
+        if (!workspace || ws_bytes < lay.total) return PF_EWORKSPACE;
+        if (!aligned16(workspace)) return PF_EINVAL;
+        if (overlap(workspace, ws_bytes, x, xb) || overlap(workspace, ws_bytes, out, xb) ||
+            overlap(workspace, ws_bytes, ids, ib) || overlap(workspace, ws_bytes, weights, ib))
+            return PF_EINVAL;
+        if (pf_status st = check_device()) return st;
+        hipStream_t s = (hipStream_t)stream;
+        char* ws = static_cast<char*>(workspace);
+        int8_t* xq = reinterpret_cast<int8_t*>(ws + lay.xq);
+        float* xs = reinterpret_cast<float*>(ws + lay.xs);
+        float* logits = reinterpret_cast<float*>(ws + lay.logits);
+        int* off = reinterpret_cast<int*>(ws + lay.off);
+        int* pair_tok = reinterpret_cast<int*>(ws + lay.pair_tok);
+        int* comb_row = reinterpret_cast<int*>(ws + lay.comb_row);
+        float* comb_w = reinterpret_cast<float*>(ws + lay.comb_w);
+        float* r = reinterpret_cast<float*>(ws + lay.r);
+        int8_t* hq = reinterpret_cast<int8_t*>(ws + lay.hq);
+        float* hs = reinterpret_cast<float*>(ws + lay.hs);
+        float* ypair = reinterpret_cast<float*>(ws + lay.ypair);
+        const int Ti = (int)T, Ei = (int)E, ki = (int)k;
+
+        pf_status st = launched(launch_quantize(x, H, Ti, (int)H, xq, xs, s));
+        if (!st) st = launched(launch_router(moe->W_router, x, Ei, (int)H, Ti, logits, s));
+        if (!st) st = launched(launch_softmax_topk(logits, Ei, Ti, ki, ids, weights, s));
+        if (!st) st = launched(launch_group(ids, weights, Ti, ki, Ei, off, pair_tok, comb_row, comb_w, s));
+        if (st) return st;
+        ExpertArgs gu;
+        std::memset(&gu, 0, sizeof(gu));
+        gu.W0 = moe->W_gate; gu.W1 = moe->W_up; gu.s0 = moe->s_gate; gu.s1 = moe->s_up;
+        gu.off = off; gu.gather = pair_tok; gu.X = xq; gu.xs = xs; gu.Y = r;
+        gu.ldx = H; gu.ldy = I; gu.N = (int)I; gu.K = (int)H; gu.E = Ei;
+        gu.tiles_n = (int)((I + 63) / 64);
+        st = launched(launch_expert(gu, s));
+        if (!st) st = launched(launch_quantize(r, I, Ti * ki, (int)I, hq, hs, s));
+        if (st) return st;
+        ExpertArgs dn;
+        std::memset(&dn, 0, sizeof(dn));
+        dn.W0 = moe->W_down; dn.s0 = moe->s_down;
+        dn.off = off; dn.gather = nullptr; dn.X = hq; dn.xs = hs; dn.Y = ypair;
+        dn.ldx = I; dn.ldy = H; dn.N = (int)H; dn.K = (int)I; dn.E = Ei;
+        dn.tiles_n = (int)((H + 63) / 64);
+        st = launched(launch_expert(dn, s));
+        if (!st) st = launched(launch_combine(ypair, comb_row, comb_w, Ti, ki, (int)H, out, s));
+        return st;
+    } catch (...) {
+        return PF_EINTERNAL;
+    }
+}
+
+pf_status pf_expf_cr(const float* x, int64_t n, float* y, void* stream)
+{
+    try {
+        if (n < 0) return PF_EINVAL;
+        if (n == 0) return PF_OK;
+        if (!x || !y || !aligned16(x) || !aligned16(y)) return PF_EINVAL;
+        if (overlap(x, (size_t)n * 4, y, (size_t)n * 4) && x != y) return PF_EINVAL;
+        if (pf_status st = check_device()) return st;
+        return launched(launch_expf(x, n, y, (hipStream_t)stream));
+    } catch (...) {
+        return PF_EINTERNAL;
+    }
+}
+
+}  // extern "C"

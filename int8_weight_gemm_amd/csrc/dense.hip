@@ -1,0 +1,382 @@
+// dense.hip — quantiser, per-token GEMV and the two MFMA products (gfx950).
+//
+// "Batched Prefill" (cellm), §The Solution: a weight row is loaded once and
+// dotted against every token of the chunk; activations are quantised once per
+// chunk; work is split over weight rows so that every weight byte is read once.
+// Here a workgroup owns a band of weight rows, streams them from HBM with
+// 128-bit loads straight into the MFMA operand registers, and takes the chunk's
+// quantised tokens from LDS, where they are staged once per workgroup.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace pf {
+
+// ---------------------------------------------------------------------------
+// Zero fill (workspace clearing without memset nodes).
+__global__ __launch_bounds__(256) void k_fill_zero(v4i* p, size_t n16, int8_t* tail, int ntail)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        p[i] = v4i{0, 0, 0, 0};
+    if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s)
+{
+    if (bytes == 0) return hipSuccess;
+    const size_t n16 = bytes / 16;
+    const int ntail = (int)(bytes - n16 * 16);
+    size_t blocks = (n16 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks == 0) blocks = 1;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<v4i*>(p), n16, reinterpret_cast<int8_t*>(p) + n16 * 16,
+                       ntail);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-token quantisation: one workgroup per token row.  amax is an exact
+// maximum (order-free); the scale and every code follow the per-token
+// definition bit for bit.
+__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x, int64_t ldx, int K,
+                                                  int8_t* __restrict__ q, float* __restrict__ scale)
+{
+    const int t = blockIdx.x;
+    const float4* row = reinterpret_cast<const float4*>(x + (int64_t)t * ldx);
+    int* qrow = reinterpret_cast<int*>(q + (int64_t)t * K);
+    const int n4 = K >> 2;
+    float amax = 0.0f;
+    for (int i = threadIdx.x; i < n4; i += 256) {
+        const float4 v = row[i];
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    amax = wave_max(amax);
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = amax / 127.0f;
+    if (threadIdx.x == 0) scale[t] = s;
+    for (int i = threadIdx.x; i < n4; i += 256) {
+        int packed = 0;
+        if (s != 0.0f) {
+            const float4 v = row[i];
+            packed = (quant_code(v.x, s) & 0xff) | ((quant_code(v.y, s) & 0xff) << 8) |
+                     ((quant_code(v.z, s) & 0xff) << 16) | ((quant_code(v.w, s) & 0xff) << 24);
+        }
+        qrow[i] = packed;
+    }
+}
+
+hipError_t launch_quantize(const float* x, int64_t ldx, int M, int K, int8_t* q, float* scale,
+                           hipStream_t s)
+{
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_quantize, dim3(M), dim3(256), 0, s, x, ldx, K, q, scale);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Problem lookup inside a grouped launch.  Static indices only, so the
+// descriptors stay in scalar registers.
+__device__ __forceinline__ GemmProb find_prob(const GemmSet& set, int bid)
+{
+    GemmProb P = set.p[0];
+#pragma unroll
+    for (int j = 1; j < kMaxProbs; ++j)
+        if (j < set.nprob && bid >= set.p[j].tile_begin) P = set.p[j];
+    return P;
+}
+
+__device__ __forceinline__ void store_out(const GemmProb& P, int t, int n, float v)
+{
+    P.Y[(int64_t)t * P.ldy + n] = v;
+    if (P.Y2) P.Y2[(int64_t)t * P.ldy2 + n] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Per-token GEMV (M = 1): one wave per 4 weight rows; each lane streams 16-byte
+// pieces of the rows, multiplies with v_dot4_i32_i8 and the wave reduces the
+// int32 sums.  The token's 16-byte pieces are re-read from L1/L2 per row group.
+constexpr int kGemvRows = 4;
+
+__global__ __launch_bounds__(256) void k_gemv(GemmSet set)
+{
+    const GemmProb P = find_prob(set, blockIdx.x);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nbase = ((blockIdx.x - P.tile_begin) * 4 + wave) * kGemvRows;
+    const int nchunks = P.K >> 4;
+    const int8_t* wrow[kGemvRows];
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) {
+        const int n = min(nbase + r, P.N - 1);
+        wrow[r] = P.W + (int64_t)n * P.K;
+    }
+    int acc[kGemvRows] = {0, 0, 0, 0};
+#pragma unroll 4
+    for (int c = lane; c < nchunks; c += 64) {
+        const v4i qv = ld16(P.X + c * 16);
+#pragma unroll
+        for (int r = 0; r < kGemvRows; ++r) {
+            const v4i wv = ld16(wrow[r] + c * 16);
+            acc[r] = __builtin_amdgcn_sdot4(wv.x, qv.x, acc[r], false);
+            acc[r] = __builtin_amdgcn_sdot4(wv.y, qv.y, acc[r], false);
+            acc[r] = __builtin_amdgcn_sdot4(wv.z, qv.z, acc[r], false);
+            acc[r] = __builtin_amdgcn_sdot4(wv.w, qv.w, acc[r], false);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) acc[r] = wave_sum(acc[r]);
+    if (lane == 0) {
+        const float xs = P.xs[0];
+#pragma unroll
+        for (int r = 0; r < kGemvRows; ++r) {
+            const int n = nbase + r;
+            if (n < P.N) store_out(P, 0, n, epilogue(acc[r], P.ws[n], xs));
+        }
+    }
+}
+
+hipError_t launch_gemv(const GemmSet& set, hipStream_t s)
+{
+    if (set.total_tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_gemv, dim3(set.total_tiles), dim3(256), 0, s, set);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Skinny product (M <= 64): v_mfma_i32_16x16x64_i8 with the weights as the A
+// operand (16 rows x 64 k per wave and instruction) and the tokens as B.
+// Workgroup = 4 waves = 64 weight rows x one K slice; the chunk's tokens for the
+// slice are staged in LDS in pieces of kSkPiece k-blocks and read by all 4 waves.
+// Each lane loads its A operand (16 bytes of one row) straight from HBM; the
+// four lanes l, l+16, l+32, l+48 cover 64 contiguous bytes of a row.
+// The int32 sum is order-free, so any K split gives the per-token bytes; split
+// partial sums meet in an int32 accumulator (agent-scope atomics) and the last
+// workgroup of a row band applies the epilogue and re-zeroes the accumulator.
+constexpr int kSkPiece = 16;                       // k-blocks (of 64 bytes) per LDS piece
+constexpr int kSkStride = kSkPiece * 64 + 16;      // LDS bytes per token row (padded)
+
+template <int TB>
+__global__ __launch_bounds__(256) void k_gemm_skinny(GemmSet set)
+{
+    __shared__ __attribute__((aligned(16))) int8_t xl[16 * TB * kSkStride];
+    __shared__ int s_last;
+    const GemmProb P = find_prob(set, blockIdx.x);
+    const int local = blockIdx.x - P.tile_begin;
+    const int split = local % P.splits;
+    const int tn = local / P.splits;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nw0 = tn * 64 + wave * 16;
+    const int nkb = P.K >> 6;
+    const int kb0 = split * P.kb_per_split;
+    const int kb1 = min(kb0 + P.kb_per_split, nkb);
+    const int arow = min(nw0 + (lane & 15), P.N - 1);
+    const int8_t* wp = P.W + (int64_t)arow * P.K + ((lane >> 4) << 4);
+    const int boff = (lane & 15) * kSkStride + ((lane >> 4) << 4);
+
+    v4i acc[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[tb] = v4i{0, 0, 0, 0};
+
+    for (int kp = kb0; kp < kb1; kp += kSkPiece) {
+        const int npc = min(kSkPiece, kb1 - kp);
+        v4i a[kSkPiece];
+#pragma unroll
+        for (int i = 0; i < kSkPiece; ++i)
+            if (i < npc) a[i] = ld16(wp + (int64_t)(kp + i) * 64);
+        __syncthreads();
+        const int cpr = npc * 4;
+        for (int idx = threadIdx.x; idx < 16 * TB * cpr; idx += 256) {
+            const int t = idx / cpr, c = idx - t * cpr;
+            v4i v = v4i{0, 0, 0, 0};
+            if (t < P.M) v = ld16(P.X + (int64_t)t * P.ldx + (int64_t)kp * 64 + c * 16);
+            st16(xl + t * kSkStride + c * 16, v);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSkPiece; ++i) {
+            if (i < npc) {
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const v4i b = *reinterpret_cast<const v4i*>(xl + tb * 16 * kSkStride + boff + i * 64);
+                    acc[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b, acc[tb], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // Lane l holds rows nw0 + 4*(l/16) + r (r = 0..3) of token column l%16.
+    const int nr = nw0 + ((lane >> 4) << 2);
+    if (P.splits == 1) {
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const int t = tb * 16 + (lane & 15);
+            if (t < P.M) {
+                const float xs = P.xs[t];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (nr + r < P.N) store_out(P, t, nr + r, epilogue(acc[tb][r], P.ws[nr + r], xs));
+            }
+        }
+        return;
+    }
+
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        const int t = tb * 16 + (lane & 15);
+        if (t < P.M) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (nr + r < P.N) atomic_add_agent(P.acc + (int64_t)t * P.N + nr + r, acc[tb][r]);
+        }
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned old = __hip_atomic_fetch_add(P.cnt + tn, 1u, __ATOMIC_ACQ_REL,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old == (unsigned)(P.splits - 1));
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    const int rows = min(64, P.N - tn * 64);
+    for (int idx = threadIdx.x; idx < P.M * 64; idx += 256) {
+        const int t = idx >> 6, n = tn * 64 + (idx & 63);
+        if ((idx & 63) < rows) {
+            int* pa = P.acc + (int64_t)t * P.N + n;
+            const int v = load_agent(pa);
+            store_out(P, t, n, epilogue(v, P.ws[n], P.xs[t]));
+            store_agent(pa, 0);
+        }
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(P.cnt + tn, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t s)
+{
+    if (set.total_tiles <= 0) return hipSuccess;
+    const dim3 g(set.total_tiles), b(256);
+    switch (token_blocks) {
+        case 1: hipLaunchKernelGGL(k_gemm_skinny<1>, g, b, 0, s, set); break;
+        case 2: hipLaunchKernelGGL(k_gemm_skinny<2>, g, b, 0, s, set); break;
+        case 3: hipLaunchKernelGGL(k_gemm_skinny<3>, g, b, 0, s, set); break;
+        case 4: hipLaunchKernelGGL(k_gemm_skinny<4>, g, b, 0, s, set); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Tiled product (M > 64): 128 weight rows x 128 tokens per workgroup, k-blocks of
+// 64 bytes double-buffered through LDS, v_mfma_i32_32x32x32_i8 with 2 x 2 tiles of
+// 32 x 32 per wave (waves arranged 2 x 2 over the 128 x 128 tile).
+constexpr int kTlStride = 80;                      // LDS bytes per row (64 + 16 pad)
+constexpr int kTlRows = 128;
+
+__global__ __launch_bounds__(256) void k_gemm_tiled(GemmSet set)
+{
+    __shared__ __attribute__((aligned(16))) int8_t sw[2][kTlRows * kTlStride];
+    __shared__ __attribute__((aligned(16))) int8_t sx[2][kTlRows * kTlStride];
+    const GemmProb P = find_prob(set, blockIdx.x);
+    const int local = blockIdx.x - P.tile_begin;
+    const int tm = local % P.tiles_m;
+    const int tn = local / P.tiles_m;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = tn * kTlRows, t0 = tm * kTlRows;
+    const int nkb = P.K >> 6;
+
+    // global -> register mapping: rows lr and lr + 64, 16-byte column lc
+    const int lr = tid >> 2, lc = (tid & 3) << 4;
+    const int8_t* wsrc[2];
+    const int8_t* xsrc[2];
+    bool xok[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int n = min(n0 + lr + 64 * h, P.N - 1);
+        wsrc[h] = P.W + (int64_t)n * P.K + lc;
+        const int t = t0 + lr + 64 * h;
+        xok[h] = t < P.M;
+        xsrc[h] = P.X + (int64_t)(xok[h] ? t : 0) * P.ldx + lc;
+    }
+    v4i rw[2], rx[2];
+    auto gload = [&](int kb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            rw[h] = ld16(wsrc[h] + (int64_t)kb * 64);
+            rx[h] = xok[h] ? ld16(xsrc[h] + (int64_t)kb * 64) : v4i{0, 0, 0, 0};
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            st16(&sw[buf][(lr + 64 * h) * kTlStride + lc], rw[h]);
+            st16(&sx[buf][(lr + 64 * h) * kTlStride + lc], rx[h]);
+        }
+    };
+
+    const int wn = (wave >> 1) * 64, wm = (wave & 1) * 64;
+    v16i acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int buf = kb & 1;
+        if (kb + 1 < nkb) gload(kb + 1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int col = ks * 32 + ((lane >> 5) << 4);
+            v4i a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = *reinterpret_cast<const v4i*>(&sw[buf][(wn + 32 * i + (lane & 31)) * kTlStride + col]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[j] = *reinterpret_cast<const v4i*>(&sx[buf][(wm + 32 * j + (lane & 31)) * kTlStride + col]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        if (kb + 1 < nkb) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Lane l, register r of a 32x32 tile: row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int t = t0 + wm + 32 * j + (lane & 31);
+            if (t >= P.M) continue;
+            const float xs = P.xs[t];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nb = n0 + wn + 32 * i + 8 * g + ((lane >> 5) << 2);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (nb + r < P.N) store_out(P, t, nb + r, epilogue(acc[i][j][4 * g + r], P.ws[nb + r], xs));
+            }
+        }
+    }
+}
+
+hipError_t launch_gemm_tiled(const GemmSet& set, hipStream_t s)
+{
+    if (set.total_tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_gemm_tiled, dim3(set.total_tiles), dim3(256), 0, s, set);
+    return hipGetLastError();
+}
+
+}  // namespace pf

@@ -1,0 +1,79 @@
+// kernels.hpp — kernel argument blocks and host-side launch wrappers of libprefill.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pf {
+
+// One int8 product y[t][n] = epilogue(sum_k W[n][k] * X[t][k]) of a grouped launch.
+struct GemmProb {
+    const int8_t* W;      // [N][K]
+    const float* ws;      // [N]
+    const int8_t* X;      // [M][ldx]
+    const float* xs;      // [M]
+    float* Y;             // [M][ldy]
+    float* Y2;            // optional second copy of the output [M][ldy2] (or null)
+    int* acc;             // split-K int32 accumulator [M][N], zero between calls (or null)
+    unsigned* cnt;        // split-K arrival counters [tiles_n], zero between calls (or null)
+    int64_t ldx;          // bytes between token rows of X
+    int64_t ldy;          // floats between token rows of Y
+    int64_t ldy2;         // floats between token rows of Y2
+    int N, K, M;
+    int tiles_n;          // row tiles
+    int tiles_m;          // token tiles (tiled kernel only)
+    int splits;           // K splits (skinny kernel only)
+    int kb_per_split;     // 64-byte k-blocks per split
+    int tile_begin;       // first flat workgroup index of this problem
+};
+
+constexpr int kMaxProbs = 8;
+struct GemmSet {
+    GemmProb p[kMaxProbs];
+    int nprob;
+    int total_tiles;
+};
+
+// Expert-grouped product: expert e multiplies its W_e with the rows of its token
+// group (rows off[e] .. off[e+1] of the pair list).
+struct ExpertArgs {
+    const int8_t* W0;     // [E][N][K]
+    const int8_t* W1;     // second weight with the same shape (gate/up pair) or null
+    const float* s0;      // [E][N]
+    const float* s1;      // [E][N] or null
+    const int* off;       // [E+1] pair offsets per expert
+    const int* gather;    // pair -> X row (token) or null: X row = pair index
+    const int8_t* X;      // [rows][ldx]
+    const float* xs;      // per X row
+    float* Y;             // [pairs][ldy]
+    int64_t ldx, ldy;
+    int N, K, E;
+    int tiles_n;
+};
+
+// Host launch wrappers (return a hipError_t of the launch).
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_quantize(const float* x, int64_t ldx, int M, int K, int8_t* q, float* scale,
+                           hipStream_t s);
+hipError_t launch_quantize_mul(const float* a, const float* b, int64_t ld, int M, int K,
+                               int8_t* q, float* scale, hipStream_t s);
+hipError_t launch_gemv(const GemmSet& set, hipStream_t s);
+hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t s);
+hipError_t launch_gemm_tiled(const GemmSet& set, hipStream_t s);
+
+hipError_t launch_router(const float* Wr, const float* x, int E, int H, int T, float* logits,
+                         hipStream_t s);
+hipError_t launch_softmax_topk(const float* logits, int E, int T, int k, int* ids, float* w,
+                               hipStream_t s);
+hipError_t launch_group(const int* ids, const float* w, int T, int k, int E, int* off,
+                        int* pair_tok, int* comb_row, float* comb_w, hipStream_t s);
+hipError_t launch_expert(const ExpertArgs& a, hipStream_t s);
+hipError_t launch_combine(const float* ypair, const int* comb_row, const float* comb_w, int T,
+                          int k, int H, float* out, hipStream_t s);
+hipError_t launch_expf(const float* x, int64_t n, float* y, hipStream_t s);
+
+// Sizes of the grouping kernel's shared bitmap.
+inline size_t group_lds_bytes(int T, int E) { return (size_t)E * ((T + 31) / 32) * 4; }
+
+}  // namespace pf

@@ -1,0 +1,451 @@
+// moe.hip — expert prefill of one chunk on the device ("Red Lite dev24",
+// What changed: route every token of the chunk, take the union of the selected
+// experts, run each expert once over its token group).
+//
+// Router -> softmax/top-k -> grouping -> gate/up product (with r = g * u fused in
+// the epilogue) -> per-row quantisation -> down product -> weighted combine.
+// No host round trip: the expert plan stays in device memory.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace pf {
+
+// ---------------------------------------------------------------------------
+// Router logits: l[t][e] = sum over k ascending of fl(Wr[e][k] * x[t][k]), each
+// product and each partial sum rounded on its own (no fused multiply-add: the
+// library is compiled with -ffp-contract=off).  32 tokens x 32 experts per
+// workgroup, 64-wide k pieces staged in LDS, 4 independent chains per thread.
+constexpr int kRtTile = 32;
+constexpr int kRtK = 64;
+
+__global__ __launch_bounds__(256) void k_router(const float* __restrict__ Wr,
+                                                const float* __restrict__ x, int E, int H, int T,
+                                                float* __restrict__ logits)
+{
+    __shared__ float sx[kRtTile][kRtK + 1];
+    __shared__ float sw[kRtTile][kRtK + 1];
+    const int e0 = blockIdx.x * kRtTile, t0 = blockIdx.y * kRtTile;
+    const int ti = threadIdx.x >> 4, ei = threadIdx.x & 15;
+    float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+    for (int k0 = 0; k0 < H; k0 += kRtK) {
+        for (int idx = threadIdx.x; idx < kRtTile * kRtK; idx += 256) {
+            const int r = idx / kRtK, c = idx % kRtK;
+            const int t = t0 + r, e = e0 + r;
+            sx[r][c] = t < T ? x[(int64_t)t * H + k0 + c] : 0.0f;
+            sw[r][c] = e < E ? Wr[(int64_t)e * H + k0 + c] : 0.0f;
+        }
+        __syncthreads();
+        for (int kk = 0; kk < kRtK; ++kk) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float p = sw[ei + 16 * j][kk] * sx[ti + 16 * i][kk];
+                    acc[i][j] = acc[i][j] + p;
+                }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int t = t0 + ti + 16 * i, e = e0 + ei + 16 * j;
+            if (t < T && e < E) logits[(int64_t)t * E + e] = acc[i][j];
+        }
+}
+
+hipError_t launch_router(const float* Wr, const float* x, int E, int H, int T, float* logits,
+                         hipStream_t s)
+{
+    if (T <= 0) return hipSuccess;
+    dim3 g((E + kRtTile - 1) / kRtTile, (T + kRtTile - 1) / kRtTile);
+    hipLaunchKernelGGL(k_router, g, dim3(256), 0, s, Wr, x, E, H, T, logits);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Correctly rounded binary32 exp.  exp(x) is evaluated in double-double
+// arithmetic (about 95 correct bits after the squarings below), far more than
+// the roughly 24 + 40 bits that any binary32 argument needs to decide its
+// rounding, and the double-double value is then rounded to binary32 exactly.
+//   x = k ln2 + r, |r| <= ln2/2 (k = rint(x / ln2); k ln2 in double-double);
+//   s = r / 2^10;  e^s - 1 by its Taylor series to s^10 (|s| < 3.4e-4);
+//   (1 + m)^(2^10) by ten squarings m <- 2m + m^2;  e^x = 2^k (1 + m).
+struct dd {
+    double hi, lo;
+};
+
+__device__ __forceinline__ dd two_sum(double a, double b)
+{
+    const double s = a + b;
+    const double bb = s - a;
+    const double e = (a - (s - bb)) + (b - bb);
+    return {s, e};
+}
+__device__ __forceinline__ dd fast_two_sum(double a, double b)
+{
+    const double s = a + b;
+    const double e = b - (s - a);
+    return {s, e};
+}
+__device__ __forceinline__ dd two_prod(double a, double b)
+{
+    const double p = a * b;
+    const double e = fma(a, b, -p);
+    return {p, e};
+}
+__device__ __forceinline__ dd dd_add(dd a, dd b)
+{
+    dd s = two_sum(a.hi, b.hi);
+    const dd t = two_sum(a.lo, b.lo);
+    s.lo = s.lo + t.hi;
+    s = fast_two_sum(s.hi, s.lo);
+    s.lo = s.lo + t.lo;
+    return fast_two_sum(s.hi, s.lo);
+}
+__device__ __forceinline__ dd dd_mul(dd a, dd b)
+{
+    dd p = two_prod(a.hi, b.hi);
+    const double c = a.hi * b.lo;
+    const double d = a.lo * b.hi;
+    p.lo = p.lo + (c + d);
+    return fast_two_sum(p.hi, p.lo);
+}
+__device__ __forceinline__ dd dd_mul_d(dd a, double b)
+{
+    dd p = two_prod(a.hi, b);
+    p.lo = p.lo + a.lo * b;
+    return fast_two_sum(p.hi, p.lo);
+}
+__device__ __forceinline__ dd dd_div_d(dd a, double b)
+{
+    const double q1 = a.hi / b;
+    const dd p = two_prod(q1, b);
+    const double r = ((a.hi - p.hi) - p.lo + a.lo) / b;
+    return fast_two_sum(q1, r);
+}
+
+// ln 2 split into double-double: the nearest double and the nearest double to
+// the remainder.
+__device__ constexpr double kLn2Hi = 0x1.62e42fefa39efp-1;
+__device__ constexpr double kLn2Lo = 0x1.abc9e3b39803fp-56;
+
+__device__ float expf_cr(float xf)
+{
+    if (xf != xf) return xf;
+    if (xf < -104.0f) return 0.0f;    // exp(x) < 2^-150: rounds to +0
+    if (xf > 89.0f) return __builtin_huge_valf();
+    if (xf == 0.0f) return 1.0f;
+    const double x = (double)xf;
+    const double k = rint(x * (1.0 / kLn2Hi));
+    const dd kl = dd_mul_d(dd{kLn2Hi, kLn2Lo}, k);
+    const dd r = dd_add(dd{x, 0.0}, dd{-kl.hi, -kl.lo});
+    const dd s{ldexp(r.hi, -10), ldexp(r.lo, -10)};
+    // m = e^s - 1 = s (1 + s/2 (1 + s/3 (1 + ... (1 + s/10))))
+    dd m{1.0, 0.0};
+    for (int n = 10; n >= 2; --n) m = dd_add(dd{1.0, 0.0}, dd_mul(dd_div_d(s, (double)n), m));
+    m = dd_mul(s, m);
+    for (int i = 0; i < 10; ++i) m = dd_add(dd_mul_d(m, 2.0), dd_mul(m, m));
+    dd y = dd_add(dd{1.0, 0.0}, m);
+    const int ki = (int)k;
+    y.hi = ldexp(y.hi, ki);
+    y.lo = ldexp(y.lo, ki);
+    // Round hi + lo to binary32.  f = RN(hi); the exact value lies on the far
+    // side of the midpoint between f and its neighbour only if hi is that
+    // midpoint and lo points away from f.
+    float f = (float)y.hi;
+    const double d = y.hi - (double)f;   // exact
+    if (d != 0.0) {
+        const float g = d > 0.0 ? nextafterf(f, __builtin_huge_valf()) : nextafterf(f, 0.0f);
+        const double half = ((double)g - (double)f) * 0.5;
+        if (d == half && ((d > 0.0 && y.lo > 0.0) || (d < 0.0 && y.lo < 0.0))) f = g;
+    } else if (y.lo != 0.0) {
+        // hi is a binary32 value: the exact value differs by |lo| << half a unit
+    }
+    return f;
+}
+
+__global__ __launch_bounds__(256) void k_expf(const float* __restrict__ x, int64_t n,
+                                              float* __restrict__ y)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        y[i] = expf_cr(x[i]);
+}
+
+hipError_t launch_expf(const float* x, int64_t n, float* y, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(k_expf, dim3((unsigned)blocks), dim3(256), 0, s, x, n, y);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Softmax and top-k, one wave per token.  m = max l (exact); z_e = expf_cr(l_e - m);
+// S = z_0 + z_1 + ... in ascending e (one lane, sequential); p_e = z_e / S;
+// then k rounds of a wave-wide maximum over the key (p, -e): ties go to the
+// lower expert id.
+constexpr int kSmMaxE = 1024;
+
+__global__ __launch_bounds__(256) void k_softmax_topk(const float* __restrict__ logits, int E, int T,
+                                                      int k, int* __restrict__ ids,
+                                                      float* __restrict__ w)
+{
+    __shared__ float sp[4][kSmMaxE];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    const bool valid = t < T;
+    const float* row = logits + (int64_t)(valid ? t : 0) * E;
+    float m = -__builtin_huge_valf();
+    for (int e = lane; e < E; e += 64) m = fmaxf(m, row[e]);
+    m = wave_max(m);
+    for (int e = lane; e < E; e += 64) sp[wave][e] = expf_cr(row[e] - m);
+    __syncthreads();
+    float S = 0.0f;
+    if (lane == 0)
+        for (int e = 0; e < E; ++e) S = S + sp[wave][e];
+    S = __shfl(S, 0);
+    for (int e = lane; e < E; e += 64) sp[wave][e] = sp[wave][e] / S;
+    __syncthreads();
+    // each round: the lane-local best untaken (p, -e), then the wave maximum
+    unsigned taken[kSmMaxE / 64];
+#pragma unroll
+    for (int i = 0; i < kSmMaxE / 64; ++i) taken[i] = 0;
+    for (int j = 0; j < k; ++j) {
+        unsigned long long best = 0;
+#pragma unroll
+        for (int i = 0; i < kSmMaxE / 64; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E && !taken[i]) {
+                const unsigned pb = __float_as_uint(sp[wave][e]);
+                const unsigned long long key =
+                    ((unsigned long long)pb << 32) | (unsigned long long)(0xffffffffu - (unsigned)e);
+                best = key > best ? key : best;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const unsigned long long o = __shfl_xor(best, off);
+            best = o > best ? o : best;
+        }
+        const int e = (int)(0xffffffffu - (unsigned)(best & 0xffffffffu));
+        if ((e & 63) == lane) {
+#pragma unroll
+            for (int i = 0; i < kSmMaxE / 64; ++i)
+                if (i == (e >> 6)) taken[i] = 1;
+        }
+        if (lane == 0 && valid) {
+            ids[(int64_t)t * k + j] = e;
+            w[(int64_t)t * k + j] = __uint_as_float((unsigned)(best >> 32));
+        }
+    }
+}
+
+hipError_t launch_softmax_topk(const float* logits, int E, int T, int k, int* ids, float* w,
+                               hipStream_t s)
+{
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_softmax_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, E, T, k, ids, w);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Grouping by the union of selected experts (one workgroup): a bitmap of
+// (expert, token) selections in LDS, per-expert counts, an exclusive scan into
+// offsets, then each expert lists its tokens in ascending order.  The combine
+// table gets, per token, its pair rows in ascending expert id.
+__global__ __launch_bounds__(1024) void k_group(const int* __restrict__ ids,
+                                                const float* __restrict__ w, int T, int k, int E,
+                                                int* __restrict__ off, int* __restrict__ pair_tok,
+                                                int* __restrict__ comb_row,
+                                                float* __restrict__ comb_w)
+{
+    extern __shared__ unsigned sel[];
+    __shared__ int cnt[1024];
+    __shared__ int scan[1024];
+    const int words = (T + 31) >> 5;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < E * words; i += 1024) sel[i] = 0;
+    for (int i = tid; i < 1024; i += 1024) cnt[i] = 0;
+    __syncthreads();
+    for (int p = tid; p < T * k; p += 1024) {
+        const int t = p / k, e = ids[p];
+        atomicOr(&sel[e * words + (t >> 5)], 1u << (t & 31));
+        atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    // inclusive scan of cnt[0..1024) (Hillis-Steele)
+    scan[tid] = cnt[tid];
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int v = tid >= d ? scan[tid - d] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    if (tid < E) off[tid + 1] = scan[tid];
+    if (tid == 0) off[0] = 0;
+    for (int e = tid; e < E; e += 1024) {
+        int pos = scan[e] - cnt[e];
+        for (int wd = 0; wd < words; ++wd) {
+            unsigned bits = sel[e * words + wd];
+            while (bits) {
+                const int t = (wd << 5) + (__ffs(bits) - 1);
+                bits &= bits - 1;
+                pair_tok[pos] = t;
+                int rank = 0;
+                float we = 0.0f;
+                for (int j = 0; j < k; ++j) {
+                    const int ej = ids[t * k + j];
+                    rank += ej < e;
+                    if (ej == e) we = w[t * k + j];
+                }
+                comb_row[t * k + rank] = pos;
+                comb_w[t * k + rank] = we;
+                ++pos;
+            }
+        }
+    }
+}
+
+hipError_t launch_group(const int* ids, const float* w, int T, int k, int E, int* off,
+                        int* pair_tok, int* comb_row, float* comb_w, hipStream_t s)
+{
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), group_lds_bytes(T, E), s, ids, w, T, k, E,
+                       off, pair_tok, comb_row, comb_w);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Expert products.  Workgroup = (expert e, band of 64 rows); the expert's token
+// group (pairs off[e] .. off[e+1]) is processed 32 tokens at a time, so a group
+// of up to 32 tokens reads the expert's weight band exactly once; an unselected
+// expert returns at once and reads no weight.  With two weights (gate and up)
+// the epilogue writes r = fl(g * u).
+constexpr int kExPiece = 8;
+constexpr int kExStride = kExPiece * 64 + 16;
+constexpr int kExTB = 2;
+
+template <bool kPair>
+__global__ __launch_bounds__(256) void k_expert(ExpertArgs A)
+{
+    __shared__ __attribute__((aligned(16))) int8_t xl[16 * kExTB * kExStride];
+    __shared__ int rows[16 * kExTB];
+    const int e = blockIdx.x / A.tiles_n, tn = blockIdx.x % A.tiles_n;
+    const int p0 = A.off[e], p1 = A.off[e + 1];
+    if (p0 == p1) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nw0 = tn * 64 + wave * 16;
+    const int nkb = A.K >> 6;
+    const int arow = min(nw0 + (lane & 15), A.N - 1);
+    const int64_t wbase = (int64_t)e * A.N * A.K + (int64_t)arow * A.K + ((lane >> 4) << 4);
+    const int8_t* w0 = A.W0 + wbase;
+    const int8_t* w1 = kPair ? A.W1 + wbase : nullptr;
+    const int boff = (lane & 15) * kExStride + ((lane >> 4) << 4);
+    const int nr = nw0 + ((lane >> 4) << 2);
+
+    for (int g0 = p0; g0 < p1; g0 += 16 * kExTB) {
+        const int gm = min(16 * kExTB, p1 - g0);
+        __syncthreads();
+        if (threadIdx.x < 16 * kExTB)
+            rows[threadIdx.x] = threadIdx.x < gm
+                                    ? (A.gather ? A.gather[g0 + threadIdx.x] : g0 + threadIdx.x)
+                                    : -1;
+        v4i acc0[kExTB], acc1[kExTB];
+#pragma unroll
+        for (int tb = 0; tb < kExTB; ++tb) acc0[tb] = acc1[tb] = v4i{0, 0, 0, 0};
+        for (int kp = 0; kp < nkb; kp += kExPiece) {
+            const int npc = min(kExPiece, nkb - kp);
+            v4i a0[kExPiece], a1[kExPiece];
+#pragma unroll
+            for (int i = 0; i < kExPiece; ++i)
+                if (i < npc) {
+                    a0[i] = ld16(w0 + (int64_t)(kp + i) * 64);
+                    if (kPair) a1[i] = ld16(w1 + (int64_t)(kp + i) * 64);
+                }
+            __syncthreads();
+            const int cpr = npc * 4;
+            for (int idx = threadIdx.x; idx < 16 * kExTB * cpr; idx += 256) {
+                const int t = idx / cpr, c = idx - t * cpr;
+                const int r = rows[t];
+                v4i v = v4i{0, 0, 0, 0};
+                if (r >= 0) v = ld16(A.X + (int64_t)r * A.ldx + (int64_t)kp * 64 + c * 16);
+                st16(xl + t * kExStride + c * 16, v);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kExPiece; ++i) {
+                if (i < npc) {
+#pragma unroll
+                    for (int tb = 0; tb < kExTB; ++tb) {
+                        const v4i b = *reinterpret_cast<const v4i*>(xl + tb * 16 * kExStride + boff + i * 64);
+                        acc0[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[i], b, acc0[tb], 0, 0, 0);
+                        if (kPair)
+                            acc1[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[i], b, acc1[tb], 0, 0, 0);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int tb = 0; tb < kExTB; ++tb) {
+            const int j = tb * 16 + (lane & 15);
+            if (j >= gm) continue;
+            const int r = rows[j];
+            const float xs = A.xs[r];
+            float* yrow = A.Y + (int64_t)(g0 + j) * A.ldy;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = nr + q;
+                if (n >= A.N) continue;
+                const float g = epilogue(acc0[tb][q], A.s0[(int64_t)e * A.N + n], xs);
+                if (kPair) {
+                    const float u = epilogue(acc1[tb][q], A.s1[(int64_t)e * A.N + n], xs);
+                    yrow[n] = g * u;
+                } else {
+                    yrow[n] = g;
+                }
+            }
+        }
+    }
+}
+
+hipError_t launch_expert(const ExpertArgs& a, hipStream_t s)
+{
+    const dim3 g(a.E * a.tiles_n), b(256);
+    if (a.W1) hipLaunchKernelGGL(k_expert<true>, g, b, 0, s, a);
+    else hipLaunchKernelGGL(k_expert<false>, g, b, 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Weighted combine: out[t][j] = +0, then over the token's experts in ascending
+// id out = fl(out + fl(w * y)).
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ypair,
+                                                 const int* __restrict__ comb_row,
+                                                 const float* __restrict__ comb_w, int k, int H,
+                                                 float* __restrict__ out)
+{
+    const int t = blockIdx.x;
+    for (int j = threadIdx.x; j < H; j += 256) {
+        float o = 0.0f;
+        for (int r = 0; r < k; ++r) {
+            const float c = comb_w[t * k + r] * ypair[(int64_t)comb_row[t * k + r] * H + j];
+            o = o + c;
+        }
+        out[(int64_t)t * H + j] = o;
+    }
+}
+
+hipError_t launch_combine(const float* ypair, const int* comb_row, const float* comb_w, int T,
+                          int k, int H, float* out, hipStream_t s)
+{
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, ypair, comb_row, comb_w, k, H, out);
+    return hipGetLastError();
+}
+
+}  // namespace pf

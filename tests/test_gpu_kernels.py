@@ -1,0 +1,196 @@
+"""GPU parity of the single-kernel entry points against the oracle (bit-exact).
+
+Every comparison is byte-for-byte: int8 codes identical, f32 outputs 0 ulp
+(``assert_array_equal`` on the raw values).  Inputs come from prefill_inputs.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import prefill_inputs
+import int8_weight_gemm_amd as pf
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def test_init_reports_gfx950():
+    pf.init()
+
+
+# --- quantisation ----------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K", [(1, 64), (11, 1024), (32, 4096), (7, 11008), (512, 2048)])
+def test_quantize_matches_oracle(M, K):
+    x = prefill_inputs.activations(np.random.default_rng(M * 7 + K), (M, K))
+    x[0, :5] = [0.0, -0.0, 2.5, -2.5, 1e-30]
+    if M > 2:
+        x[2] = 0.0                      # all-zero token
+    q, s = pf.quantize_act(dev(x))
+    qo, so = oracle.quantize(x)
+    np.testing.assert_array_equal(host(s), so)
+    np.testing.assert_array_equal(host(q), qo)
+
+
+def test_quantize_exact_halves_and_golden():
+    rows = []
+    for j in (-6, 0, 3):
+        n = np.arange(-126, 126)
+        rows.append(np.concatenate([[127 * 2.0 ** j], (n + 0.5) * 2.0 ** j, np.zeros(2)]))
+    x = np.array(rows, np.float32)
+    q, s = pf.quantize_act(dev(x))
+    qo, so = oracle.quantize(x)
+    np.testing.assert_array_equal(host(q), qo)
+    np.testing.assert_array_equal(host(s), so)
+
+
+# --- GEMV and the chunk product ------------------------------------------------------
+
+def _proj(N, K, M, seed):
+    d = prefill_inputs.projection(N, K, M, seed)
+    q, s = oracle.quantize(d["x"])
+    return d["W"], d["w_scale"], q, s
+
+
+@pytest.mark.parametrize("N,K", [(1024, 1024), (70, 128), (4096, 4096), (512, 2048)])
+def test_gemv_matches_oracle(N, K):
+    W, ws, q, s = _proj(N, K, 3, 100 + N)
+    Wd, wsd = dev(W), dev(ws)
+    for t in range(3):
+        y = pf.gemv_i8(Wd, wsd, dev(q[t]), dev(s[t:t + 1]))
+        np.testing.assert_array_equal(host(y), oracle.gemv(W, ws, q[t], s[t]))
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_proj1024_batched_equals_oracle_and_gemvs(split):
+    """32 tokens against W [1024, 1024]: the chunk product, 32 per-token GEMVs and the
+    oracle agree byte for byte ("Batched Prefill", §Correctness)."""
+    d = prefill_inputs.workload("proj1024")
+    W, ws, x = d["W"], d["w_scale"], d["x"]
+    Wd, wsd = dev(W), dev(ws)
+    q, s = pf.quantize_act(dev(x))
+    qo, so = oracle.quantize(x)
+    np.testing.assert_array_equal(host(q), qo)
+    wsp = pf.workspace(pf.gemm_i8_chunk_workspace(1024, 1024, 32)) if split else None
+    y = host(pf.gemm_i8_chunk(Wd, wsd, q, s, ws=wsp))
+    np.testing.assert_array_equal(y, oracle.linear(W, ws, qo, so))
+    for t in range(32):
+        g = pf.gemv_i8(Wd, wsd, q[t].contiguous(), s[t:t + 1].contiguous())
+        np.testing.assert_array_equal(host(g), y[t])
+
+
+@pytest.mark.parametrize("M", list(range(1, 18)) + [31, 33, 48, 63, 64])
+@pytest.mark.parametrize("split", [False, True])
+def test_skinny_tails(M, split):
+    N, K = 200, 1536                     # 200 rows: a ragged last band of 8 rows
+    W, ws, q, s = _proj(N, K, M, 300 + M)
+    wsp = pf.workspace(pf.gemm_i8_chunk_workspace(N, K, M)) if split else None
+    if split:
+        assert pf.gemm_i8_chunk_workspace(N, K, M) > 0
+    y = pf.gemm_i8_chunk(dev(W), dev(ws), dev(q), dev(s), ws=wsp)
+    np.testing.assert_array_equal(host(y), oracle.linear(W, ws, q, s))
+
+
+def test_split_workspace_reused_and_left_zero():
+    N, K, M = 1024, 4096, 32
+    W, ws, q, s = _proj(N, K, M, 41)
+    wsp = pf.workspace(pf.gemm_i8_chunk_workspace(N, K, M))
+    args = (dev(W), dev(ws), dev(q), dev(s))
+    ref = oracle.linear(W, ws, q, s)
+    for _ in range(5):
+        np.testing.assert_array_equal(host(pf.gemm_i8_chunk(*args, ws=wsp)), ref)
+    assert int(host(wsp).astype(np.int64).sum()) == 0 and not host(wsp).any()
+
+
+@pytest.mark.parametrize("M", [65, 100, 128, 129, 300])
+def test_tiled_matches_oracle(M):
+    N, K = 392, 1024                     # ragged rows (392 = 3 * 128 + 8) and tokens
+    W, ws, q, s = _proj(N, K, M, 500 + M)
+    y = pf.gemm_i8_chunk(dev(W), dev(ws), dev(q), dev(s))
+    np.testing.assert_array_equal(host(y), oracle.linear(W, ws, q, s))
+
+
+def test_mfma_single_tiles_extreme_values():
+    """One 16x16x64 and one 32x32x32 tile region with +-127 everywhere: operand
+    layout and int32 range of the MFMA paths against exact integers."""
+    rng = np.random.default_rng(9)
+    for M in (16, 128):
+        N, K = (16, 64) if M == 16 else (128, 128)
+        W = rng.choice(np.array([-127, 127], np.int8), (N, K))
+        q = rng.choice(np.array([-127, 127], np.int8), (M, K))
+        ws = np.ones(N, np.float32)
+        s = np.ones(M, np.float32)
+        y = host(pf.gemm_i8_chunk(dev(W), dev(ws), dev(q), dev(s)))
+        exact = (q.astype(np.int64) @ W.astype(np.int64).T).astype(np.float32)
+        np.testing.assert_array_equal(y, exact)
+
+
+def test_sweep4096_chunks_match_oracle_and_each_other():
+    """W [4096, 4096]: chunk M in {1,...,512} uses the first M tokens; every M gives
+    the oracle's bytes, so y_M equals the first M rows of y_512."""
+    d = prefill_inputs.workload("sweep4096")
+    W, ws, x = d["W"], d["w_scale"], d["x"]
+    qo, so = oracle.quantize(x)
+    ref = oracle.linear(W, ws, qo, so)
+    Wd, wsd = dev(W), dev(ws)
+    q, s = pf.quantize_act(dev(x))
+    np.testing.assert_array_equal(host(q), qo)
+    for M in prefill_inputs.WORKLOADS["sweep4096"]["chunks"]:
+        say("sweep4096 M =", M)
+        wsp = pf.workspace(pf.gemm_i8_chunk_workspace(4096, 4096, M))
+        if M == 1:
+            y = pf.gemv_i8(Wd, wsd, q[0].contiguous(), s[:1].contiguous())[None, :]
+            np.testing.assert_array_equal(host(y), ref[:1])
+        y = pf.gemm_i8_chunk(Wd, wsd, q[:M].contiguous(), s[:M].contiguous(), ws=wsp)
+        np.testing.assert_array_equal(host(y), ref[:M])
+
+
+def test_rejects_bad_arguments_without_launch():
+    W = torch.zeros((64, 100), dtype=torch.int8, device="cuda")
+    with pytest.raises(pf.PrefillError) as e:
+        pf.gemm_i8_chunk(W, torch.ones(64, device="cuda"), torch.zeros((4, 100), dtype=torch.int8, device="cuda"),
+                         torch.ones(4, device="cuda"))
+    assert e.value.status == pf.PF_EINVAL
+
+
+# --- exp -------------------------------------------------------------------------------
+
+def test_expf_cr_whole_nonpositive_domain():
+    """Every binary32 x in [-104, 0] (and a few beyond): the GPU exp equals the
+    oracle's correctly rounded exp.  Where float64 exp decides the rounding the
+    oracle is known to equal RN(float64 exp) (exhaustive CPU pin), elsewhere the
+    oracle is called directly."""
+    top = int(np.array(-104.0, np.float32).view(np.uint32))
+    start = int(np.array(-0.0, np.float32).view(np.uint32))
+    step = 1 << 26
+    for lo in range(start, top + 1, step):
+        bits = np.arange(lo, min(lo + step, top + 1), dtype=np.uint64).astype(np.uint32)
+        x = bits.view(np.float32)
+        g = host(pf.expf_cr(dev(x)))
+        d = np.exp(x.astype(np.float64))
+        r = d.astype(np.float32)
+        nb = np.where(d > r.astype(np.float64), np.nextafter(r, np.float32(np.inf)),
+                      np.nextafter(r, np.float32(-np.inf)))
+        mid = (r.astype(np.float64) + nb.astype(np.float64)) / 2
+        close = np.abs(d - mid) <= np.abs(d) * 2.0 ** -50
+        far_bad = (g != r) & ~close
+        assert not far_bad.any(), x[far_bad][:5]
+        if close.any():
+            np.testing.assert_array_equal(g[close], oracle.expf_cr(x[close]))
+    extra = np.float32([-104.5, -150.0, -1e30, -np.inf, 0.0, -0.0])
+    np.testing.assert_array_equal(host(pf.expf_cr(dev(extra))), oracle.expf_cr(extra))

@@ -1,0 +1,138 @@
+"""GPU parity of pf_prefill_stack against the per-token oracle (bit-exact).
+
+Covers: a small stack compared in full (outputs and every projection), the
+350M-class stack (16 layers, hidden 1024, 747 tokens in 32-token chunks plus an
+11-token tail) on sampled tokens with chunk invariance and the per-token GEMV
+mode, and the 7B-class stack (32 layers, hidden 4096, 2048 tokens in 512-token
+chunks) on sampled tokens.
+"""
+import hashlib
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import prefill_inputs
+import int8_weight_gemm_amd as pf
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_stack(st):
+    return pf.Stack([[dev(w) for w in wl] for wl in st["weights"]],
+                    [[dev(s) for s in sl] for sl in st["scales"]])
+
+
+def run(stack, x, chunk, proj=None, per_token=False, stats=False):
+    ws = pf.workspace(stack.workspace_bytes(chunk))
+    old = os.environ.get("PF_BATCHED_PREFILL")
+    if per_token:
+        os.environ["PF_BATCHED_PREFILL"] = "0"
+    try:
+        out = stack.prefill(x, chunk, ws, proj=proj, stats=stats)
+    finally:
+        if per_token:
+            if old is None:
+                del os.environ["PF_BATCHED_PREFILL"]
+            else:
+                os.environ["PF_BATCHED_PREFILL"] = old
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("chunk", [1, 5, 32, 64, 75, 96, 128])
+def test_small_stack_full_compare(chunk):
+    st = prefill_inputs.stack(L=3, H=128, F=320, P=75, seed=21)
+    y_ref, proj_ref = oracle.stack(st["weights"], st["scales"], st["x"], return_proj=True)
+    stack = to_stack(st)
+    x = dev(st["x"])
+    proj = torch.empty((3, 75, 5 * 128 + 2 * 320), dtype=torch.float32, device="cuda")
+    y = run(stack, x, chunk, proj=proj)
+    np.testing.assert_array_equal(host(y), y_ref)
+    np.testing.assert_array_equal(host(proj), proj_ref)
+    y2 = run(stack, x, chunk)                      # without the projection copy
+    np.testing.assert_array_equal(host(y2), y_ref)
+
+
+def test_small_stack_per_token_mode_identical():
+    st = prefill_inputs.stack(L=2, H=256, F=512, P=40, seed=22)
+    stack = to_stack(st)
+    x = dev(st["x"])
+    yb, sb = run(stack, x, 32, stats=True)
+    yt, stt = run(stack, x, 32, per_token=True, stats=True)
+    assert sb["per_token_mode"] == 0 and stt["per_token_mode"] == 1
+    assert sb["chunks"] == 2 and sb["tail_tokens"] == 8
+    np.testing.assert_array_equal(host(yb), host(yt))
+    np.testing.assert_array_equal(host(yb), oracle.stack(st["weights"], st["scales"], st["x"]))
+
+
+@pytest.fixture(scope="module")
+def stack350m():
+    st = prefill_inputs.workload("stack350m")
+    return st, to_stack(st), dev(st["x"])
+
+
+def _digest(a):
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def test_stack350m_sampled_tokens_match_oracle(stack350m):
+    st, stack, x = stack350m
+    say("stack350m chunk 32")
+    y = host(run(stack, x, 32))
+    # first chunk, a middle chunk, the last full chunk and the 11-token tail
+    toks = np.r_[0:4, 31:33, 400:404, 704:708, 735:747]
+    ref = oracle.stack(st["weights"], st["scales"], st["x"][toks])
+    np.testing.assert_array_equal(y[toks], ref)
+    assert np.all(np.isfinite(y))
+
+
+def test_stack350m_chunk_invariance_and_per_token(stack350m):
+    st, stack, x = stack350m
+    base = _digest(host(run(stack, x, 32)))
+    for chunk in (7, 64, 96, 747):
+        say("stack350m chunk", chunk)
+        assert _digest(host(run(stack, x, chunk))) == base, chunk
+    say("stack350m per-token GEMV mode")
+    assert _digest(host(run(stack, x, 32, per_token=True))) == base
+
+
+def test_stack350m_repeatable(stack350m):
+    st, stack, x = stack350m
+    ws = pf.workspace(stack.workspace_bytes(32))
+    y0 = host(stack.prefill(x, 32, ws))
+    for _ in range(5):
+        np.testing.assert_array_equal(host(stack.prefill(x, 32, ws)), y0)
+
+
+def test_stack7b_sampled_tokens_match_oracle():
+    say("stack7b: generating 6.5 GB of weights")
+    st = prefill_inputs.workload("stack7b")
+    stack = to_stack(st)
+    x = dev(st["x"])
+    say("stack7b chunk 512")
+    y = host(run(stack, x, 512))
+    assert np.all(np.isfinite(y))
+    toks = np.array([0, 511, 512, 1500, 2047])
+    say("stack7b oracle on", len(toks), "tokens")
+    ref = oracle.stack(st["weights"], st["scales"], st["x"][toks])
+    np.testing.assert_array_equal(y[toks], ref)
+    say("stack7b chunk 1000 (ragged tail 48) and 64 (skinny path)")
+    np.testing.assert_array_equal(host(run(stack, x, 1000)), y)
+    np.testing.assert_array_equal(host(run(stack, x[:256].contiguous(), 64)), y[:256])
