@@ -16,7 +16,10 @@
  *   experts and runs the experts on their token groups.
  *
  * Conventions (all entry points):
- *   - Array arguments are DEVICE pointers owned by the caller, 16-byte aligned.
+ *   - Array arguments are DEVICE pointers owned by the caller.  int8 matrices
+ *     and f32 inputs that are read with 128-bit loads (x of the quantiser, the
+ *     stack and the experts; the projection buffer) are 16-byte aligned; scales,
+ *     ids and f32 outputs need 4-byte alignment.
  *     Host-side descriptors (pf_stack, pf_layer, pf_moe, pf_stack_stats) are
  *     read during the call only.
  *   - Layouts are row-major.  A weight W is [N][K] (K contiguous); activations

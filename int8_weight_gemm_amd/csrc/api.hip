@@ -44,6 +44,7 @@ pf_status check_device()
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb)
@@ -187,7 +188,7 @@ pf_status validate_stack(const pf_stack* st)
     for (int64_t l = 0; l < st->n_layers; ++l)
         for (int j = 0; j < PF_NPROJ; ++j) {
             const pf_layer& ly = st->layers[l];
-            if (!ly.W[j] || !ly.w_scale[j] || !aligned16(ly.W[j]) || !aligned16(ly.w_scale[j]))
+            if (!ly.W[j] || !ly.w_scale[j] || !aligned16(ly.W[j]) || !aligned4(ly.w_scale[j]))
                 return PF_EINVAL;
         }
     return PF_OK;
@@ -232,9 +233,12 @@ pf_status validate_moe(const pf_moe* m)
         m->top_k > m->n_experts)
         return PF_EINVAL;
     if (!valid_k(m->hidden) || !valid_k(m->inter)) return PF_EINVAL;
-    const void* ptrs[] = {m->W_router, m->W_gate, m->W_up, m->W_down, m->s_gate, m->s_up, m->s_down};
-    for (const void* p : ptrs)
+    const void* mats[] = {m->W_router, m->W_gate, m->W_up, m->W_down};
+    for (const void* p : mats)
         if (!p || !aligned16(p)) return PF_EINVAL;
+    const void* scales[] = {m->s_gate, m->s_up, m->s_down};
+    for (const void* p : scales)
+        if (!p || !aligned4(p)) return PF_EINVAL;
     return PF_OK;
 }
 
@@ -284,7 +288,7 @@ pf_status pf_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int
         if (M < 0 || K <= 0 || K % 4 != 0 || ldx < K || ldx % 4 != 0 || M > INT32_MAX)
             return PF_EINVAL;
         if (M == 0) return PF_OK;
-        if (!x || !xq || !a_scale || !aligned16(x) || !aligned16(xq) || !aligned16(a_scale))
+        if (!x || !xq || !a_scale || !aligned16(x) || !aligned16(xq) || !aligned4(a_scale))
             return PF_EINVAL;
         const size_t xb = (size_t)((M - 1) * ldx + K) * 4;
         if (overlap(x, xb, xq, (size_t)M * K) || overlap(x, xb, a_scale, (size_t)M * 4) ||
@@ -312,8 +316,8 @@ pf_status pf_gemm_i8_chunk(const int8_t* W, const float* w_scale, int64_t N, int
         if (N <= 0 || N > INT32_MAX || !valid_k(K) || M < 0 || M > INT32_MAX) return PF_EINVAL;
         if (M == 0) return PF_OK;
         if (!W || !w_scale || !xq || !a_scale || !y) return PF_EINVAL;
-        if (!aligned16(W) || !aligned16(w_scale) || !aligned16(xq) || !aligned16(a_scale) ||
-            !aligned16(y))
+        if (!aligned16(W) || !aligned4(w_scale) || !aligned16(xq) || !aligned4(a_scale) ||
+            !aligned4(y))
             return PF_EINVAL;
         const size_t yb = (size_t)M * N * 4;
         if (overlap(y, yb, W, (size_t)N * K) || overlap(y, yb, w_scale, (size_t)N * 4) ||
@@ -348,8 +352,8 @@ pf_status pf_gemv_i8(const int8_t* W, const float* w_scale, int64_t N, int64_t K
     try {
         if (N <= 0 || N > INT32_MAX || !valid_k(K)) return PF_EINVAL;
         if (!W || !w_scale || !xq || !a_scale || !y) return PF_EINVAL;
-        if (!aligned16(W) || !aligned16(w_scale) || !aligned16(xq) || !aligned16(a_scale) ||
-            !aligned16(y))
+        if (!aligned16(W) || !aligned4(w_scale) || !aligned16(xq) || !aligned4(a_scale) ||
+            !aligned4(y))
             return PF_EINVAL;
         const size_t yb = (size_t)N * 4;
         if (overlap(y, yb, W, (size_t)N * K) || overlap(y, yb, w_scale, yb) ||
@@ -388,7 +392,7 @@ pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int
             if (stats) std::memset(stats, 0, sizeof(*stats));
             return PF_OK;
         }
-        if (!x || !y || !aligned16(x) || !aligned16(y) || (proj && !aligned16(proj)))
+        if (!x || !y || !aligned16(x) || !aligned4(y) || (proj && !aligned16(proj)))
             return PF_EINVAL;
         const size_t xb = (size_t)P * H * 4, pb = proj ? (size_t)L * P * NT * 4 : 0;
         if (overlap(x, xb, y, xb) || overlap(proj, pb, x, xb) || overlap(proj, pb, y, xb))
@@ -537,7 +541,7 @@ pf_status pf_moe_chunk(const pf_moe* moe, const float* x, int64_t T, int32_t* id
         const int64_t E = moe->n_experts, k = moe->top_k, H = moe->hidden, I = moe->inter;
         if ((size_t)E * ((T + 31) / 32) > 12288) return PF_EINVAL;   // grouping bitmap in LDS
         if (!x || !ids || !weights || !out) return PF_EINVAL;
-        if (!aligned16(x) || !aligned16(ids) || !aligned16(weights) || !aligned16(out))
+        if (!aligned16(x) || !aligned4(ids) || !aligned4(weights) || !aligned4(out))
             return PF_EINVAL;
         const size_t xb = (size_t)T * H * 4, ib = (size_t)T * k * 4;
         if (overlap(x, xb, out, xb) || overlap(ids, ib, weights, ib) || overlap(ids, ib, out, xb) ||
@@ -598,7 +602,7 @@ pf_status pf_expf_cr(const float* x, int64_t n, float* y, void* stream)
     try {
         if (n < 0) return PF_EINVAL;
         if (n == 0) return PF_OK;
-        if (!x || !y || !aligned16(x) || !aligned16(y)) return PF_EINVAL;
+        if (!x || !y || !aligned4(x) || !aligned4(y)) return PF_EINVAL;
         if (overlap(x, (size_t)n * 4, y, (size_t)n * 4) && x != y) return PF_EINVAL;
         if (pf_status st = check_device()) return st;
         return launched(launch_expf(x, n, y, (hipStream_t)stream));

@@ -48,7 +48,8 @@ def test_gemm_rejects_bad_k_and_alignment():
     # K too large for an exact int32 accumulator
     assert lib.pf_gemm_i8_chunk(FAKE, FAKE, 64, 131072 + 64, FAKE, FAKE, 4, P(0x20000), None, 0, None) == pf.PF_EINVAL
     # misaligned output
-    assert lib.pf_gemm_i8_chunk(FAKE, FAKE, 64, 128, FAKE, FAKE, 4, P(0x20004), None, 0, None) == pf.PF_EINVAL
+    assert lib.pf_gemm_i8_chunk(FAKE, FAKE, 64, 128, FAKE, FAKE, 4, P(0x20002), None, 0, None) == pf.PF_EINVAL
+    assert lib.pf_gemm_i8_chunk(P(0x10008), FAKE, 64, 128, FAKE, FAKE, 4, P(0x20000), None, 0, None) == pf.PF_EINVAL
     # null pointer
     assert lib.pf_gemm_i8_chunk(None, FAKE, 64, 128, FAKE, FAKE, 4, P(0x20000), None, 0, None) == pf.PF_EINVAL
     # output overlapping the weights

@@ -51,7 +51,7 @@ def test_quantize_exact_halves_and_golden():
     rows = []
     for j in (-6, 0, 3):
         n = np.arange(-126, 126)
-        rows.append(np.concatenate([[127 * 2.0 ** j], (n + 0.5) * 2.0 ** j, np.zeros(2)]))
+        rows.append(np.concatenate([[127 * 2.0 ** j], (n + 0.5) * 2.0 ** j, np.zeros(3)]))
     x = np.array(rows, np.float32)
     q, s = pf.quantize_act(dev(x))
     qo, so = oracle.quantize(x)
