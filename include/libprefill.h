@@ -32,12 +32,9 @@
  *   - Outputs are fully overwritten, never accumulated into.
  *   - The library allocates no device memory inside calls.  Calls that need
  *     scratch memory take a caller-owned workspace whose size comes from the
- *     matching *_workspace() query.  A workspace must be zero-filled once
- *     before its first use (pf_workspace_clear, or any zero fill); each call
- *     returns the parts that must start at zero (split-K accumulators and
- *     their counters) to zero before it ends, so later calls need no clearing.
- *     Calls that share one workspace must be ordered (same stream); calls that
- *     overlap on one workspace race.
+ *     matching *_workspace() query; its contents on entry do not matter and
+ *     are undefined on return.  Calls that share one workspace must be ordered
+ *     (same stream); calls that overlap on one workspace race.
  *   - Input activations must be finite; results for NaN or Inf inputs are
  *     unspecified.
  *   - K of every product must be a positive multiple of 64 and at most 131072,
@@ -74,7 +71,8 @@ const char* pf_status_string(pf_status status);
  * use; calling it first only moves the cost.  PF_ENODEV without a device. */
 pf_status pf_init(void);
 
-/* Zero-fills `bytes` of workspace on `stream` (a fill kernel, no memset node). */
+/* Zero-fills `bytes` of device memory on `stream` (a fill kernel, no memset
+ * node); a convenience for callers that want a defined workspace. */
 pf_status pf_workspace_clear(void* workspace, size_t bytes, void* stream);
 
 /* Per-token symmetric int8 quantisation of a chunk, done once per chunk
@@ -118,13 +116,26 @@ typedef struct {
     const pf_layer* layers;  /* host array of n_layers */
 } pf_stack;
 
+/* Statistics of one pf_prefill_stack call.  time_kernels is the only input:
+ * set it to 1 to bracket every launch with HIP events on the call's stream and
+ * get per-class device times (adds an event pair per launch).  Algorithmic
+ * bytes count each kernel's inputs read once and outputs written once: for a
+ * product, weights + weight scales + quantised tokens + token scales + f32
+ * outputs; for a quantisation, f32 inputs + int8 codes + scales. */
 typedef struct {
-    int64_t chunks;          /* chunks processed (the last may be ragged)       */
-    int64_t tail_tokens;     /* tokens in the last chunk                       */
-    int64_t launches;        /* kernel launches queued                         */
-    double alg_bytes;        /* weight + scale + activation bytes, algorithmic  */
-    double elapsed_ms;       /* device time between first and last launch      */
-    int per_token_mode;      /* 1 if the per-token GEMV path ran                */
+    int time_kernels;          /* in: 1 = time every launch                       */
+    int per_token_mode;        /* out: 1 if the per-token GEMV path ran           */
+    int64_t chunks;            /* chunks processed (the last may be ragged)       */
+    int64_t tail_tokens;       /* tokens in the last chunk                        */
+    int64_t launches;          /* kernel launches queued                          */
+    double alg_bytes;          /* algorithmic bytes of all launches               */
+    double elapsed_ms;         /* device time from before the first launch to after the last */
+    int64_t product_launches;  /* int8 products (chunk GEMMs, or GEMVs per token) */
+    int64_t quant_launches;    /* quantisations                                   */
+    double product_alg_bytes;
+    double quant_alg_bytes;
+    double product_ms;         /* summed device time of the products (time_kernels) */
+    double quant_ms;           /* summed device time of the quantisations (time_kernels) */
 } pf_stack_stats;
 
 /* Workspace bytes for pf_prefill_stack with this stack and chunk size. */
@@ -142,7 +153,7 @@ size_t pf_prefill_stack_workspace(const pf_stack* stack, int64_t chunk);
  * PF_BATCHED_PREFILL=0 the same call runs one GEMV per token and projection
  * instead (the per-token baseline); the bytes of y and proj are identical
  * ("Batched Prefill", §Correctness).  stats, when not NULL, is filled in and the
- * call then synchronises the stream. */
+ * call then synchronises the stream (see pf_stack_stats). */
 pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int64_t chunk,
                            float* y, float* proj, void* workspace, size_t ws_bytes,
                            pf_stack_stats* stats, void* stream);

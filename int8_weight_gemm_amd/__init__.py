@@ -44,9 +44,13 @@ class _Stack(ctypes.Structure):
 
 
 class StackStats(ctypes.Structure):
-    _fields_ = [("chunks", ctypes.c_int64), ("tail_tokens", ctypes.c_int64),
+    _fields_ = [("time_kernels", ctypes.c_int), ("per_token_mode", ctypes.c_int),
+                ("chunks", ctypes.c_int64), ("tail_tokens", ctypes.c_int64),
                 ("launches", ctypes.c_int64), ("alg_bytes", ctypes.c_double),
-                ("elapsed_ms", ctypes.c_double), ("per_token_mode", ctypes.c_int)]
+                ("elapsed_ms", ctypes.c_double), ("product_launches", ctypes.c_int64),
+                ("quant_launches", ctypes.c_int64), ("product_alg_bytes", ctypes.c_double),
+                ("quant_alg_bytes", ctypes.c_double), ("product_ms", ctypes.c_double),
+                ("quant_ms", ctypes.c_double)]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -206,13 +210,17 @@ class Stack:
         return int(lib().pf_prefill_stack_workspace(ctypes.byref(self._desc), chunk))
 
     def prefill(self, x: torch.Tensor, chunk: int, ws: torch.Tensor, y: torch.Tensor | None = None,
-                proj: torch.Tensor | None = None, stats: bool = False):
-        """x f32 [P, H] -> y f32 [P, H]; proj (optional) f32 [L, P, 5H + 2F]."""
+                proj: torch.Tensor | None = None, stats: bool = False, time_kernels: bool = False):
+        """x f32 [P, H] -> y f32 [P, H]; proj (optional) f32 [L, P, 5H + 2F].
+        With stats (or time_kernels) also returns the call's statistics."""
+        stats = stats or time_kernels
         _dev(x, torch.float32, "x")
         P = x.shape[0]
         if y is None:
             y = torch.empty((P, self.H), dtype=torch.float32, device=x.device)
         st = StackStats() if stats else None
+        if st is not None:
+            st.time_kernels = 1 if time_kernels else 0
         _check("pf_prefill_stack", lib().pf_prefill_stack(
             ctypes.byref(self._desc), _ptr(x), P, chunk, _ptr(y), _ptr(proj), _ptr(ws), ws.numel(),
             ctypes.byref(st) if st is not None else None, _stream()))

@@ -18,7 +18,6 @@ namespace {
 
 constexpr int64_t kMaxK = 131072;
 constexpr size_t kAlign = 256;
-constexpr int kTargetWorkgroups = 512;   // two per compute unit
 
 // Per-device result of the architecture check: 0 unknown, 1 gfx950, -1 other.
 std::atomic<int> g_arch[64];
@@ -64,28 +63,37 @@ pf_status launched(hipError_t e)
 }
 
 // ---------------------------------------------------------------------------
-// Split plan of the skinny product: 64-row bands x K slices, enough
-// workgroups to cover the chip twice, every slice at least 4 k-blocks long.
+// Split plan of the skinny product: 16-row tiles; when a launch has fewer tiles
+// than compute units, the K range is split across workgroups (each split at
+// least 8 k-blocks of 64 bytes) until every compute unit has one.
 struct SkinnyPlan {
     int tiles_n, splits, kb_per_split;
 };
 
-SkinnyPlan plan_skinny(int64_t N, int64_t K, int64_t total_bands)
+constexpr int kSkinnyRows = 16;
+constexpr int64_t kComputeUnits = 256;
+
+SkinnyPlan plan_skinny(int64_t N, int64_t K, int64_t total_tiles)
 {
     SkinnyPlan p;
-    p.tiles_n = (int)((N + 63) / 64);
+    p.tiles_n = (int)((N + kSkinnyRows - 1) / kSkinnyRows);
     const int nkb = (int)(K / 64);
     int s = 1;
-    while (total_bands * s * 2 <= kTargetWorkgroups && nkb / (s * 2) >= 4) s *= 2;
+    while (total_tiles * s < kComputeUnits && nkb / (2 * s) >= 8) s *= 2;
     p.kb_per_split = (nkb + s - 1) / s;
     p.splits = (nkb + p.kb_per_split - 1) / p.kb_per_split;
     return p;
 }
 
+SkinnyPlan unsplit(int64_t N, int64_t K)
+{
+    return SkinnyPlan{(int)((N + kSkinnyRows - 1) / kSkinnyRows), 1, (int)(K / 64)};
+}
+
 size_t split_bytes(int64_t N, int64_t M, const SkinnyPlan& p)
 {
     if (p.splits <= 1) return 0;
-    return round_up((size_t)M * (size_t)N * 4, kAlign) + round_up((size_t)p.tiles_n * 4, kAlign);
+    return round_up((size_t)p.splits * (size_t)M * (size_t)N * 4, kAlign);
 }
 
 int token_blocks(int64_t M) { return (int)((M + 15) / 16); }
@@ -104,9 +112,7 @@ void make_skinny(GemmProb& g, const int8_t* W, const float* ws, int64_t N, int64
     g.splits = p.splits; g.kb_per_split = p.kb_per_split;
     if (p.splits > 1) {
         g.acc = reinterpret_cast<int*>(scratch);
-        scratch += round_up((size_t)m_alloc * (size_t)N * 4, kAlign);
-        g.cnt = reinterpret_cast<unsigned*>(scratch);
-        scratch += round_up((size_t)p.tiles_n * 4, kAlign);
+        scratch += split_bytes(N, m_alloc, p);
     }
 }
 
@@ -166,13 +172,13 @@ StackLayout stack_layout(int64_t H, int64_t F, int64_t chunk)
     L.proj = o; o += round_up((size_t)chunk * (5 * H + 2 * F) * 4, kAlign);
     L.split = o;
     const int64_t rows[PF_NPROJ] = {H, H, H, H, F, F, H};
-    int64_t bands_a = 0;
-    for (int j = 0; j < 6; ++j) bands_a += (rows[j] + 63) / 64;
+    int64_t tiles_a = 0;
+    for (int j = 0; j < 6; ++j) tiles_a += (rows[j] + kSkinnyRows - 1) / kSkinnyRows;
     size_t split = 0;
     if (chunk <= 64) {
         for (int j = 0; j < PF_NPROJ; ++j) {
             const int64_t K = j < 6 ? H : F;
-            L.plan[j] = plan_skinny(rows[j], K, j < 6 ? bands_a : (H + 63) / 64);
+            L.plan[j] = plan_skinny(rows[j], K, j < 6 ? tiles_a : (H + kSkinnyRows - 1) / kSkinnyRows);
             split += split_bytes(rows[j], chunk, L.plan[j]);
         }
     }
@@ -242,6 +248,99 @@ pf_status validate_moe(const pf_moe* m)
     return PF_OK;
 }
 
+
+// Algorithmic bytes of one product: weights, their scales, the quantised tokens
+// and their scales read once, the f32 outputs written once.
+double product_bytes(int64_t N, int64_t K, int64_t M)
+{
+    return (double)N * K + 4.0 * N + (double)M * K + 4.0 * M + 4.0 * M * N;
+}
+
+// Launch bookkeeping of pf_prefill_stack: counts launches and algorithmic
+// bytes per kernel class and, when asked, brackets every launch with a pair of
+// HIP events on the caller's stream to time it.
+class Recorder {
+public:
+    enum Kind { kQuant = 0, kProduct = 1 };
+    Recorder(hipStream_t s, bool on, bool timed) : s_(s), on_(on), timed_(timed) {}
+    ~Recorder()
+    {
+        for (auto& e : events_) (void)hipEventDestroy(e);
+        if (t0_) (void)hipEventDestroy(t0_);
+        if (t1_) (void)hipEventDestroy(t1_);
+    }
+    pf_status begin()
+    {
+        if (!on_) return PF_OK;
+        if (hipEventCreate(&t0_) != hipSuccess || hipEventCreate(&t1_) != hipSuccess ||
+            hipEventRecord(t0_, s_) != hipSuccess)
+            return fail();
+        return PF_OK;
+    }
+    template <class F>
+    pf_status run(Kind k, double bytes, F&& launch)
+    {
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        if (timed_) {
+            if (hipEventCreate(&e0) != hipSuccess) return fail();
+            events_.push_back(e0);
+            if (hipEventCreate(&e1) != hipSuccess) return fail();
+            events_.push_back(e1);
+            if (hipEventRecord(e0, s_) != hipSuccess) return fail();
+        }
+        const pf_status st = launch();
+        if (st) return st;
+        if (timed_ && hipEventRecord(e1, s_) != hipSuccess) return fail();
+        ++launches_[k];
+        bytes_[k] += bytes;
+        if (timed_) kinds_.push_back(k);
+        return PF_OK;
+    }
+    pf_status end()
+    {
+        if (!on_) return PF_OK;
+        if (hipEventRecord(t1_, s_) != hipSuccess || hipEventSynchronize(t1_) != hipSuccess)
+            return fail();
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, t0_, t1_) != hipSuccess) return fail();
+        total_ms_ = ms;
+        for (size_t i = 0; i < kinds_.size(); ++i) {
+            if (hipEventElapsedTime(&ms, events_[2 * i], events_[2 * i + 1]) != hipSuccess)
+                return fail();
+            ms_[kinds_[i]] += ms;
+        }
+        return PF_OK;
+    }
+    void fill(pf_stack_stats* st) const
+    {
+        st->launches = launches_[0] + launches_[1];
+        st->alg_bytes = bytes_[0] + bytes_[1];
+        st->elapsed_ms = total_ms_;
+        st->quant_launches = launches_[kQuant];
+        st->product_launches = launches_[kProduct];
+        st->quant_alg_bytes = bytes_[kQuant];
+        st->product_alg_bytes = bytes_[kProduct];
+        st->quant_ms = timed_ ? ms_[kQuant] : 0.0;
+        st->product_ms = timed_ ? ms_[kProduct] : 0.0;
+    }
+
+private:
+    pf_status fail()
+    {
+        (void)hipGetLastError();
+        return PF_ELAUNCH;
+    }
+    hipStream_t s_;
+    bool on_, timed_;
+    hipEvent_t t0_ = nullptr, t1_ = nullptr;
+    std::vector<hipEvent_t> events_;
+    std::vector<int> kinds_;
+    int64_t launches_[2] = {0, 0};
+    double bytes_[2] = {0.0, 0.0};
+    double ms_[2] = {0.0, 0.0};
+    double total_ms_ = 0.0;
+};
+
 }  // namespace
 
 // ===========================================================================
@@ -304,7 +403,7 @@ pf_status pf_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int
 size_t pf_gemm_i8_chunk_workspace(int64_t N, int64_t K, int64_t M)
 {
     if (N <= 0 || !valid_k(K) || M <= 0 || M > 64) return 0;
-    const SkinnyPlan p = plan_skinny(N, K, (N + 63) / 64);
+    const SkinnyPlan p = plan_skinny(N, K, (N + kSkinnyRows - 1) / kSkinnyRows);
     return split_bytes(N, M, p);
 }
 
@@ -329,11 +428,8 @@ pf_status pf_gemm_i8_chunk(const int8_t* W, const float* w_scale, int64_t N, int
         std::memset(&set, 0, sizeof(set));
         set.nprob = 1;
         if (M <= 64) {
-            SkinnyPlan p = plan_skinny(N, K, (N + 63) / 64);
-            if (!workspace || ws_bytes < split_bytes(N, M, p)) {
-                p.splits = 1;
-                p.kb_per_split = (int)(K / 64);
-            }
+            SkinnyPlan p = plan_skinny(N, K, (N + kSkinnyRows - 1) / kSkinnyRows);
+            if (!workspace || ws_bytes < split_bytes(N, M, p)) p = unsplit(N, K);
             if (workspace && overlap(workspace, ws_bytes, y, yb)) return PF_EINVAL;
             char* scratch = static_cast<char*>(workspace);
             make_skinny(set.p[0], W, w_scale, N, K, xq, K, a_scale, M, y, N, p, scratch, M);
@@ -364,8 +460,7 @@ pf_status pf_gemv_i8(const int8_t* W, const float* w_scale, int64_t N, int64_t K
         std::memset(&set, 0, sizeof(set));
         set.nprob = 1;
         char* none = nullptr;
-        const SkinnyPlan p{(int)((N + 63) / 64), 1, (int)(K / 64)};
-        make_skinny(set.p[0], W, w_scale, N, K, xq, K, a_scale, 1, y, N, p, none, 1);
+        make_skinny(set.p[0], W, w_scale, N, K, xq, K, a_scale, 1, y, N, unsplit(N, K), none, 1);
         finish_set(set, 0);
         return launched(launch_gemv(set, (hipStream_t)stream));
     } catch (...) {
@@ -388,8 +483,12 @@ pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int
         if (P < 0 || chunk <= 0 || chunk > INT32_MAX || P > INT32_MAX) return PF_EINVAL;
         const int64_t L = stack->n_layers, H = stack->hidden, F = stack->ffn;
         const int64_t NT = 5 * H + 2 * F;
+        const bool timed = stats && stats->time_kernels;
         if (P == 0) {
-            if (stats) std::memset(stats, 0, sizeof(*stats));
+            if (stats) {
+                std::memset(stats, 0, sizeof(*stats));
+                stats->time_kernels = timed ? 1 : 0;
+            }
             return PF_OK;
         }
         if (!x || !y || !aligned16(x) || !aligned4(y) || (proj && !aligned16(proj)))
@@ -417,15 +516,8 @@ pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int
         for (int j = 0; j < PF_NPROJ; ++j) offs[j + 1] = offs[j] + rows[j];
         const bool per_token = per_token_mode();
 
-        hipEvent_t ev0 = nullptr, ev1 = nullptr;
-        if (stats) {
-            if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess)
-                return PF_ELAUNCH;
-            if (hipEventRecord(ev0, s) != hipSuccess) return PF_ELAUNCH;
-        }
-        int64_t launches = 0;
-        double alg = 0.0;
-        pf_status st = PF_OK;
+        Recorder rec(s, stats != nullptr, timed);
+        pf_status st = rec.begin();
         const int64_t step = per_token ? 1 : ch;
         for (int64_t c0 = 0; c0 < P && st == PF_OK; c0 += step) {
             const int64_t M = std::min(step, P - c0);
@@ -433,52 +525,51 @@ pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int
                 const pf_layer& ly = stack->layers[l];
                 float* prow = proj ? proj + ((size_t)l * P + c0) * NT : pscratch;
                 // input of this layer: x for layer 0, else the previous down output
-                const float* hin;
-                int64_t ldh;
-                if (l == 0) {
-                    hin = x + c0 * H;
-                    ldh = H;
-                } else {
+                const float* hin = x + c0 * H;
+                int64_t ldh = H;
+                if (l > 0) {
                     hin = (proj ? proj + ((size_t)(l - 1) * P + c0) * NT : pscratch) + offs[6];
                     ldh = NT;
                 }
-                st = launched(launch_quantize(hin, ldh, (int)M, (int)H, a, sa, s));
-                ++launches;
-                alg += (double)M * H * 4 + (double)M * H + M * 4.0;
+                double bytes = (double)M * H * 4 + (double)M * H + M * 4.0;
+                st = rec.run(Recorder::kQuant, bytes, [&] {
+                    return launched(launch_quantize(hin, ldh, (int)M, (int)H, a, sa, s));
+                });
                 if (st) break;
                 GemmSet set;
                 std::memset(&set, 0, sizeof(set));
                 set.nprob = 6;
                 char* scratch = ws + lay.split;
+                bytes = 0.0;
                 for (int j = 0; j < 6; ++j) {
                     SkinnyPlan p = lay.plan[j];
-                    if (per_token) p = SkinnyPlan{(int)((rows[j] + 63) / 64), 1, (int)(H / 64)};
-                    if (per_token || M <= 64) {
+                    if (per_token) p = unsplit(rows[j], H);
+                    if (per_token || M <= 64)
                         make_skinny(set.p[j], ly.W[j], ly.w_scale[j], rows[j], H, a, H, sa, M,
                                     prow + offs[j], NT, p, scratch, ch);
-                    } else {
+                    else
                         make_tiled(set.p[j], ly.W[j], ly.w_scale[j], rows[j], H, a, H, sa, M,
                                    prow + offs[j], NT);
+                    bytes += product_bytes(rows[j], H, M);
+                }
+                st = rec.run(Recorder::kProduct, bytes, [&] {
+                    if (per_token) {
+                        finish_set(set, 0);
+                        return launched(launch_gemv(set, s));
                     }
-                    alg += (double)rows[j] * H + rows[j] * 4.0 + (double)M * H + (double)M * rows[j] * 4;
-                }
-                if (per_token) {
-                    finish_set(set, 0);
-                    st = launched(launch_gemv(set, s));
-                } else {
-                    st = run_products(set, M, s);
-                }
-                ++launches;
+                    return run_products(set, M, s);
+                });
                 if (st) break;
-                st = launched(launch_quantize(prow + offs[5], NT, (int)M, (int)F, b, sb, s));
-                ++launches;
-                alg += (double)M * F * 4 + (double)M * F + M * 4.0;
+                bytes = (double)M * F * 4 + (double)M * F + M * 4.0;
+                st = rec.run(Recorder::kQuant, bytes, [&] {
+                    return launched(launch_quantize(prow + offs[5], NT, (int)M, (int)F, b, sb, s));
+                });
                 if (st) break;
                 GemmSet dn;
                 std::memset(&dn, 0, sizeof(dn));
                 dn.nprob = 1;
                 SkinnyPlan p = lay.plan[6];
-                if (per_token) p = SkinnyPlan{(int)((H + 63) / 64), 1, (int)(F / 64)};
+                if (per_token) p = unsplit(H, F);
                 if (per_token || M <= 64)
                     make_skinny(dn.p[0], ly.W[6], ly.w_scale[6], H, F, b, F, sb, M, prow + offs[6], NT,
                                 p, scratch, ch);
@@ -488,35 +579,23 @@ pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int
                     dn.p[0].Y2 = y + c0 * H;
                     dn.p[0].ldy2 = H;
                 }
-                alg += (double)H * F + H * 4.0 + (double)M * F + (double)M * H * 4;
-                if (per_token) {
-                    finish_set(dn, 0);
-                    st = launched(launch_gemv(dn, s));
-                } else {
-                    st = run_products(dn, M, s);
-                }
-                ++launches;
+                st = rec.run(Recorder::kProduct, product_bytes(H, F, M), [&] {
+                    if (per_token) {
+                        finish_set(dn, 0);
+                        return launched(launch_gemv(dn, s));
+                    }
+                    return run_products(dn, M, s);
+                });
             }
         }
-        if (st != PF_OK) {
-            if (ev0) (void)hipEventDestroy(ev0);
-            if (ev1) (void)hipEventDestroy(ev1);
-            return st;
-        }
-        if (stats) {
+        if (st == PF_OK) st = rec.end();
+        if (st == PF_OK && stats) {
             std::memset(stats, 0, sizeof(*stats));
-            float ms = 0.0f;
-            if (hipEventRecord(ev1, s) != hipSuccess || hipEventSynchronize(ev1) != hipSuccess ||
-                hipEventElapsedTime(&ms, ev0, ev1) != hipSuccess)
-                st = PF_ELAUNCH;
-            (void)hipEventDestroy(ev0);
-            (void)hipEventDestroy(ev1);
+            stats->time_kernels = timed ? 1 : 0;
+            stats->per_token_mode = per_token ? 1 : 0;
             stats->chunks = per_token ? P : (P + ch - 1) / ch;
             stats->tail_tokens = per_token ? 1 : P - (stats->chunks - 1) * ch;
-            stats->launches = launches;
-            stats->alg_bytes = alg;
-            stats->elapsed_ms = ms;
-            stats->per_token_mode = per_token ? 1 : 0;
+            rec.fill(stats);
         }
         return st;
     } catch (...) {

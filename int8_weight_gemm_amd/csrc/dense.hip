@@ -147,113 +147,103 @@ hipError_t launch_gemv(const GemmSet& set, hipStream_t s)
 
 // ---------------------------------------------------------------------------
 // Skinny product (M <= 64): v_mfma_i32_16x16x64_i8 with the weights as the A
-// operand (16 rows x 64 k per wave and instruction) and the tokens as B.
-// Workgroup = 4 waves = 64 weight rows x one K slice; the chunk's tokens for the
-// slice are staged in LDS in pieces of kSkPiece k-blocks and read by all 4 waves.
-// Each lane loads its A operand (16 bytes of one row) straight from HBM; the
-// four lanes l, l+16, l+32, l+48 cover 64 contiguous bytes of a row.
-// The int32 sum is order-free, so any K split gives the per-token bytes; split
-// partial sums meet in an int32 accumulator (agent-scope atomics) and the last
-// workgroup of a row band applies the epilogue and re-zeroes the accumulator.
-constexpr int kSkPiece = 16;                       // k-blocks (of 64 bytes) per LDS piece
-constexpr int kSkStride = kSkPiece * 64 + 16;      // LDS bytes per token row (padded)
+// operand (lane l holds 16 bytes of weight row l%16) and the tokens as B (lane l
+// holds the same 16 k positions of token l%16).  A workgroup owns 16 weight rows
+// and all M tokens; its 4 waves take a contiguous quarter of the K range each and
+// load both operands from global memory straight into registers, kSkStage
+// k-blocks (of 64 bytes) per stage; the four lanes l, l+16, l+32, l+48 read 64
+// contiguous bytes of a row.  The four partial int32 tiles are summed through
+// LDS (integer sums: any order gives the same bits).  When one launch has too
+// few rows to fill the chip, the K range is also split across workgroups: each
+// writes its int32 partial tile to the workspace and k_split_reduce sums the
+// partials and applies the epilogue.
+constexpr int kSkStage = 8;
 
 template <int TB>
 __global__ __launch_bounds__(256) void k_gemm_skinny(GemmSet set)
 {
-    __shared__ __attribute__((aligned(16))) int8_t xl[16 * TB * kSkStride];
-    __shared__ int s_last;
+    __shared__ v4i red[4][TB][64];
     const GemmProb P = find_prob(set, blockIdx.x);
     const int local = blockIdx.x - P.tile_begin;
     const int split = local % P.splits;
     const int tn = local / P.splits;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nw0 = tn * 64 + wave * 16;
+    const int n0 = tn * 16;
     const int nkb = P.K >> 6;
-    const int kb0 = split * P.kb_per_split;
-    const int kb1 = min(kb0 + P.kb_per_split, nkb);
-    const int arow = min(nw0 + (lane & 15), P.N - 1);
-    const int8_t* wp = P.W + (int64_t)arow * P.K + ((lane >> 4) << 4);
-    const int boff = (lane & 15) * kSkStride + ((lane >> 4) << 4);
-
+    const int s0 = split * P.kb_per_split;
+    const int len = min(P.kb_per_split, nkb - s0);
+    const int kb0 = s0 + (len * wave) / 4, kb1 = s0 + (len * (wave + 1)) / 4;
+    const int koff = (lane >> 4) << 4;
+    const int8_t* wp = P.W + (int64_t)min(n0 + (lane & 15), P.N - 1) * P.K + koff;
+    const int8_t* xp[TB];
+    bool xok[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        const int t = tb * 16 + (lane & 15);
+        xok[tb] = t < P.M;
+        xp[tb] = P.X + (int64_t)(xok[tb] ? t : 0) * P.ldx + koff;
+    }
     v4i acc[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) acc[tb] = v4i{0, 0, 0, 0};
 
-    for (int kp = kb0; kp < kb1; kp += kSkPiece) {
-        const int npc = min(kSkPiece, kb1 - kp);
-        v4i a[kSkPiece];
+    for (int kb = kb0; kb < kb1; kb += kSkStage) {
+        const int n = min(kSkStage, kb1 - kb);
+        v4i a[kSkStage];
+        v4i b[kSkStage][TB];
 #pragma unroll
-        for (int i = 0; i < kSkPiece; ++i)
-            if (i < npc) a[i] = ld16(wp + (int64_t)(kp + i) * 64);
-        __syncthreads();
-        const int cpr = npc * 4;
-        for (int idx = threadIdx.x; idx < 16 * TB * cpr; idx += 256) {
-            const int t = idx / cpr, c = idx - t * cpr;
-            v4i v = v4i{0, 0, 0, 0};
-            if (t < P.M) v = ld16(P.X + (int64_t)t * P.ldx + (int64_t)kp * 64 + c * 16);
-            st16(xl + t * kSkStride + c * 16, v);
+        for (int i = 0; i < kSkStage; ++i) {
+            if (i < n) {
+                a[i] = ld16(wp + (int64_t)(kb + i) * 64);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+                    b[i][tb] = xok[tb] ? ld16(xp[tb] + (int64_t)(kb + i) * 64) : v4i{0, 0, 0, 0};
+            }
         }
-        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < kSkPiece; ++i) {
-            if (i < npc) {
+        for (int i = 0; i < kSkStage; ++i) {
+            if (i < n) {
 #pragma unroll
-                for (int tb = 0; tb < TB; ++tb) {
-                    const v4i b = *reinterpret_cast<const v4i*>(xl + tb * 16 * kSkStride + boff + i * 64);
-                    acc[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b, acc[tb], 0, 0, 0);
-                }
+                for (int tb = 0; tb < TB; ++tb)
+                    acc[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[i][tb], acc[tb], 0, 0, 0);
             }
         }
     }
 
-    // Lane l holds rows nw0 + 4*(l/16) + r (r = 0..3) of token column l%16.
-    const int nr = nw0 + ((lane >> 4) << 2);
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) red[wave][tb][lane] = acc[tb];
+    __syncthreads();
+    if (wave >= TB) return;
+    // wave w finishes token block w.  Lane l holds rows nr .. nr+3 of token t.
+    const int tb = wave;
+    const v4i sum = red[0][tb][lane] + red[1][tb][lane] + red[2][tb][lane] + red[3][tb][lane];
+    const int t = tb * 16 + (lane & 15);
+    const int nr = n0 + ((lane >> 4) << 2);
+    if (t >= P.M) return;
     if (P.splits == 1) {
+        const float xs = P.xs[t];
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            const int t = tb * 16 + (lane & 15);
-            if (t < P.M) {
-                const float xs = P.xs[t];
+        for (int r = 0; r < 4; ++r)
+            if (nr + r < P.N) store_out(P, t, nr + r, epilogue(sum[r], P.ws[nr + r], xs));
+    } else {
+        int* part = P.acc + ((int64_t)split * P.M + t) * P.N;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (nr + r < P.N) store_out(P, t, nr + r, epilogue(acc[tb][r], P.ws[nr + r], xs));
-            }
-        }
-        return;
+        for (int r = 0; r < 4; ++r)
+            if (nr + r < P.N) part[nr + r] = sum[r];
     }
+}
 
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-        const int t = tb * 16 + (lane & 15);
-        if (t < P.M) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (nr + r < P.N) atomic_add_agent(P.acc + (int64_t)t * P.N + nr + r, acc[tb][r]);
-        }
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned old = __hip_atomic_fetch_add(P.cnt + tn, 1u, __ATOMIC_ACQ_REL,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old == (unsigned)(P.splits - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const int rows = min(64, P.N - tn * 64);
-    for (int idx = threadIdx.x; idx < P.M * 64; idx += 256) {
-        const int t = idx >> 6, n = tn * 64 + (idx & 63);
-        if ((idx & 63) < rows) {
-            int* pa = P.acc + (int64_t)t * P.N + n;
-            const int v = load_agent(pa);
-            store_out(P, t, n, epilogue(v, P.ws[n], P.xs[t]));
-            store_agent(pa, 0);
-        }
-    }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(P.cnt + tn, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Sum of the split partials [splits][M][N] and the epilogue; one thread per
+// output.  Here tile_begin counts blocks of 256 outputs.
+__global__ __launch_bounds__(256) void k_split_reduce(GemmSet set)
+{
+    const GemmProb P = find_prob(set, blockIdx.x);
+    const int64_t idx = (int64_t)(blockIdx.x - P.tile_begin) * 256 + threadIdx.x;
+    if (idx >= (int64_t)P.M * P.N) return;
+    const int t = (int)(idx / P.N), n = (int)(idx - (int64_t)t * P.N);
+    int v = 0;
+    for (int sp = 0; sp < P.splits; ++sp) v += P.acc[((int64_t)sp * P.M + t) * P.N + n];
+    store_out(P, t, n, epilogue(v, P.ws[n], P.xs[t]));
 }
 
 hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t s)
@@ -267,6 +257,20 @@ hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t 
         case 4: hipLaunchKernelGGL(k_gemm_skinny<4>, g, b, 0, s, set); break;
         default: return hipErrorInvalidValue;
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // reduce launch over the split problems only
+    GemmSet r = set;
+    int begin = 0;
+    for (int i = 0; i < r.nprob; ++i) {
+        r.p[i].tile_begin = begin;
+        if (r.p[i].splits > 1) begin += (int)(((int64_t)r.p[i].M * r.p[i].N + 255) / 256);
+    }
+    if (begin == 0) return hipSuccess;
+    // problems without splits get no blocks: find_prob never selects them
+    // because their tile_begin equals the next problem's.
+    r.total_tiles = begin;
+    hipLaunchKernelGGL(k_split_reduce, dim3(begin), b, 0, s, r);
     return hipGetLastError();
 }
 

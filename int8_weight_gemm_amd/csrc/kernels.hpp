@@ -15,15 +15,14 @@ struct GemmProb {
     const float* xs;      // [M]
     float* Y;             // [M][ldy]
     float* Y2;            // optional second copy of the output [M][ldy2] (or null)
-    int* acc;             // split-K int32 accumulator [M][N], zero between calls (or null)
-    unsigned* cnt;        // split-K arrival counters [tiles_n], zero between calls (or null)
+    int* acc;             // split-K int32 partials [splits][M][N] (or null)
     int64_t ldx;          // bytes between token rows of X
     int64_t ldy;          // floats between token rows of Y
     int64_t ldy2;         // floats between token rows of Y2
     int N, K, M;
-    int tiles_n;          // row tiles
+    int tiles_n;          // row tiles (16 rows skinny, 128 rows tiled)
     int tiles_m;          // token tiles (tiled kernel only)
-    int splits;           // K splits (skinny kernel only)
+    int splits;           // K splits across workgroups (skinny kernel only)
     int kb_per_split;     // 64-byte k-blocks per split
     int tile_begin;       // first flat workgroup index of this problem
 };

@@ -106,15 +106,17 @@ def test_skinny_tails(M, split):
     np.testing.assert_array_equal(host(y), oracle.linear(W, ws, q, s))
 
 
-def test_split_workspace_reused_and_left_zero():
+def test_split_workspace_reused_with_garbage():
+    # the split partials are overwritten each call: any workspace contents work
     N, K, M = 1024, 4096, 32
     W, ws, q, s = _proj(N, K, M, 41)
-    wsp = pf.workspace(pf.gemm_i8_chunk_workspace(N, K, M))
+    nb = pf.gemm_i8_chunk_workspace(N, K, M)
+    assert nb > 0
+    wsp = torch.randint(0, 255, (nb,), dtype=torch.uint8, device="cuda")
     args = (dev(W), dev(ws), dev(q), dev(s))
     ref = oracle.linear(W, ws, q, s)
     for _ in range(5):
         np.testing.assert_array_equal(host(pf.gemm_i8_chunk(*args, ws=wsp)), ref)
-    assert int(host(wsp).astype(np.int64).sum()) == 0 and not host(wsp).any()
 
 
 @pytest.mark.parametrize("M", [65, 100, 128, 129, 300])
