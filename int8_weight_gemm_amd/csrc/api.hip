@@ -153,37 +153,28 @@ pf_status run_products(GemmSet& set, int64_t M, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
-// Stack workspace layout (per chunk): quantised input a [chunk][H], quantised
-// up b [chunk][F], their scales, the projection rows [chunk][5H+2F] when the
-// caller keeps none, and the split-K scratch of the seven products.
+// Stack workspace: `slots` chunk slots, each with the quantised layer input
+// a [chunk][H], the quantised up output b [chunk][F], their scales, and the
+// projection rows [chunk][5H+2F] used when the caller keeps none.  A chunk in
+// flight owns one slot for all of its layers.
 struct StackLayout {
-    size_t a, b, sa, sb, proj, split, total;
-    SkinnyPlan plan[PF_NPROJ];
+    int slots;
+    size_t a, b, sa, sb, proj, slot_bytes, total;
 };
 
-StackLayout stack_layout(int64_t H, int64_t F, int64_t chunk)
+StackLayout stack_layout(int64_t L, int64_t H, int64_t F, int64_t chunk)
 {
-    StackLayout L{};
+    StackLayout S{};
+    S.slots = (int)std::min<int64_t>(L, kMaxPairs);
     size_t o = 0;
-    L.a = o; o += round_up((size_t)chunk * H, kAlign);
-    L.b = o; o += round_up((size_t)chunk * F, kAlign);
-    L.sa = o; o += round_up((size_t)chunk * 4, kAlign);
-    L.sb = o; o += round_up((size_t)chunk * 4, kAlign);
-    L.proj = o; o += round_up((size_t)chunk * (5 * H + 2 * F) * 4, kAlign);
-    L.split = o;
-    const int64_t rows[PF_NPROJ] = {H, H, H, H, F, F, H};
-    int64_t tiles_a = 0;
-    for (int j = 0; j < 6; ++j) tiles_a += (rows[j] + kSkinnyRows - 1) / kSkinnyRows;
-    size_t split = 0;
-    if (chunk <= 64) {
-        for (int j = 0; j < PF_NPROJ; ++j) {
-            const int64_t K = j < 6 ? H : F;
-            L.plan[j] = plan_skinny(rows[j], K, j < 6 ? tiles_a : (H + kSkinnyRows - 1) / kSkinnyRows);
-            split += split_bytes(rows[j], chunk, L.plan[j]);
-        }
-    }
-    L.total = o + split;
-    return L;
+    S.a = o; o += round_up((size_t)chunk * H, kAlign);
+    S.b = o; o += round_up((size_t)chunk * F, kAlign);
+    S.sa = o; o += round_up((size_t)chunk * 4, kAlign);
+    S.sb = o; o += round_up((size_t)chunk * 4, kAlign);
+    S.proj = o; o += round_up((size_t)chunk * (5 * H + 2 * F) * 4, kAlign);
+    S.slot_bytes = o;
+    S.total = o * S.slots;
+    return S;
 }
 
 pf_status validate_stack(const pf_stack* st)
@@ -341,6 +332,212 @@ private:
     double total_ms_ = 0.0;
 };
 
+
+// One pf_prefill_stack call.  Two schedules give the same bytes:
+//   sweep():     chunk c reaches layer l at step start(c) + l, so one step runs
+//                the (chunk, layer) pairs of a diagonal together: each pair
+//                still reads its own layer's weights once for its chunk, and a
+//                launch streams up to 16 layers' weights at once.  At most
+//                `slots` chunks are in flight; chunk c waits for chunk c - slots.
+//                Per step: quantise the layer inputs, the six K = H products,
+//                quantise up, the down product.
+//   per_token(): one token at a time, one GEMV per projection (the baseline).
+struct StackRun {
+    const pf_stack* st;
+    const float* x;
+    int64_t P, ch;
+    float* y;
+    float* proj;
+    char* ws;
+    StackLayout lay;
+    hipStream_t s;
+
+    int64_t H() const { return st->hidden; }
+    int64_t F() const { return st->ffn; }
+    int64_t NT() const { return 5 * st->hidden + 2 * st->ffn; }
+    char* slot(int64_t c) const { return ws + (size_t)(c % lay.slots) * lay.slot_bytes; }
+    // projection rows of (chunk c, layer l): [M][NT], q..down concatenated
+    float* rows(int64_t c, int64_t l) const
+    {
+        if (proj) return proj + ((size_t)l * P + (size_t)c * ch) * NT();
+        return reinterpret_cast<float*>(slot(c) + lay.proj);
+    }
+    int64_t offs(int j) const
+    {
+        const int64_t o[PF_NPROJ] = {0, H(), 2 * H(), 3 * H(), 4 * H(), 4 * H() + F(), 4 * H() + 2 * F()};
+        return o[j];
+    }
+    int64_t start(int64_t c) const
+    {
+        const int64_t L = st->n_layers, S = lay.slots;
+        return c + (c / S) * (L - S);
+    }
+
+    pf_status sweep(Recorder& rec)
+    {
+        const int64_t L = st->n_layers, C = (P + ch - 1) / ch;
+        const int64_t nsteps = start(C - 1) + L;
+        const bool skinny = ch <= 64;
+        const int64_t rowsA[6] = {H(), H(), H(), H(), F(), F()};
+        int64_t c_lo = 0;
+        for (int64_t step = 0; step < nsteps; ++step) {
+            while (c_lo < C && start(c_lo) + L <= step) ++c_lo;
+            std::vector<int64_t> cs;
+            for (int64_t c = c_lo; c < C && start(c) <= step; ++c) cs.push_back(c);
+            if (cs.empty()) continue;
+            QuantStep qa, qd;
+            StackStep A, D;
+            std::memset(&qa, 0, sizeof(qa));
+            std::memset(&qd, 0, sizeof(qd));
+            std::memset(&A, 0, sizeof(A));
+            std::memset(&D, 0, sizeof(D));
+            qa.npairs = qd.npairs = A.npairs = D.npairs = (int)cs.size();
+            qa.K = (int)H();
+            qd.K = (int)F();
+            A.nproj = 6;
+            A.K = (int)H();
+            D.nproj = 1;
+            D.K = (int)F();
+            const int tm = (int)((ch + 127) / 128);
+            A.tiles_m = D.tiles_m = tm;
+            A.ldx = H();
+            D.ldx = F();
+            A.ldy = D.ldy = NT();
+            D.ldy2 = H();
+            for (int j = 0; j < 6; ++j) {
+                A.rows[j] = (int)rowsA[j];
+                A.yoff[j] = (int)offs(j);
+                const int64_t t = skinny ? (rowsA[j] + 15) / 16 : ((rowsA[j] + 127) / 128) * tm;
+                A.tile_off[j + 1] = A.tile_off[j] + (int)t;
+            }
+            D.rows[0] = (int)H();
+            D.yoff[0] = (int)offs(6);
+            D.tile_off[1] = (int)(skinny ? (H() + 15) / 16 : ((H() + 127) / 128) * tm);
+            double qa_bytes = 0, qd_bytes = 0, a_bytes = 0, d_bytes = 0;
+            int rows_total = 0;
+            for (size_t i = 0; i < cs.size(); ++i) {
+                const int64_t c = cs[i], l = step - start(c);
+                const int64_t c0 = c * ch, M = std::min(ch, P - c0);
+                const pf_layer& ly = st->layers[l];
+                char* sl = slot(c);
+                int8_t* a = reinterpret_cast<int8_t*>(sl + lay.a);
+                int8_t* b = reinterpret_cast<int8_t*>(sl + lay.b);
+                float* sa = reinterpret_cast<float*>(sl + lay.sa);
+                float* sb = reinterpret_cast<float*>(sl + lay.sb);
+                float* out = rows(c, l);
+                QuantPair& q0 = qa.pair[i];
+                if (l == 0) {
+                    q0.src = x + c0 * H();
+                    q0.ld = H();
+                } else {
+                    q0.src = rows(c, l - 1) + offs(6);
+                    q0.ld = NT();
+                }
+                q0.q = a;
+                q0.s = sa;
+                q0.row0 = rows_total;
+                QuantPair& q1 = qd.pair[i];
+                q1.src = out + offs(5);
+                q1.ld = NT();
+                q1.q = b;
+                q1.s = sb;
+                q1.row0 = rows_total;
+                rows_total += (int)M;
+                StepPair& pa = A.pair[i];
+                for (int j = 0; j < 6; ++j) {
+                    pa.W[j] = ly.W[j];
+                    pa.ws[j] = ly.w_scale[j];
+                    a_bytes += product_bytes(rowsA[j], H(), M);
+                }
+                pa.X = a;
+                pa.xs = sa;
+                pa.Y = out;
+                pa.M = (int)M;
+                StepPair& pd = D.pair[i];
+                pd.W[0] = ly.W[6];
+                pd.ws[0] = ly.w_scale[6];
+                pd.X = b;
+                pd.xs = sb;
+                pd.Y = out;
+                pd.Y2 = l == L - 1 ? y + c0 * H() : nullptr;
+                pd.M = (int)M;
+                d_bytes += product_bytes(H(), F(), M);
+                qa_bytes += (double)M * H() * 5 + M * 4.0;
+                qd_bytes += (double)M * F() * 5 + M * 4.0;
+            }
+            qa.total_rows = qd.total_rows = rows_total;
+            const int tb = (int)((ch + 15) / 16);
+            pf_status r = rec.run(Recorder::kQuant, qa_bytes,
+                                  [&] { return launched(launch_quantize_step(qa, s)); });
+            if (!r) r = rec.run(Recorder::kProduct, a_bytes, [&] {
+                return launched(skinny ? launch_gemm_skinny_step(A, tb, s) : launch_gemm_tiled_step(A, s));
+            });
+            if (!r) r = rec.run(Recorder::kQuant, qd_bytes,
+                                [&] { return launched(launch_quantize_step(qd, s)); });
+            if (!r) r = rec.run(Recorder::kProduct, d_bytes, [&] {
+                return launched(skinny ? launch_gemm_skinny_step(D, tb, s) : launch_gemm_tiled_step(D, s));
+            });
+            if (r) return r;
+        }
+        return PF_OK;
+    }
+
+    pf_status per_token(Recorder& rec)
+    {
+        const int64_t L = st->n_layers;
+        char* sl = slot(0);
+        int8_t* a = reinterpret_cast<int8_t*>(sl + lay.a);
+        int8_t* b = reinterpret_cast<int8_t*>(sl + lay.b);
+        float* sa = reinterpret_cast<float*>(sl + lay.sa);
+        float* sb = reinterpret_cast<float*>(sl + lay.sb);
+        float* scratch = reinterpret_cast<float*>(sl + lay.proj);
+        const int64_t rowsA[6] = {H(), H(), H(), H(), F(), F()};
+        char* none = nullptr;
+        for (int64_t t = 0; t < P; ++t) {
+            for (int64_t l = 0; l < L; ++l) {
+                const pf_layer& ly = st->layers[l];
+                float* out = proj ? proj + ((size_t)l * P + t) * NT() : scratch;
+                const float* hin = l == 0 ? x + t * H()
+                                          : (proj ? proj + ((size_t)(l - 1) * P + t) * NT() : scratch) + offs(6);
+                pf_status r = rec.run(Recorder::kQuant, (double)H() * 5 + 4, [&] {
+                    return launched(launch_quantize(hin, H(), 1, (int)H(), a, sa, s));
+                });
+                if (r) return r;
+                GemmSet set;
+                std::memset(&set, 0, sizeof(set));
+                set.nprob = 6;
+                double bytes = 0;
+                for (int j = 0; j < 6; ++j) {
+                    make_skinny(set.p[j], ly.W[j], ly.w_scale[j], rowsA[j], H(), a, H(), sa, 1,
+                                out + offs(j), NT(), unsplit(rowsA[j], H()), none, 1);
+                    bytes += product_bytes(rowsA[j], H(), 1);
+                }
+                finish_set(set, 0);
+                r = rec.run(Recorder::kProduct, bytes, [&] { return launched(launch_gemv(set, s)); });
+                if (r) return r;
+                r = rec.run(Recorder::kQuant, (double)F() * 5 + 4, [&] {
+                    return launched(launch_quantize(out + offs(5), NT(), 1, (int)F(), b, sb, s));
+                });
+                if (r) return r;
+                GemmSet dn;
+                std::memset(&dn, 0, sizeof(dn));
+                dn.nprob = 1;
+                make_skinny(dn.p[0], ly.W[6], ly.w_scale[6], H(), F(), b, F(), sb, 1, out + offs(6),
+                            NT(), unsplit(H(), F()), none, 1);
+                if (l == L - 1) {
+                    dn.p[0].Y2 = y + t * H();
+                    dn.p[0].ldy2 = H();
+                }
+                finish_set(dn, 0);
+                r = rec.run(Recorder::kProduct, product_bytes(H(), F(), 1),
+                            [&] { return launched(launch_gemv(dn, s)); });
+                if (r) return r;
+            }
+        }
+        return PF_OK;
+    }
+};
+
 }  // namespace
 
 // ===========================================================================
@@ -471,7 +668,7 @@ pf_status pf_gemv_i8(const int8_t* W, const float* w_scale, int64_t N, int64_t K
 size_t pf_prefill_stack_workspace(const pf_stack* stack, int64_t chunk)
 {
     if (!stack || stack->hidden <= 0 || stack->ffn <= 0 || chunk <= 0) return 0;
-    return stack_layout(stack->hidden, stack->ffn, chunk).total;
+    return stack_layout(stack->n_layers, stack->hidden, stack->ffn, chunk).total;
 }
 
 pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int64_t chunk,
@@ -497,97 +694,19 @@ pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int
         if (overlap(x, xb, y, xb) || overlap(proj, pb, x, xb) || overlap(proj, pb, y, xb))
             return PF_EINVAL;
         const int64_t ch = std::min(chunk, P);
-        const StackLayout lay = stack_layout(H, F, ch);
+        const StackLayout lay = stack_layout(L, H, F, ch);
         if (!workspace || ws_bytes < lay.total) return PF_EWORKSPACE;
         if (!aligned16(workspace)) return PF_EINVAL;
         if (overlap(workspace, ws_bytes, x, xb) || overlap(workspace, ws_bytes, y, xb) ||
             overlap(workspace, ws_bytes, proj, pb))
             return PF_EINVAL;
         if (pf_status st = check_device()) return st;
-        hipStream_t s = (hipStream_t)stream;
-        char* ws = static_cast<char*>(workspace);
-        int8_t* a = reinterpret_cast<int8_t*>(ws + lay.a);
-        int8_t* b = reinterpret_cast<int8_t*>(ws + lay.b);
-        float* sa = reinterpret_cast<float*>(ws + lay.sa);
-        float* sb = reinterpret_cast<float*>(ws + lay.sb);
-        float* pscratch = reinterpret_cast<float*>(ws + lay.proj);
-        const int64_t rows[PF_NPROJ] = {H, H, H, H, F, F, H};
-        int64_t offs[PF_NPROJ + 1] = {0};
-        for (int j = 0; j < PF_NPROJ; ++j) offs[j + 1] = offs[j] + rows[j];
+        StackRun run{stack, x, P, ch, y, proj, static_cast<char*>(workspace), lay,
+                     (hipStream_t)stream};
+        Recorder rec(run.s, stats != nullptr, timed);
         const bool per_token = per_token_mode();
-
-        Recorder rec(s, stats != nullptr, timed);
         pf_status st = rec.begin();
-        const int64_t step = per_token ? 1 : ch;
-        for (int64_t c0 = 0; c0 < P && st == PF_OK; c0 += step) {
-            const int64_t M = std::min(step, P - c0);
-            for (int64_t l = 0; l < L && st == PF_OK; ++l) {
-                const pf_layer& ly = stack->layers[l];
-                float* prow = proj ? proj + ((size_t)l * P + c0) * NT : pscratch;
-                // input of this layer: x for layer 0, else the previous down output
-                const float* hin = x + c0 * H;
-                int64_t ldh = H;
-                if (l > 0) {
-                    hin = (proj ? proj + ((size_t)(l - 1) * P + c0) * NT : pscratch) + offs[6];
-                    ldh = NT;
-                }
-                double bytes = (double)M * H * 4 + (double)M * H + M * 4.0;
-                st = rec.run(Recorder::kQuant, bytes, [&] {
-                    return launched(launch_quantize(hin, ldh, (int)M, (int)H, a, sa, s));
-                });
-                if (st) break;
-                GemmSet set;
-                std::memset(&set, 0, sizeof(set));
-                set.nprob = 6;
-                char* scratch = ws + lay.split;
-                bytes = 0.0;
-                for (int j = 0; j < 6; ++j) {
-                    SkinnyPlan p = lay.plan[j];
-                    if (per_token) p = unsplit(rows[j], H);
-                    if (per_token || M <= 64)
-                        make_skinny(set.p[j], ly.W[j], ly.w_scale[j], rows[j], H, a, H, sa, M,
-                                    prow + offs[j], NT, p, scratch, ch);
-                    else
-                        make_tiled(set.p[j], ly.W[j], ly.w_scale[j], rows[j], H, a, H, sa, M,
-                                   prow + offs[j], NT);
-                    bytes += product_bytes(rows[j], H, M);
-                }
-                st = rec.run(Recorder::kProduct, bytes, [&] {
-                    if (per_token) {
-                        finish_set(set, 0);
-                        return launched(launch_gemv(set, s));
-                    }
-                    return run_products(set, M, s);
-                });
-                if (st) break;
-                bytes = (double)M * F * 4 + (double)M * F + M * 4.0;
-                st = rec.run(Recorder::kQuant, bytes, [&] {
-                    return launched(launch_quantize(prow + offs[5], NT, (int)M, (int)F, b, sb, s));
-                });
-                if (st) break;
-                GemmSet dn;
-                std::memset(&dn, 0, sizeof(dn));
-                dn.nprob = 1;
-                SkinnyPlan p = lay.plan[6];
-                if (per_token) p = unsplit(H, F);
-                if (per_token || M <= 64)
-                    make_skinny(dn.p[0], ly.W[6], ly.w_scale[6], H, F, b, F, sb, M, prow + offs[6], NT,
-                                p, scratch, ch);
-                else
-                    make_tiled(dn.p[0], ly.W[6], ly.w_scale[6], H, F, b, F, sb, M, prow + offs[6], NT);
-                if (l == L - 1) {
-                    dn.p[0].Y2 = y + c0 * H;
-                    dn.p[0].ldy2 = H;
-                }
-                st = rec.run(Recorder::kProduct, product_bytes(H, F, M), [&] {
-                    if (per_token) {
-                        finish_set(dn, 0);
-                        return launched(launch_gemv(dn, s));
-                    }
-                    return run_products(dn, M, s);
-                });
-            }
-        }
+        if (st == PF_OK) st = per_token ? run.per_token(rec) : run.sweep(rec);
         if (st == PF_OK) st = rec.end();
         if (st == PF_OK && stats) {
             std::memset(stats, 0, sizeof(*stats));

@@ -39,12 +39,11 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s)
 // Per-token quantisation: one workgroup per token row.  amax is an exact
 // maximum (order-free); the scale and every code follow the per-token
 // definition bit for bit.
-__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x, int64_t ldx, int K,
-                                                  int8_t* __restrict__ q, float* __restrict__ scale)
+__device__ __forceinline__ void quantize_row(const float* __restrict__ x, int K,
+                                             int8_t* __restrict__ q, float* __restrict__ scale)
 {
-    const int t = blockIdx.x;
-    const float4* row = reinterpret_cast<const float4*>(x + (int64_t)t * ldx);
-    int* qrow = reinterpret_cast<int*>(q + (int64_t)t * K);
+    const float4* row = reinterpret_cast<const float4*>(x);
+    int* qrow = reinterpret_cast<int*>(q);
     const int n4 = K >> 2;
     float amax = 0.0f;
     for (int i = threadIdx.x; i < n4; i += 256) {
@@ -57,7 +56,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x, i
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float s = amax / 127.0f;
-    if (threadIdx.x == 0) scale[t] = s;
+    if (threadIdx.x == 0) *scale = s;
     for (int i = threadIdx.x; i < n4; i += 256) {
         int packed = 0;
         if (s != 0.0f) {
@@ -69,11 +68,38 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x, i
     }
 }
 
+__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x, int64_t ldx, int K,
+                                                  int8_t* __restrict__ q, float* __restrict__ scale)
+{
+    const int t = blockIdx.x;
+    quantize_row(x + (int64_t)t * ldx, K, q + (int64_t)t * K, scale + t);
+}
+
 hipError_t launch_quantize(const float* x, int64_t ldx, int M, int K, int8_t* q, float* scale,
                            hipStream_t s)
 {
     if (M <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_quantize, dim3(M), dim3(256), 0, s, x, ldx, K, q, scale);
+    return hipGetLastError();
+}
+
+// The token rows of several chunks in one launch (one workgroup per row).
+__global__ __launch_bounds__(256) void k_quantize_step(QuantStep S)
+{
+    const int bid = blockIdx.x;
+    int pi = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxPairs; ++q)
+        if (q < S.npairs && bid >= S.pair[q].row0) pi = q;
+    const QuantPair& P = S.pair[pi];
+    const int t = bid - P.row0;
+    quantize_row(P.src + (int64_t)t * P.ld, S.K, P.q + (int64_t)t * S.K, P.s + t);
+}
+
+hipError_t launch_quantize_step(const QuantStep& S, hipStream_t s)
+{
+    if (S.total_rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_quantize_step, dim3(S.total_rows), dim3(256), 0, s, S);
     return hipGetLastError();
 }
 
@@ -86,6 +112,40 @@ __device__ __forceinline__ GemmProb find_prob(const GemmSet& set, int bid)
 #pragma unroll
     for (int j = 1; j < kMaxProbs; ++j)
         if (j < set.nprob && bid >= set.p[j].tile_begin) P = set.p[j];
+    return P;
+}
+
+// Problem of a stack step: workgroup bid -> (pair, projection, tile).
+__device__ __forceinline__ GemmProb step_prob(const StackStep& S, int bid, int& local)
+{
+    const int per = S.tile_off[S.nproj];
+    const int pi = bid / per;
+    const int lp = bid - pi * per;
+    int j = 0;
+#pragma unroll
+    for (int q = 1; q < 6; ++q)
+        if (q < S.nproj && lp >= S.tile_off[q]) j = q;
+    local = lp - S.tile_off[j];
+    const StepPair& pp = S.pair[pi];
+    GemmProb P;
+    P.W = pp.W[j];
+    P.ws = pp.ws[j];
+    P.X = pp.X;
+    P.xs = pp.xs;
+    P.Y = pp.Y + S.yoff[j];
+    P.Y2 = pp.Y2;
+    P.acc = nullptr;
+    P.ldx = S.ldx;
+    P.ldy = S.ldy;
+    P.ldy2 = S.ldy2;
+    P.N = S.rows[j];
+    P.K = S.K;
+    P.M = pp.M;
+    P.tiles_n = 0;
+    P.tiles_m = S.tiles_m;
+    P.splits = 1;
+    P.kb_per_split = S.K >> 6;
+    P.tile_begin = 0;
     return P;
 }
 
@@ -160,11 +220,9 @@ hipError_t launch_gemv(const GemmSet& set, hipStream_t s)
 constexpr int kSkStage = 8;
 
 template <int TB>
-__global__ __launch_bounds__(256) void k_gemm_skinny(GemmSet set)
+__device__ __forceinline__ void skinny_tile(const GemmProb& P, int local)
 {
     __shared__ v4i red[4][TB][64];
-    const GemmProb P = find_prob(set, blockIdx.x);
-    const int local = blockIdx.x - P.tile_begin;
     const int split = local % P.splits;
     const int tn = local / P.splits;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -233,6 +291,21 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmSet set)
     }
 }
 
+template <int TB>
+__global__ __launch_bounds__(256) void k_gemm_skinny(GemmSet set)
+{
+    const GemmProb P = find_prob(set, blockIdx.x);
+    skinny_tile<TB>(P, blockIdx.x - P.tile_begin);
+}
+
+template <int TB>
+__global__ __launch_bounds__(256) void k_gemm_skinny_step(StackStep S)
+{
+    int local;
+    const GemmProb P = step_prob(S, blockIdx.x, local);
+    skinny_tile<TB>(P, local);
+}
+
 // Sum of the split partials [splits][M][N] and the epilogue; one thread per
 // output.  Here tile_begin counts blocks of 256 outputs.
 __global__ __launch_bounds__(256) void k_split_reduce(GemmSet set)
@@ -274,6 +347,21 @@ hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t 
     return hipGetLastError();
 }
 
+hipError_t launch_gemm_skinny_step(const StackStep& S, int token_blocks, hipStream_t s)
+{
+    const int blocks = S.npairs * S.tile_off[S.nproj];
+    if (blocks <= 0) return hipSuccess;
+    const dim3 g(blocks), b(256);
+    switch (token_blocks) {
+        case 1: hipLaunchKernelGGL(k_gemm_skinny_step<1>, g, b, 0, s, S); break;
+        case 2: hipLaunchKernelGGL(k_gemm_skinny_step<2>, g, b, 0, s, S); break;
+        case 3: hipLaunchKernelGGL(k_gemm_skinny_step<3>, g, b, 0, s, S); break;
+        case 4: hipLaunchKernelGGL(k_gemm_skinny_step<4>, g, b, 0, s, S); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Tiled product (M > 64): 128 weight rows x 128 tokens per workgroup, k-blocks of
 // 64 bytes double-buffered through LDS, v_mfma_i32_32x32x32_i8 with 2 x 2 tiles of
@@ -281,12 +369,10 @@ hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t 
 constexpr int kTlStride = 80;                      // LDS bytes per row (64 + 16 pad)
 constexpr int kTlRows = 128;
 
-__global__ __launch_bounds__(256) void k_gemm_tiled(GemmSet set)
+__device__ __forceinline__ void tiled_tile(const GemmProb& P, int local)
 {
     __shared__ __attribute__((aligned(16))) int8_t sw[2][kTlRows * kTlStride];
     __shared__ __attribute__((aligned(16))) int8_t sx[2][kTlRows * kTlStride];
-    const GemmProb P = find_prob(set, blockIdx.x);
-    const int local = blockIdx.x - P.tile_begin;
     const int tm = local % P.tiles_m;
     const int tn = local / P.tiles_m;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -376,10 +462,31 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmSet set)
     }
 }
 
+__global__ __launch_bounds__(256) void k_gemm_tiled(GemmSet set)
+{
+    const GemmProb P = find_prob(set, blockIdx.x);
+    tiled_tile(P, blockIdx.x - P.tile_begin);
+}
+
+__global__ __launch_bounds__(256) void k_gemm_tiled_step(StackStep S)
+{
+    int local;
+    const GemmProb P = step_prob(S, blockIdx.x, local);
+    tiled_tile(P, local);
+}
+
 hipError_t launch_gemm_tiled(const GemmSet& set, hipStream_t s)
 {
     if (set.total_tiles <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_gemm_tiled, dim3(set.total_tiles), dim3(256), 0, s, set);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_tiled_step(const StackStep& S, hipStream_t s)
+{
+    const int blocks = S.npairs * S.tile_off[S.nproj];
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_gemm_tiled_step, dim3(blocks), dim3(256), 0, s, S);
     return hipGetLastError();
 }
 

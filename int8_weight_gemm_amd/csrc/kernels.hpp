@@ -34,6 +34,45 @@ struct GemmSet {
     int total_tiles;
 };
 
+// One step of the chunk x layer sweep: up to kMaxPairs (chunk, layer) pairs,
+// each multiplying its chunk's quantised tokens with the same projection slots
+// (q..up, or down) of its own layer.  Workgroup b -> pair b / tiles_per_pair.
+constexpr int kMaxPairs = 16;
+struct StepPair {
+    const int8_t* W[6];
+    const float* ws[6];
+    const int8_t* X;      // quantised tokens [M][ldx]
+    const float* xs;      // token scales [M]
+    float* Y;             // output rows [M][ldy]; projection j at column yoff[j]
+    float* Y2;            // optional second copy [M][ldy2] (single-projection steps) or null
+    int M;
+};
+struct StackStep {
+    StepPair pair[kMaxPairs];
+    int npairs;
+    int nproj;            // projections per pair (6 or 1)
+    int K;
+    int rows[6];          // rows of projection j
+    int yoff[6];          // column of projection j inside an output row
+    int tile_off[7];      // tile prefix over projections, per pair
+    int tiles_m;          // token tiles (tiled kernel)
+    int64_t ldx, ldy, ldy2;
+};
+
+struct QuantPair {
+    const float* src;     // [M][ld] f32 rows
+    int8_t* q;            // [M][K]
+    float* s;             // [M]
+    int64_t ld;           // floats between source rows
+    int row0;             // first workgroup of this pair
+};
+struct QuantStep {
+    QuantPair pair[kMaxPairs];
+    int npairs;
+    int K;
+    int total_rows;
+};
+
 // Expert-grouped product: expert e multiplies its W_e with the rows of its token
 // group (rows off[e] .. off[e+1] of the pair list).
 struct ExpertArgs {
@@ -55,9 +94,10 @@ struct ExpertArgs {
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_quantize(const float* x, int64_t ldx, int M, int K, int8_t* q, float* scale,
                            hipStream_t s);
-hipError_t launch_quantize_mul(const float* a, const float* b, int64_t ld, int M, int K,
-                               int8_t* q, float* scale, hipStream_t s);
+hipError_t launch_quantize_step(const QuantStep& S, hipStream_t s);
 hipError_t launch_gemv(const GemmSet& set, hipStream_t s);
+hipError_t launch_gemm_skinny_step(const StackStep& S, int token_blocks, hipStream_t s);
+hipError_t launch_gemm_tiled_step(const StackStep& S, hipStream_t s);
 hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_tiled(const GemmSet& set, hipStream_t s);
 
