@@ -63,14 +63,14 @@ pf_status launched(hipError_t e)
 }
 
 // ---------------------------------------------------------------------------
-// Split plan of the skinny product: 16-row tiles; when a launch has fewer tiles
+// Split plan of the skinny product: 64-row tiles; when a launch has fewer tiles
 // than compute units, the K range is split across workgroups (each split at
 // least 8 k-blocks of 64 bytes) until every compute unit has one.
 struct SkinnyPlan {
     int tiles_n, splits, kb_per_split;
 };
 
-constexpr int kSkinnyRows = 16;
+constexpr int kSkinnyRows = 64;
 constexpr int64_t kComputeUnits = 256;
 
 SkinnyPlan plan_skinny(int64_t N, int64_t K, int64_t total_tiles)
@@ -407,12 +407,13 @@ struct StackRun {
             for (int j = 0; j < 6; ++j) {
                 A.rows[j] = (int)rowsA[j];
                 A.yoff[j] = (int)offs(j);
-                const int64_t t = skinny ? (rowsA[j] + 15) / 16 : ((rowsA[j] + 127) / 128) * tm;
+                const int64_t t = skinny ? (rowsA[j] + kSkinnyRows - 1) / kSkinnyRows
+                                         : ((rowsA[j] + 127) / 128) * tm;
                 A.tile_off[j + 1] = A.tile_off[j] + (int)t;
             }
             D.rows[0] = (int)H();
             D.yoff[0] = (int)offs(6);
-            D.tile_off[1] = (int)(skinny ? (H() + 15) / 16 : ((H() + 127) / 128) * tm);
+            D.tile_off[1] = (int)(skinny ? (H() + kSkinnyRows - 1) / kSkinnyRows : ((H() + 127) / 128) * tm);
             double qa_bytes = 0, qd_bytes = 0, a_bytes = 0, d_bytes = 0;
             int rows_total = 0;
             for (size_t i = 0; i < cs.size(); ++i) {

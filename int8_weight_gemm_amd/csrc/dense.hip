@@ -208,102 +208,131 @@ hipError_t launch_gemv(const GemmSet& set, hipStream_t s)
 // ---------------------------------------------------------------------------
 // Skinny product (M <= 64): v_mfma_i32_16x16x64_i8 with the weights as the A
 // operand (lane l holds 16 bytes of weight row l%16) and the tokens as B (lane l
-// holds the same 16 k positions of token l%16).  A workgroup owns 16 weight rows
-// and all M tokens; its 4 waves take a contiguous quarter of the K range each and
-// load both operands from global memory straight into registers, kSkStage
-// k-blocks (of 64 bytes) per stage; the four lanes l, l+16, l+32, l+48 read 64
-// contiguous bytes of a row.  The four partial int32 tiles are summed through
-// LDS (integer sums: any order gives the same bits).  When one launch has too
-// few rows to fill the chip, the K range is also split across workgroups: each
-// writes its int32 partial tile to the workspace and k_split_reduce sums the
-// partials and applies the epilogue.
-constexpr int kSkStage = 8;
+// holds the same 16 k positions of token l%16).  A workgroup owns 64 weight rows
+// (16 per wave) and all M tokens over its K range.  The tokens are staged in LDS
+// one piece of KP k-blocks (of 64 bytes) at a time and shared by the four waves;
+// each lane loads its weight fragments straight from HBM into registers, one
+// piece ahead of the MFMAs (the four lanes l, l+16, l+32, l+48 read 64
+// contiguous bytes of a row).  LDS holds two token pieces: while the waves
+// multiply piece p, piece p+1 travels from L2 into registers and is written to
+// the other buffer.  When a launch has too few 64-row tiles to fill the chip,
+// the K range is also split across workgroups: each writes its int32 partial
+// tile to the workspace and k_split_reduce sums the partials (integer sums,
+// so the bits do not depend on the split) and applies the epilogue.
+constexpr int kSkRows = 64;
 
-template <int TB>
+template <int TB, int KP>
 __device__ __forceinline__ void skinny_tile(const GemmProb& P, int local)
 {
-    __shared__ v4i red[4][TB][64];
+    constexpr int kStride = KP * 64 + 16;               // LDS bytes per token row
+    constexpr int kChunks = 16 * TB * KP * 4;            // 16-byte chunks per token piece
+    constexpr int kPerThread = (kChunks + 255) / 256;
+    __shared__ __attribute__((aligned(16))) int8_t xl[2][16 * TB * kStride];
     const int split = local % P.splits;
     const int tn = local / P.splits;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n0 = tn * 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nw0 = tn * kSkRows + wave * 16;
     const int nkb = P.K >> 6;
-    const int s0 = split * P.kb_per_split;
-    const int len = min(P.kb_per_split, nkb - s0);
-    const int kb0 = s0 + (len * wave) / 4, kb1 = s0 + (len * (wave + 1)) / 4;
+    const int kb0 = split * P.kb_per_split;
+    const int kb1 = min(kb0 + P.kb_per_split, nkb);
+    const int npieces = (kb1 - kb0 + KP - 1) / KP;
     const int koff = (lane >> 4) << 4;
-    const int8_t* wp = P.W + (int64_t)min(n0 + (lane & 15), P.N - 1) * P.K + koff;
-    const int8_t* xp[TB];
-    bool xok[TB];
+    const int8_t* wp = P.W + (int64_t)min(nw0 + (lane & 15), P.N - 1) * P.K + koff;
+    const int boff = (lane & 15) * kStride + koff;
+
+    // token piece staging: thread chunk c -> token c / (4 KP), 16-byte column c % (4 KP)
+    auto xload = [&](int kp, int npc, v4i (&r)[kPerThread]) {
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-        const int t = tb * 16 + (lane & 15);
-        xok[tb] = t < P.M;
-        xp[tb] = P.X + (int64_t)(xok[tb] ? t : 0) * P.ldx + koff;
-    }
+        for (int u = 0; u < kPerThread; ++u) {
+            const int c = tid + 256 * u;
+            const int t = c / (4 * KP), col = c % (4 * KP);
+            r[u] = v4i{0, 0, 0, 0};
+            if (c < kChunks && t < P.M && col < 4 * npc)
+                r[u] = ld16(P.X + (int64_t)t * P.ldx + (int64_t)kp * 64 + col * 16);
+        }
+    };
+    auto xstore = [&](int buf, const v4i (&r)[kPerThread]) {
+#pragma unroll
+        for (int u = 0; u < kPerThread; ++u) {
+            const int c = tid + 256 * u;
+            if (c < kChunks) st16(&xl[buf][(c / (4 * KP)) * kStride + (c % (4 * KP)) * 16], r[u]);
+        }
+    };
+    auto wload = [&](int kp, int npc, v4i (&a)[KP]) {
+#pragma unroll
+        for (int i = 0; i < KP; ++i)
+            if (i < npc) a[i] = ld16(wp + (int64_t)(kp + i) * 64);
+    };
+
     v4i acc[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) acc[tb] = v4i{0, 0, 0, 0};
+    v4i a0[KP], a1[KP], xr[kPerThread];
 
-    for (int kb = kb0; kb < kb1; kb += kSkStage) {
-        const int n = min(kSkStage, kb1 - kb);
-        v4i a[kSkStage];
-        v4i b[kSkStage][TB];
+    int npc = min(KP, kb1 - kb0);
+    wload(kb0, npc, a0);
+    xload(kb0, npc, xr);
+    xstore(0, xr);
+    for (int p = 0; p < npieces; ++p) {
+        const int kp = kb0 + p * KP;
+        const int npc_next = p + 1 < npieces ? min(KP, kb1 - kp - KP) : 0;
+        if (npc_next > 0) {
+            wload(kp + KP, npc_next, a1);
+            xload(kp + KP, npc_next, xr);
+        }
+        __syncthreads();
+        const int8_t* xb = xl[p & 1] + boff;
 #pragma unroll
-        for (int i = 0; i < kSkStage; ++i) {
-            if (i < n) {
-                a[i] = ld16(wp + (int64_t)(kb + i) * 64);
+        for (int i = 0; i < KP; ++i) {
+            if (i < npc) {
 #pragma unroll
-                for (int tb = 0; tb < TB; ++tb)
-                    b[i][tb] = xok[tb] ? ld16(xp[tb] + (int64_t)(kb + i) * 64) : v4i{0, 0, 0, 0};
+                for (int tb = 0; tb < TB; ++tb) {
+                    const v4i b = *reinterpret_cast<const v4i*>(xb + tb * 16 * kStride + i * 64);
+                    acc[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[i], b, acc[tb], 0, 0, 0);
+                }
             }
         }
+        if (npc_next > 0) {
+            xstore((p + 1) & 1, xr);
 #pragma unroll
-        for (int i = 0; i < kSkStage; ++i) {
-            if (i < n) {
-#pragma unroll
-                for (int tb = 0; tb < TB; ++tb)
-                    acc[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[i][tb], acc[tb], 0, 0, 0);
-            }
+            for (int i = 0; i < KP; ++i) a0[i] = a1[i];
         }
+        npc = npc_next;
     }
 
+    // Lane l holds rows nr .. nr+3 of token column l%16 in each token block.
+    const int nr = nw0 + ((lane >> 4) << 2);
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) red[wave][tb][lane] = acc[tb];
-    __syncthreads();
-    if (wave >= TB) return;
-    // wave w finishes token block w.  Lane l holds rows nr .. nr+3 of token t.
-    const int tb = wave;
-    const v4i sum = red[0][tb][lane] + red[1][tb][lane] + red[2][tb][lane] + red[3][tb][lane];
-    const int t = tb * 16 + (lane & 15);
-    const int nr = n0 + ((lane >> 4) << 2);
-    if (t >= P.M) return;
-    if (P.splits == 1) {
-        const float xs = P.xs[t];
+    for (int tb = 0; tb < TB; ++tb) {
+        const int t = tb * 16 + (lane & 15);
+        if (t >= P.M) continue;
+        if (P.splits == 1) {
+            const float xs = P.xs[t];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (nr + r < P.N) store_out(P, t, nr + r, epilogue(sum[r], P.ws[nr + r], xs));
-    } else {
-        int* part = P.acc + ((int64_t)split * P.M + t) * P.N;
+            for (int r = 0; r < 4; ++r)
+                if (nr + r < P.N) store_out(P, t, nr + r, epilogue(acc[tb][r], P.ws[nr + r], xs));
+        } else {
+            int* part = P.acc + ((int64_t)split * P.M + t) * P.N;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (nr + r < P.N) part[nr + r] = sum[r];
+            for (int r = 0; r < 4; ++r)
+                if (nr + r < P.N) part[nr + r] = acc[tb][r];
+        }
     }
 }
 
-template <int TB>
+template <int TB, int KP>
 __global__ __launch_bounds__(256) void k_gemm_skinny(GemmSet set)
 {
     const GemmProb P = find_prob(set, blockIdx.x);
-    skinny_tile<TB>(P, blockIdx.x - P.tile_begin);
+    skinny_tile<TB, KP>(P, blockIdx.x - P.tile_begin);
 }
 
-template <int TB>
+template <int TB, int KP>
 __global__ __launch_bounds__(256) void k_gemm_skinny_step(StackStep S)
 {
     int local;
     const GemmProb P = step_prob(S, blockIdx.x, local);
-    skinny_tile<TB>(P, local);
+    skinny_tile<TB, KP>(P, local);
 }
 
 // Sum of the split partials [splits][M][N] and the epilogue; one thread per
@@ -319,17 +348,25 @@ __global__ __launch_bounds__(256) void k_split_reduce(GemmSet set)
     store_out(P, t, n, epilogue(v, P.ws[n], P.xs[t]));
 }
 
+// Token pieces of 8 k-blocks (512 bytes): with the weight double buffer that is
+// 32 KB of weights in flight per workgroup at four workgroups per compute unit.
+constexpr int kSkPiece = 8;
+
+#define PF_SKINNY_CASES(KERNEL, ARG)                                                   \
+    switch (token_blocks) {                                                            \
+        case 1: hipLaunchKernelGGL((KERNEL<1, kSkPiece>), g, b, 0, s, ARG); break;      \
+        case 2: hipLaunchKernelGGL((KERNEL<2, kSkPiece>), g, b, 0, s, ARG); break;      \
+        case 3: hipLaunchKernelGGL((KERNEL<3, kSkPiece>), g, b, 0, s, ARG); break;      \
+        case 4: hipLaunchKernelGGL((KERNEL<4, kSkPiece>), g, b, 0, s, ARG); break;      \
+        default: return hipErrorInvalidValue;                                          \
+    }
+
 hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t s)
 {
     if (set.total_tiles <= 0) return hipSuccess;
+    if (token_blocks < 1 || token_blocks > 4) return hipErrorInvalidValue;
     const dim3 g(set.total_tiles), b(256);
-    switch (token_blocks) {
-        case 1: hipLaunchKernelGGL(k_gemm_skinny<1>, g, b, 0, s, set); break;
-        case 2: hipLaunchKernelGGL(k_gemm_skinny<2>, g, b, 0, s, set); break;
-        case 3: hipLaunchKernelGGL(k_gemm_skinny<3>, g, b, 0, s, set); break;
-        case 4: hipLaunchKernelGGL(k_gemm_skinny<4>, g, b, 0, s, set); break;
-        default: return hipErrorInvalidValue;
-    }
+    PF_SKINNY_CASES(k_gemm_skinny, set)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // reduce launch over the split problems only
@@ -351,14 +388,9 @@ hipError_t launch_gemm_skinny_step(const StackStep& S, int token_blocks, hipStre
 {
     const int blocks = S.npairs * S.tile_off[S.nproj];
     if (blocks <= 0) return hipSuccess;
+    if (token_blocks < 1 || token_blocks > 4) return hipErrorInvalidValue;
     const dim3 g(blocks), b(256);
-    switch (token_blocks) {
-        case 1: hipLaunchKernelGGL(k_gemm_skinny_step<1>, g, b, 0, s, S); break;
-        case 2: hipLaunchKernelGGL(k_gemm_skinny_step<2>, g, b, 0, s, S); break;
-        case 3: hipLaunchKernelGGL(k_gemm_skinny_step<3>, g, b, 0, s, S); break;
-        case 4: hipLaunchKernelGGL(k_gemm_skinny_step<4>, g, b, 0, s, S); break;
-        default: return hipErrorInvalidValue;
-    }
+    PF_SKINNY_CASES(k_gemm_skinny_step, S)
     return hipGetLastError();
 }
 
