@@ -471,12 +471,12 @@ struct StackRun {
             pf_status r = rec.run(Recorder::kQuant, qa_bytes,
                                   [&] { return launched(launch_quantize_step(qa, s)); });
             if (!r) r = rec.run(Recorder::kProduct, a_bytes, [&] {
-                return launched(skinny ? launch_gemm_skinny_step(A, tb, s) : launch_gemm_tiled_step(A, s));
+                return launched(skinny ? launch_gemm_stream(A, tb, s) : launch_gemm_tiled_step(A, s));
             });
             if (!r) r = rec.run(Recorder::kQuant, qd_bytes,
                                 [&] { return launched(launch_quantize_step(qd, s)); });
             if (!r) r = rec.run(Recorder::kProduct, d_bytes, [&] {
-                return launched(skinny ? launch_gemm_skinny_step(D, tb, s) : launch_gemm_tiled_step(D, s));
+                return launched(skinny ? launch_gemm_stream(D, tb, s) : launch_gemm_tiled_step(D, s));
             });
             if (r) return r;
         }

@@ -98,6 +98,7 @@ hipError_t launch_quantize_step(const QuantStep& S, hipStream_t s);
 hipError_t launch_gemv(const GemmSet& set, hipStream_t s);
 hipError_t launch_gemm_skinny_step(const StackStep& S, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_tiled_step(const StackStep& S, hipStream_t s);
+hipError_t launch_gemm_stream(const StackStep& S, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_tiled(const GemmSet& set, hipStream_t s);
 
