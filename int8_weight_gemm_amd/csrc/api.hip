@@ -159,19 +159,28 @@ pf_status run_products(GemmSet& set, int64_t M, hipStream_t s)
 // flight owns one slot for all of its layers.
 struct StackLayout {
     int slots;
-    size_t a, b, sa, sb, proj, slot_bytes, total;
+    int dsplits;          // K splits of the down product (skinny path)
+    size_t a, b, sa, sb, proj, part, slot_bytes, total;
 };
+
+// Down-product K splits on the skinny path: at most 16 k-blocks (1 KB of K) each.
+int down_splits(int64_t F, int64_t chunk)
+{
+    return chunk <= 64 ? (int)((F / 64 + 15) / 16) : 1;
+}
 
 StackLayout stack_layout(int64_t L, int64_t H, int64_t F, int64_t chunk)
 {
     StackLayout S{};
     S.slots = (int)std::min<int64_t>(L, kMaxPairs);
+    S.dsplits = down_splits(F, chunk);
     size_t o = 0;
     S.a = o; o += round_up((size_t)chunk * H, kAlign);
     S.b = o; o += round_up((size_t)chunk * F, kAlign);
     S.sa = o; o += round_up((size_t)chunk * 4, kAlign);
     S.sb = o; o += round_up((size_t)chunk * 4, kAlign);
     S.proj = o; o += round_up((size_t)chunk * (5 * H + 2 * F) * 4, kAlign);
+    S.part = o; o += chunk <= 64 ? round_up((size_t)S.dsplits * chunk * H * 4, kAlign) : 0;
     S.slot_bytes = o;
     S.total = o * S.slots;
     return S;
@@ -378,32 +387,43 @@ struct StackRun {
         const int64_t L = st->n_layers, C = (P + ch - 1) / ch;
         const int64_t nsteps = start(C - 1) + L;
         const bool skinny = ch <= 64;
+        // token-resident kernel for the six K = H products when a split of H fits
+        const bool xres_a = skinny && H() / 64 <= 16;
+        const int sd = lay.dsplits;
         const int64_t rowsA[6] = {H(), H(), H(), H(), F(), F()};
+        const int tm = (int)((ch + 127) / 128);
+        const int tb = (int)((ch + 15) / 16);
+        int64_t fin = -1;                     // chunk whose last down product ran last step
         int64_t c_lo = 0;
-        for (int64_t step = 0; step < nsteps; ++step) {
+        for (int64_t step = 0; step <= nsteps; ++step) {
             while (c_lo < C && start(c_lo) + L <= step) ++c_lo;
             std::vector<int64_t> cs;
-            for (int64_t c = c_lo; c < C && start(c) <= step; ++c) cs.push_back(c);
-            if (cs.empty()) continue;
+            if (step < nsteps)
+                for (int64_t c = c_lo; c < C && start(c) <= step; ++c) cs.push_back(c);
             QuantStep qa, qd;
             StackStep A, D;
             std::memset(&qa, 0, sizeof(qa));
             std::memset(&qd, 0, sizeof(qd));
             std::memset(&A, 0, sizeof(A));
             std::memset(&D, 0, sizeof(D));
-            qa.npairs = qd.npairs = A.npairs = D.npairs = (int)cs.size();
             qa.K = (int)H();
             qd.K = (int)F();
             A.nproj = 6;
             A.K = (int)H();
+            A.splits = 1;
+            A.kb_per_split = (int)(H() / 64);
             D.nproj = 1;
             D.K = (int)F();
-            const int tm = (int)((ch + 127) / 128);
+            D.splits = skinny ? sd : 1;
+            D.partials = skinny ? 1 : 0;
+            D.kb_per_split = (int)((F() / 64 + D.splits - 1) / D.splits);
             A.tiles_m = D.tiles_m = tm;
             A.ldx = H();
             D.ldx = F();
             A.ldy = D.ldy = NT();
             D.ldy2 = H();
+            D.ldp = H();
+            D.part_stride = ch * H();
             for (int j = 0; j < 6; ++j) {
                 A.rows[j] = (int)rowsA[j];
                 A.yoff[j] = (int)offs(j);
@@ -415,7 +435,19 @@ struct StackRun {
             D.yoff[0] = (int)offs(6);
             D.tile_off[1] = (int)(skinny ? (H() + kSkinnyRows - 1) / kSkinnyRows : ((H() + 127) / 128) * tm);
             double qa_bytes = 0, qd_bytes = 0, a_bytes = 0, d_bytes = 0;
-            int rows_total = 0;
+            int rows_a = 0, rows_d = 0;
+            auto rebuild = [&](QuantPair& q, int64_t c, int64_t l_prev, bool last) {
+                // rows of (c, l_prev)'s down product, from its split partials
+                char* sl = slot(c);
+                q.part = reinterpret_cast<const int*>(sl + lay.part);
+                q.part_stride = ch * H();
+                q.splits = sd;
+                q.ws = st->layers[l_prev].w_scale[6];
+                q.as = reinterpret_cast<const float*>(sl + lay.sb);
+                q.h = rows(c, l_prev) + offs(6);
+                q.ldh = NT();
+                q.y = last ? y + c * ch * H() : nullptr;
+            };
             for (size_t i = 0; i < cs.size(); ++i) {
                 const int64_t c = cs[i], l = step - start(c);
                 const int64_t c0 = c * ch, M = std::min(ch, P - c0);
@@ -426,25 +458,29 @@ struct StackRun {
                 float* sa = reinterpret_cast<float*>(sl + lay.sa);
                 float* sb = reinterpret_cast<float*>(sl + lay.sb);
                 float* out = rows(c, l);
-                QuantPair& q0 = qa.pair[i];
+                QuantPair& q0 = qa.pair[qa.npairs++];
                 if (l == 0) {
                     q0.src = x + c0 * H();
                     q0.ld = H();
+                } else if (skinny) {
+                    rebuild(q0, c, l - 1, false);
+                    qa_bytes += (double)M * H() * 4 * sd + (double)M * H() * 4;
                 } else {
                     q0.src = rows(c, l - 1) + offs(6);
                     q0.ld = NT();
                 }
                 q0.q = a;
                 q0.s = sa;
-                q0.row0 = rows_total;
-                QuantPair& q1 = qd.pair[i];
+                q0.row0 = rows_a;
+                rows_a += (int)M;
+                QuantPair& q1 = qd.pair[qd.npairs++];
                 q1.src = out + offs(5);
                 q1.ld = NT();
                 q1.q = b;
                 q1.s = sb;
-                q1.row0 = rows_total;
-                rows_total += (int)M;
-                StepPair& pa = A.pair[i];
+                q1.row0 = rows_d;
+                rows_d += (int)M;
+                StepPair& pa = A.pair[A.npairs++];
                 for (int j = 0; j < 6; ++j) {
                     pa.W[j] = ly.W[j];
                     pa.ws[j] = ly.w_scale[j];
@@ -454,31 +490,49 @@ struct StackRun {
                 pa.xs = sa;
                 pa.Y = out;
                 pa.M = (int)M;
-                StepPair& pd = D.pair[i];
+                StepPair& pd = D.pair[D.npairs++];
                 pd.W[0] = ly.W[6];
                 pd.ws[0] = ly.w_scale[6];
                 pd.X = b;
                 pd.xs = sb;
                 pd.Y = out;
-                pd.Y2 = l == L - 1 ? y + c0 * H() : nullptr;
+                pd.Y2 = (!skinny && l == L - 1) ? y + c0 * H() : nullptr;
+                pd.part = reinterpret_cast<int*>(sl + lay.part);
                 pd.M = (int)M;
                 d_bytes += product_bytes(H(), F(), M);
                 qa_bytes += (double)M * H() * 5 + M * 4.0;
                 qd_bytes += (double)M * F() * 5 + M * 4.0;
             }
-            qa.total_rows = qd.total_rows = rows_total;
-            const int tb = (int)((ch + 15) / 16);
-            pf_status r = rec.run(Recorder::kQuant, qa_bytes,
-                                  [&] { return launched(launch_quantize_step(qa, s)); });
-            if (!r) r = rec.run(Recorder::kProduct, a_bytes, [&] {
-                return launched(skinny ? launch_gemm_stream(A, tb, s) : launch_gemm_tiled_step(A, s));
+            if (fin >= 0) {
+                // the chunk that left the last layer: rebuild its output, no quantisation
+                const int64_t M = std::min(ch, P - fin * ch);
+                QuantPair& qf = qa.pair[qa.npairs++];
+                rebuild(qf, fin, L - 1, true);
+                qf.row0 = rows_a;
+                rows_a += (int)M;
+                qa_bytes += (double)M * H() * 4 * (sd + 2);
+                fin = -1;
+            }
+            qa.total_rows = rows_a;
+            qd.total_rows = rows_d;
+            pf_status r = PF_OK;
+            if (qa.npairs > 0)
+                r = rec.run(Recorder::kQuant, qa_bytes, [&] { return launched(launch_quantize_step(qa, s)); });
+            if (r) return r;
+            if (cs.empty()) continue;
+            r = rec.run(Recorder::kProduct, a_bytes, [&] {
+                if (!skinny) return launched(launch_gemm_tiled_step(A, s));
+                return launched(xres_a ? launch_gemm_xres(A, tb, s) : launch_gemm_stream(A, tb, s));
             });
             if (!r) r = rec.run(Recorder::kQuant, qd_bytes,
                                 [&] { return launched(launch_quantize_step(qd, s)); });
             if (!r) r = rec.run(Recorder::kProduct, d_bytes, [&] {
-                return launched(skinny ? launch_gemm_stream(D, tb, s) : launch_gemm_tiled_step(D, s));
+                return launched(skinny ? launch_gemm_xres(D, tb, s) : launch_gemm_tiled_step(D, s));
             });
             if (r) return r;
+            if (skinny)
+                for (int64_t c : cs)
+                    if (step - start(c) == L - 1) fin = c;
         }
         return PF_OK;
     }

@@ -85,15 +85,53 @@ hipError_t launch_quantize(const float* x, int64_t ldx, int M, int K, int8_t* q,
 }
 
 // The token rows of several chunks in one launch (one workgroup per row).
+__device__ __forceinline__ void rebuild_row(const QuantPair& P, int t, int K)
+{
+    // h[n] = epilogue(sum over splits of part[s][t][n], ws[n], as[t]); integer
+    // sums, so the split order does not matter.
+    const float as = P.as[t];
+    const int4* prow = reinterpret_cast<const int4*>(P.part + (int64_t)t * K);
+    float4* hrow = reinterpret_cast<float4*>(P.h + (int64_t)t * P.ldh);
+    float* yrow = P.y ? P.y + (int64_t)t * K : nullptr;    // 4-byte aligned only
+    const int64_t sstride = P.part_stride / 4;
+    for (int i = threadIdx.x; i < (K >> 2); i += 256) {
+        int4 v = prow[i];
+        for (int sp = 1; sp < P.splits; ++sp) {
+            const int4 w = prow[i + sp * sstride];
+            v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+        }
+        const float* ws = P.ws + 4 * i;      // scales need only 4-byte alignment
+        float4 h;
+        h.x = epilogue(v.x, ws[0], as);
+        h.y = epilogue(v.y, ws[1], as);
+        h.z = epilogue(v.z, ws[2], as);
+        h.w = epilogue(v.w, ws[3], as);
+        hrow[i] = h;
+        if (yrow) {
+            yrow[4 * i] = h.x;
+            yrow[4 * i + 1] = h.y;
+            yrow[4 * i + 2] = h.z;
+            yrow[4 * i + 3] = h.w;
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void k_quantize_step(QuantStep S)
 {
     const int bid = blockIdx.x;
     int pi = 0;
 #pragma unroll
-    for (int q = 1; q < kMaxPairs; ++q)
+    for (int q = 1; q < kMaxQuant; ++q)
         if (q < S.npairs && bid >= S.pair[q].row0) pi = q;
     const QuantPair& P = S.pair[pi];
     const int t = bid - P.row0;
+    if (P.part) {
+        rebuild_row(P, t, S.K);
+        if (!P.q) return;
+        // each thread re-reads only the elements it wrote itself
+        quantize_row(P.h + (int64_t)t * P.ldh, S.K, P.q + (int64_t)t * S.K, P.s + t);
+        return;
+    }
     quantize_row(P.src + (int64_t)t * P.ld, S.K, P.q + (int64_t)t * S.K, P.s + t);
 }
 

@@ -45,6 +45,7 @@ struct StepPair {
     const float* xs;      // token scales [M]
     float* Y;             // output rows [M][ldy]; projection j at column yoff[j]
     float* Y2;            // optional second copy [M][ldy2] (single-projection steps) or null
+    int* part;            // split-K int32 partials [splits][part_stride] (rows of ldp) or null
     int M;
 };
 struct StackStep {
@@ -56,18 +57,37 @@ struct StackStep {
     int yoff[6];          // column of projection j inside an output row
     int tile_off[7];      // tile prefix over projections, per pair
     int tiles_m;          // token tiles (tiled kernel)
+    int splits;           // K splits
+    int partials;         // 1: store int32 partials to StepPair::part, no epilogue
+    int kb_per_split;     // 64-byte k-blocks per split
     int64_t ldx, ldy, ldy2;
+    int64_t ldp;          // int32 elements between token rows of the partials
+    int64_t part_stride;  // int32 elements between splits of the partials
 };
 
+// Per-token quantisation of several chunks' rows in one launch.  Mode 0: the
+// rows are f32 [M][ld] at src.  Mode 1 (part != null): the rows are rebuilt
+// first from split-K int32 partials of a product (sum over the splits, then the
+// epilogue with the product's weight-row and token scales), written to h (and
+// y when not null); q == null skips the quantisation itself.
+constexpr int kMaxQuant = kMaxPairs + 1;
 struct QuantPair {
-    const float* src;     // [M][ld] f32 rows
-    int8_t* q;            // [M][K]
-    float* s;             // [M]
+    const float* src;     // mode 0 rows
+    int8_t* q;            // [M][K] codes, or null
+    float* s;             // [M] scales
     int64_t ld;           // floats between source rows
     int row0;             // first workgroup of this pair
+    const int* part;      // mode 1: [splits][part_stride], rows of K int32
+    int64_t part_stride;
+    int splits;
+    const float* ws;      // mode 1: weight-row scales [K]
+    const float* as;      // mode 1: token scales [M]
+    float* h;             // mode 1: rebuilt rows [M][ldh]
+    int64_t ldh;
+    float* y;             // mode 1: optional copy [M][K]
 };
 struct QuantStep {
-    QuantPair pair[kMaxPairs];
+    QuantPair pair[kMaxQuant];
     int npairs;
     int K;
     int total_rows;
@@ -99,6 +119,7 @@ hipError_t launch_gemv(const GemmSet& set, hipStream_t s);
 hipError_t launch_gemm_skinny_step(const StackStep& S, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_tiled_step(const StackStep& S, hipStream_t s);
 hipError_t launch_gemm_stream(const StackStep& S, int token_blocks, hipStream_t s);
+hipError_t launch_gemm_xres(const StackStep& S, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_tiled(const GemmSet& set, hipStream_t s);
 

@@ -196,4 +196,219 @@ hipError_t launch_gemm_stream(const StackStep& S, int token_blocks, hipStream_t 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Token-resident weight stream.  A work item is (pair, K split, projection,
+// 64-row tile); items that share a pair and split share the token slice
+// [16 TB tokens][one split of K], which sits in LDS (as MFMA B fragments) for as
+// long as a workgroup works on that slice.  Each workgroup takes a contiguous
+// run of items, so it loads a slice once per run, not once per tile.  The
+// weights need no sharing: each wave streams its own 16 rows through a private
+// ring of NS LDS slots by DMA and waits only on its own vector-memory counter,
+// so the waves never meet at a barrier except when the token slice changes.
+// Every slot also carries the 16 rows' scales (one 4-byte DMA).  An item ends
+// with the epilogue, or (S.partials) stores its int32 partial tile, which the
+// following quantisation launch sums over the splits (rebuild mode).
+struct XresItem {
+    int pair, split, proj, local;
+};
+
+__device__ __forceinline__ XresItem xres_item(const StackStep& S, int item)
+{
+    const int per_split = S.tile_off[S.nproj];
+    const int per_pair = per_split * S.splits;
+    XresItem it;
+    it.pair = item / per_pair;
+    int r = item - it.pair * per_pair;
+    it.split = r / per_split;
+    r -= it.split * per_split;
+    int j = 0;
+#pragma unroll
+    for (int q = 1; q < 6; ++q)
+        if (q < S.nproj && r >= S.tile_off[q]) j = q;
+    it.proj = j;
+    it.local = r - S.tile_off[j];
+    return it;
+}
+
+template <int TB, int KP, int NS>
+__global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int nitems, int per_wg)
+{
+    constexpr int kKsMax = 16;                          // k-blocks per split, at most
+    constexpr int kXBytes = TB * kKsMax * 1024;         // resident token slice
+    constexpr int kXPerWave = TB * kKsMax / 4;          // token DMAs per wave per slice
+    constexpr int kSlot = KP * 1024 + 256;              // KP k-blocks of 16 rows + 64 scales
+    constexpr int kLw = KP + 1;                         // DMAs per wave per stage
+    static_assert(kLw * (NS - 2) <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) int8_t xl[kXBytes + 256];
+    __shared__ __attribute__((aligned(16))) int8_t ring[4][NS * kSlot];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i0 = (int)blockIdx.x * per_wg;
+    const int i1 = min(i0 + per_wg, nitems);
+    if (i0 >= i1) return;
+    const int nkb = S.K >> 6;
+    const int ksb = S.kb_per_split;                     // <= kKsMax
+    const int ppi = (ksb + KP - 1) / KP;                // stages per item
+    const int total = (i1 - i0) * ppi;
+    const int koff = (lane >> 4) << 4;
+    int8_t* myring = ring[wave];
+
+    // ---- token slice of (pair, split) into LDS: fragment (tb, i) at (tb*kKsMax + i) KB
+    auto xload = [&](const XresItem& it) {
+        const StepPair& pp = S.pair[it.pair];
+        const int kb0 = it.split * ksb;
+        const int kbl = min(kb0 + ksb, nkb) - 1;        // last valid k-block of the split
+#pragma unroll
+        for (int u = 0; u < kXPerWave; ++u) {
+            const int q = wave + 4 * u, tb = q / kKsMax, i = q % kKsMax;
+            const int tok = tb * 16 + (lane & 15);
+            const int kb = min(kb0 + i, kbl);
+            dma16(pp.X + (int64_t)(tok < pp.M ? tok : 0) * S.ldx + (int64_t)kb * 64 + koff,
+                  xl + q * 1024);
+        }
+        if (wave == 0) dma4(pp.xs + min(lane, pp.M - 1), xl + kXBytes);
+    };
+
+    // ---- issue side: this wave's weight rows of the item being loaded
+    int icur = -1;
+    const int8_t* iw = nullptr;
+    const float* isc = nullptr;
+    int ikb0 = 0, ikbl = 0;
+    auto issue = [&](int g) {
+        if (g >= total) return;
+        const int item = i0 + g / ppi, piece = g - (g / ppi) * ppi;
+        if (item != icur) {
+            icur = item;
+            const XresItem it = xres_item(S, item);
+            const StepPair& pp = S.pair[it.pair];
+            const int N = S.rows[it.proj];
+            const int row0 = it.local * 64 + wave * 16;
+            iw = pp.W[it.proj] + (int64_t)min(row0 + (lane & 15), N - 1) * S.K + koff;
+            isc = pp.ws[it.proj] + min(row0 + (lane & 15), N - 1);
+            ikb0 = it.split * ksb;
+            ikbl = min(ikb0 + ksb, nkb) - 1;
+        }
+        int8_t* slot = myring + (g % NS) * kSlot;
+#pragma unroll
+        for (int i = 0; i < KP; ++i)
+            dma16(iw + (int64_t)min(ikb0 + piece * KP + i, ikbl) * 64, slot + i * 1024);
+        dma4(isc, slot + KP * 1024);
+    };
+
+    v4i acc[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[tb] = v4i{0, 0, 0, 0};
+
+    XresItem cur = xres_item(S, i0);
+    xload(cur);
+    wait_vmcnt<0>();
+    stage_barrier();
+#pragma unroll
+    for (int g = 0; g < NS - 1; ++g) issue(g);
+
+    for (int g = 0; g < total; ++g) {
+        const int item = i0 + g / ppi, piece = g - (g / ppi) * ppi;
+        if (piece == 0 && g > 0) {
+            const XresItem nx = xres_item(S, item);
+            if (nx.pair != cur.pair || nx.split != cur.split) {
+                stage_barrier();                         // every wave is done with the old slice
+                xload(nx);
+                wait_vmcnt<0>();
+                stage_barrier();
+            }
+            cur = nx;
+        }
+        const int ahead = min(NS - 2, total - 1 - g);
+        if (ahead <= 0) wait_vmcnt<0>();
+        else if (ahead == 1) wait_vmcnt<kLw>();
+        else if (ahead == 2) wait_vmcnt<2 * kLw>();
+        else if (ahead == 3) wait_vmcnt<3 * kLw>();
+        else wait_vmcnt<4 * kLw>();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        issue(g + NS - 1);                               // reuses the slot of stage g - 1
+        const int8_t* slot = myring + (g % NS) * kSlot;
+        const int ks0 = piece * KP;
+        const int npc = min(KP, min(ksb, nkb - cur.split * ksb) - ks0);
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+            if (i < npc) {
+                const v4i a = *reinterpret_cast<const v4i*>(slot + i * 1024 + lane * 16);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const v4i b = *reinterpret_cast<const v4i*>(xl + (tb * kKsMax + ks0 + i) * 1024 + lane * 16);
+                    acc[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[tb], 0, 0, 0);
+                }
+            }
+        }
+        if (piece == ppi - 1) {
+            const StepPair& pp = S.pair[cur.pair];
+            const int N = S.rows[cur.proj];
+            const int nw = cur.local * 64 + wave * 16;
+            const int rl = (lane >> 4) << 2;             // row of acc[.][0] within the wave's 16
+            const float* wsl = reinterpret_cast<const float*>(slot + KP * 1024);
+            const float* xsl = reinterpret_cast<const float*>(xl + kXBytes);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const int tok = tb * 16 + (lane & 15);
+                const int n = nw + rl;                   // first of this lane's 4 rows
+                if (tok < pp.M) {
+                    if (!S.partials) {
+                        const float xs = xsl[tok];
+                        float4 v;
+                        v.x = epilogue(acc[tb][0], wsl[rl], xs);
+                        v.y = epilogue(acc[tb][1], wsl[rl + 1], xs);
+                        v.z = epilogue(acc[tb][2], wsl[rl + 2], xs);
+                        v.w = epilogue(acc[tb][3], wsl[rl + 3], xs);
+                        float* y = pp.Y + S.yoff[cur.proj] + (int64_t)tok * S.ldy + n;
+                        if (n + 3 < N) {
+                            *reinterpret_cast<float4*>(y) = v;   // rows n..n+3: 16 bytes
+                        } else {
+                            if (n < N) y[0] = v.x;
+                            if (n + 1 < N) y[1] = v.y;
+                            if (n + 2 < N) y[2] = v.z;
+                        }
+                        if (pp.Y2) {
+                            float* y2 = pp.Y2 + (int64_t)tok * S.ldy2 + n;
+                            if (n < N) y2[0] = v.x;
+                            if (n + 1 < N) y2[1] = v.y;
+                            if (n + 2 < N) y2[2] = v.z;
+                            if (n + 3 < N) y2[3] = v.w;
+                        }
+                    } else {
+                        int* part = pp.part + (int64_t)cur.split * S.part_stride + (int64_t)tok * S.ldp + n;
+                        if (n + 3 < N) {
+                            *reinterpret_cast<v4i*>(part) = acc[tb];
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 3; ++r)
+                                if (n + r < N) part[r] = acc[tb][r];
+                        }
+                    }
+                }
+                acc[tb] = v4i{0, 0, 0, 0};
+            }
+        }
+    }
+}
+
+// One workgroup per compute unit (the LDS holds a token slice and four rings),
+// each taking a contiguous run of work items.
+hipError_t launch_gemm_xres(const StackStep& S, int token_blocks, hipStream_t s)
+{
+    const int nitems = S.npairs * S.splits * S.tile_off[S.nproj];
+    if (nitems <= 0) return hipSuccess;
+    if (S.kb_per_split > 16 || (S.splits > 1 && !S.partials)) return hipErrorInvalidValue;
+    const int grid = nitems < 256 ? nitems : 256;
+    const int per_wg = (nitems + grid - 1) / grid;
+    const dim3 g((nitems + per_wg - 1) / per_wg), b(256);
+    switch (token_blocks) {
+        case 1: hipLaunchKernelGGL((k_gemm_xres<1, 4, 6>), g, b, 0, s, S, nitems, per_wg); break;
+        case 2: hipLaunchKernelGGL((k_gemm_xres<2, 4, 6>), g, b, 0, s, S, nitems, per_wg); break;
+        case 3: hipLaunchKernelGGL((k_gemm_xres<3, 4, 4>), g, b, 0, s, S, nitems, per_wg); break;
+        case 4: hipLaunchKernelGGL((k_gemm_xres<4, 4, 4>), g, b, 0, s, S, nitems, per_wg); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace pf
