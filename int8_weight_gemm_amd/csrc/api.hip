@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <cstdlib>
 #include <cstring>
 #include <vector>
@@ -256,6 +257,39 @@ double product_bytes(int64_t N, int64_t K, int64_t M)
     return (double)N * K + 4.0 * N + (double)M * K + 4.0 * M + 4.0 * M * N;
 }
 
+// Two library-owned streams per device (default priority, non-blocking) and
+// the events that fork them from and join them back to the caller's stream.
+// Created on first use and kept until the process ends; the mutex serialises
+// calls that use them from several host threads.
+struct DevStreams {
+    std::mutex mu;
+    bool ready = false;
+    hipStream_t s[2] = {nullptr, nullptr};
+    hipEvent_t fork = nullptr;
+    hipEvent_t join[2] = {nullptr, nullptr};
+};
+DevStreams g_streams[64];
+
+DevStreams* dev_streams()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    DevStreams* d = &g_streams[dev];
+    return d;
+}
+
+pf_status ensure_streams(DevStreams* d)
+{
+    if (d->ready) return PF_OK;
+    for (int i = 0; i < 2; ++i)
+        if (hipStreamCreateWithFlags(&d->s[i], hipStreamNonBlocking) != hipSuccess) return PF_ELAUNCH;
+    if (hipEventCreateWithFlags(&d->fork, hipEventDisableTiming) != hipSuccess) return PF_ELAUNCH;
+    for (int i = 0; i < 2; ++i)
+        if (hipEventCreateWithFlags(&d->join[i], hipEventDisableTiming) != hipSuccess) return PF_ELAUNCH;
+    d->ready = true;
+    return PF_OK;
+}
+
 // Launch bookkeeping of pf_prefill_stack: counts launches and algorithmic
 // bytes per kernel class and, when asked, brackets every launch with a pair of
 // HIP events on the caller's stream to time it.
@@ -278,19 +312,20 @@ public:
         return PF_OK;
     }
     template <class F>
-    pf_status run(Kind k, double bytes, F&& launch)
+    pf_status run(Kind k, double bytes, F&& launch, hipStream_t on = nullptr)
     {
+        hipStream_t s = on ? on : s_;
         hipEvent_t e0 = nullptr, e1 = nullptr;
         if (timed_) {
             if (hipEventCreate(&e0) != hipSuccess) return fail();
             events_.push_back(e0);
             if (hipEventCreate(&e1) != hipSuccess) return fail();
             events_.push_back(e1);
-            if (hipEventRecord(e0, s_) != hipSuccess) return fail();
+            if (hipEventRecord(e0, s) != hipSuccess) return fail();
         }
         const pf_status st = launch();
         if (st) return st;
-        if (timed_ && hipEventRecord(e1, s_) != hipSuccess) return fail();
+        if (timed_ && hipEventRecord(e1, s) != hipSuccess) return fail();
         ++launches_[k];
         bytes_[k] += bytes;
         if (timed_) kinds_.push_back(k);
@@ -360,11 +395,19 @@ struct StackRun {
     char* ws;
     StackLayout lay;
     hipStream_t s;
+    int ng = 1;            // chunk groups, each on its own stream (chunk c in group c % ng)
 
     int64_t H() const { return st->hidden; }
     int64_t F() const { return st->ffn; }
     int64_t NT() const { return 5 * st->hidden + 2 * st->ffn; }
-    char* slot(int64_t c) const { return ws + (size_t)(c % lay.slots) * lay.slot_bytes; }
+    int64_t L() const { return st->n_layers; }
+    int64_t gslots() const { return lay.slots / ng; }
+    // a chunk in flight owns one slot of its group for all of its layers
+    char* slot(int64_t c) const
+    {
+        const int64_t g = c % ng, k = c / ng;
+        return ws + (size_t)(g * gslots() + k % gslots()) * lay.slot_bytes;
+    }
     // projection rows of (chunk c, layer l): [M][NT], q..down concatenated
     float* rows(int64_t c, int64_t l) const
     {
@@ -376,16 +419,56 @@ struct StackRun {
         const int64_t o[PF_NPROJ] = {0, H(), 2 * H(), 3 * H(), 4 * H(), 4 * H() + F(), 4 * H() + 2 * F()};
         return o[j];
     }
-    int64_t start(int64_t c) const
+    // step at which the group's k-th chunk enters layer 0: one step after the
+    // previous chunk, and never before the chunk gslots() earlier has left
+    int64_t start(int64_t k) const
     {
-        const int64_t L = st->n_layers, S = lay.slots;
-        return c + (c / S) * (L - S);
+        const int64_t S = gslots();
+        return k + (k / S) * std::max<int64_t>(L() - S, 0);
+    }
+    int64_t chunks() const { return (P + ch - 1) / ch; }
+    int64_t group_chunks(int g) const { return (chunks() - g + ng - 1) / ng; }
+    int64_t group_steps(int g) const
+    {
+        const int64_t K = group_chunks(g);
+        return K > 0 ? start(K - 1) + L() : 0;
     }
 
-    pf_status sweep(Recorder& rec)
+    // Chunks run in `ng` independent groups, one stream each, so that one
+    // group's launches fill the start-up and tail of the other's.
+    pf_status sweep(Recorder& rec, DevStreams* ds)
     {
-        const int64_t L = st->n_layers, C = (P + ch - 1) / ch;
-        const int64_t nsteps = start(C - 1) + L;
+        if (ng == 1) {
+            int64_t fin = -1;
+            for (int64_t step = 0; step <= group_steps(0); ++step)
+                if (pf_status r = group_step(rec, 0, step, fin, s)) return r;
+            return PF_OK;
+        }
+        if (hipEventRecord(ds->fork, s) != hipSuccess) return PF_ELAUNCH;
+        for (int g = 0; g < ng; ++g)
+            if (hipStreamWaitEvent(ds->s[g], ds->fork, 0) != hipSuccess) return PF_ELAUNCH;
+        int64_t fin[2] = {-1, -1};
+        const int64_t nst = std::max(group_steps(0), group_steps(1));
+        for (int64_t step = 0; step <= nst; ++step)
+            for (int g = 0; g < ng; ++g)
+                if (step <= group_steps(g))
+                    if (pf_status r = group_step(rec, g, step, fin[g], ds->s[g])) return r;
+        for (int g = 0; g < ng; ++g) {
+            if (hipEventRecord(ds->join[g], ds->s[g]) != hipSuccess) return PF_ELAUNCH;
+            if (hipStreamWaitEvent(s, ds->join[g], 0) != hipSuccess) return PF_ELAUNCH;
+        }
+        return PF_OK;
+    }
+
+    // One step of group g: the (chunk, layer) pairs of one diagonal.  Per step:
+    // quantise the layer inputs (rebuilding them from the previous down
+    // product's split partials on the skinny path), the six K = H products,
+    // quantise up, the down product.  `fin` carries the chunk whose last down
+    // product ran in the previous step; its rows are rebuilt without
+    // quantisation into the output.  step == group_steps(g) only finalises.
+    pf_status group_step(Recorder& rec, int g, int64_t step, int64_t& fin, hipStream_t sg)
+    {
+        const int64_t L = this->L(), K = group_chunks(g);
         const bool skinny = ch <= 64;
         // token-resident kernel for the six K = H products when a split of H fits
         const bool xres_a = skinny && H() / 64 <= 16;
@@ -393,147 +476,142 @@ struct StackRun {
         const int64_t rowsA[6] = {H(), H(), H(), H(), F(), F()};
         const int tm = (int)((ch + 127) / 128);
         const int tb = (int)((ch + 15) / 16);
-        int64_t fin = -1;                     // chunk whose last down product ran last step
-        int64_t c_lo = 0;
-        for (int64_t step = 0; step <= nsteps; ++step) {
-            while (c_lo < C && start(c_lo) + L <= step) ++c_lo;
-            std::vector<int64_t> cs;
-            if (step < nsteps)
-                for (int64_t c = c_lo; c < C && start(c) <= step; ++c) cs.push_back(c);
-            QuantStep qa, qd;
-            StackStep A, D;
-            std::memset(&qa, 0, sizeof(qa));
-            std::memset(&qd, 0, sizeof(qd));
-            std::memset(&A, 0, sizeof(A));
-            std::memset(&D, 0, sizeof(D));
-            qa.K = (int)H();
-            qd.K = (int)F();
-            A.nproj = 6;
-            A.K = (int)H();
-            A.splits = 1;
-            A.kb_per_split = (int)(H() / 64);
-            D.nproj = 1;
-            D.K = (int)F();
-            D.splits = skinny ? sd : 1;
-            D.partials = skinny ? 1 : 0;
-            D.kb_per_split = (int)((F() / 64 + D.splits - 1) / D.splits);
-            A.tiles_m = D.tiles_m = tm;
-            A.ldx = H();
-            D.ldx = F();
-            A.ldy = D.ldy = NT();
-            D.ldy2 = H();
-            D.ldp = H();
-            D.part_stride = ch * H();
-            for (int j = 0; j < 6; ++j) {
-                A.rows[j] = (int)rowsA[j];
-                A.yoff[j] = (int)offs(j);
-                const int64_t t = skinny ? (rowsA[j] + kSkinnyRows - 1) / kSkinnyRows
-                                         : ((rowsA[j] + 127) / 128) * tm;
-                A.tile_off[j + 1] = A.tile_off[j] + (int)t;
-            }
-            D.rows[0] = (int)H();
-            D.yoff[0] = (int)offs(6);
-            D.tile_off[1] = (int)(skinny ? (H() + kSkinnyRows - 1) / kSkinnyRows : ((H() + 127) / 128) * tm);
-            double qa_bytes = 0, qd_bytes = 0, a_bytes = 0, d_bytes = 0;
-            int rows_a = 0, rows_d = 0;
-            auto rebuild = [&](QuantPair& q, int64_t c, int64_t l_prev, bool last) {
-                // rows of (c, l_prev)'s down product, from its split partials
-                char* sl = slot(c);
-                q.part = reinterpret_cast<const int*>(sl + lay.part);
-                q.part_stride = ch * H();
-                q.splits = sd;
-                q.ws = st->layers[l_prev].w_scale[6];
-                q.as = reinterpret_cast<const float*>(sl + lay.sb);
-                q.h = rows(c, l_prev) + offs(6);
-                q.ldh = NT();
-                q.y = last ? y + c * ch * H() : nullptr;
-            };
-            for (size_t i = 0; i < cs.size(); ++i) {
-                const int64_t c = cs[i], l = step - start(c);
-                const int64_t c0 = c * ch, M = std::min(ch, P - c0);
-                const pf_layer& ly = st->layers[l];
-                char* sl = slot(c);
-                int8_t* a = reinterpret_cast<int8_t*>(sl + lay.a);
-                int8_t* b = reinterpret_cast<int8_t*>(sl + lay.b);
-                float* sa = reinterpret_cast<float*>(sl + lay.sa);
-                float* sb = reinterpret_cast<float*>(sl + lay.sb);
-                float* out = rows(c, l);
-                QuantPair& q0 = qa.pair[qa.npairs++];
-                if (l == 0) {
-                    q0.src = x + c0 * H();
-                    q0.ld = H();
-                } else if (skinny) {
-                    rebuild(q0, c, l - 1, false);
-                    qa_bytes += (double)M * H() * 4 * sd + (double)M * H() * 4;
-                } else {
-                    q0.src = rows(c, l - 1) + offs(6);
-                    q0.ld = NT();
-                }
-                q0.q = a;
-                q0.s = sa;
-                q0.row0 = rows_a;
-                rows_a += (int)M;
-                QuantPair& q1 = qd.pair[qd.npairs++];
-                q1.src = out + offs(5);
-                q1.ld = NT();
-                q1.q = b;
-                q1.s = sb;
-                q1.row0 = rows_d;
-                rows_d += (int)M;
-                StepPair& pa = A.pair[A.npairs++];
-                for (int j = 0; j < 6; ++j) {
-                    pa.W[j] = ly.W[j];
-                    pa.ws[j] = ly.w_scale[j];
-                    a_bytes += product_bytes(rowsA[j], H(), M);
-                }
-                pa.X = a;
-                pa.xs = sa;
-                pa.Y = out;
-                pa.M = (int)M;
-                StepPair& pd = D.pair[D.npairs++];
-                pd.W[0] = ly.W[6];
-                pd.ws[0] = ly.w_scale[6];
-                pd.X = b;
-                pd.xs = sb;
-                pd.Y = out;
-                pd.Y2 = (!skinny && l == L - 1) ? y + c0 * H() : nullptr;
-                pd.part = reinterpret_cast<int*>(sl + lay.part);
-                pd.M = (int)M;
-                d_bytes += product_bytes(H(), F(), M);
-                qa_bytes += (double)M * H() * 5 + M * 4.0;
-                qd_bytes += (double)M * F() * 5 + M * 4.0;
-            }
-            if (fin >= 0) {
-                // the chunk that left the last layer: rebuild its output, no quantisation
-                const int64_t M = std::min(ch, P - fin * ch);
-                QuantPair& qf = qa.pair[qa.npairs++];
-                rebuild(qf, fin, L - 1, true);
-                qf.row0 = rows_a;
-                rows_a += (int)M;
-                qa_bytes += (double)M * H() * 4 * (sd + 2);
-                fin = -1;
-            }
-            qa.total_rows = rows_a;
-            qd.total_rows = rows_d;
-            pf_status r = PF_OK;
-            if (qa.npairs > 0)
-                r = rec.run(Recorder::kQuant, qa_bytes, [&] { return launched(launch_quantize_step(qa, s)); });
-            if (r) return r;
-            if (cs.empty()) continue;
-            r = rec.run(Recorder::kProduct, a_bytes, [&] {
-                if (!skinny) return launched(launch_gemm_tiled_step(A, s));
-                return launched(xres_a ? launch_gemm_xres(A, tb, s) : launch_gemm_stream(A, tb, s));
-            });
-            if (!r) r = rec.run(Recorder::kQuant, qd_bytes,
-                                [&] { return launched(launch_quantize_step(qd, s)); });
-            if (!r) r = rec.run(Recorder::kProduct, d_bytes, [&] {
-                return launched(skinny ? launch_gemm_xres(D, tb, s) : launch_gemm_tiled_step(D, s));
-            });
-            if (r) return r;
-            if (skinny)
-                for (int64_t c : cs)
-                    if (step - start(c) == L - 1) fin = c;
+        std::vector<int64_t> cs;              // global chunk indices active in this step
+        if (step < group_steps(g))
+            for (int64_t k = 0; k < K && start(k) <= step; ++k)
+                if (start(k) + L > step) cs.push_back(g + k * ng);
+        QuantStep qa, qd;
+        StackStep A, D;
+        std::memset(&qa, 0, sizeof(qa));
+        std::memset(&qd, 0, sizeof(qd));
+        std::memset(&A, 0, sizeof(A));
+        std::memset(&D, 0, sizeof(D));
+        qa.K = (int)H();
+        qd.K = (int)F();
+        A.nproj = 6;
+        A.K = (int)H();
+        A.splits = 1;
+        A.kb_per_split = (int)(H() / 64);
+        D.nproj = 1;
+        D.K = (int)F();
+        D.splits = skinny ? sd : 1;
+        D.partials = skinny ? 1 : 0;
+        D.kb_per_split = (int)((F() / 64 + D.splits - 1) / D.splits);
+        A.tiles_m = D.tiles_m = tm;
+        A.ldx = H();
+        D.ldx = F();
+        A.ldy = D.ldy = NT();
+        D.ldy2 = H();
+        D.ldp = H();
+        D.part_stride = ch * H();
+        for (int j = 0; j < 6; ++j) {
+            A.rows[j] = (int)rowsA[j];
+            A.yoff[j] = (int)offs(j);
+            const int64_t t = skinny ? (rowsA[j] + kSkinnyRows - 1) / kSkinnyRows
+                                     : ((rowsA[j] + 127) / 128) * tm;
+            A.tile_off[j + 1] = A.tile_off[j] + (int)t;
         }
+        D.rows[0] = (int)H();
+        D.yoff[0] = (int)offs(6);
+        D.tile_off[1] = (int)(skinny ? (H() + kSkinnyRows - 1) / kSkinnyRows : ((H() + 127) / 128) * tm);
+        double qa_bytes = 0, qd_bytes = 0, a_bytes = 0, d_bytes = 0;
+        int rows_a = 0, rows_d = 0;
+        auto rebuild = [&](QuantPair& q, int64_t c, int64_t l_prev, bool last) {
+            // rows of (c, l_prev)'s down product, from its split partials
+            char* sl = slot(c);
+            q.part = reinterpret_cast<const int*>(sl + lay.part);
+            q.part_stride = ch * H();
+            q.splits = sd;
+            q.ws = st->layers[l_prev].w_scale[6];
+            q.as = reinterpret_cast<const float*>(sl + lay.sb);
+            q.h = rows(c, l_prev) + offs(6);
+            q.ldh = NT();
+            q.y = last ? y + c * ch * H() : nullptr;
+        };
+        for (size_t i = 0; i < cs.size(); ++i) {
+            const int64_t c = cs[i], l = step - start(c / ng);
+            const int64_t c0 = c * ch, M = std::min(ch, P - c0);
+            const pf_layer& ly = st->layers[l];
+            char* sl = slot(c);
+            int8_t* a = reinterpret_cast<int8_t*>(sl + lay.a);
+            int8_t* b = reinterpret_cast<int8_t*>(sl + lay.b);
+            float* sa = reinterpret_cast<float*>(sl + lay.sa);
+            float* sb = reinterpret_cast<float*>(sl + lay.sb);
+            float* out = rows(c, l);
+            QuantPair& q0 = qa.pair[qa.npairs++];
+            if (l == 0) {
+                q0.src = x + c0 * H();
+                q0.ld = H();
+            } else if (skinny) {
+                rebuild(q0, c, l - 1, false);
+                qa_bytes += (double)M * H() * 4 * sd + (double)M * H() * 4;
+            } else {
+                q0.src = rows(c, l - 1) + offs(6);
+                q0.ld = NT();
+            }
+            q0.q = a;
+            q0.s = sa;
+            q0.row0 = rows_a;
+            rows_a += (int)M;
+            QuantPair& q1 = qd.pair[qd.npairs++];
+            q1.src = out + offs(5);
+            q1.ld = NT();
+            q1.q = b;
+            q1.s = sb;
+            q1.row0 = rows_d;
+            rows_d += (int)M;
+            StepPair& pa = A.pair[A.npairs++];
+            for (int j = 0; j < 6; ++j) {
+                pa.W[j] = ly.W[j];
+                pa.ws[j] = ly.w_scale[j];
+                a_bytes += product_bytes(rowsA[j], H(), M);
+            }
+            pa.X = a;
+            pa.xs = sa;
+            pa.Y = out;
+            pa.M = (int)M;
+            StepPair& pd = D.pair[D.npairs++];
+            pd.W[0] = ly.W[6];
+            pd.ws[0] = ly.w_scale[6];
+            pd.X = b;
+            pd.xs = sb;
+            pd.Y = out;
+            pd.Y2 = (!skinny && l == L - 1) ? y + c0 * H() : nullptr;
+            pd.part = reinterpret_cast<int*>(sl + lay.part);
+            pd.M = (int)M;
+            d_bytes += product_bytes(H(), F(), M);
+            qa_bytes += (double)M * H() * 5 + M * 4.0;
+            qd_bytes += (double)M * F() * 5 + M * 4.0;
+        }
+        if (fin >= 0) {
+            // the chunk that left the last layer: rebuild its output, no quantisation
+            const int64_t M = std::min(ch, P - fin * ch);
+            QuantPair& qf = qa.pair[qa.npairs++];
+            rebuild(qf, fin, L - 1, true);
+            qf.row0 = rows_a;
+            rows_a += (int)M;
+            qa_bytes += (double)M * H() * 4 * (sd + 2);
+            fin = -1;
+        }
+        qa.total_rows = rows_a;
+        qd.total_rows = rows_d;
+        pf_status r = PF_OK;
+        if (qa.npairs > 0)
+            r = rec.run(Recorder::kQuant, qa_bytes, [&] { return launched(launch_quantize_step(qa, sg)); }, sg);
+        if (r || cs.empty()) return r;
+        r = rec.run(Recorder::kProduct, a_bytes, [&] {
+            if (!skinny) return launched(launch_gemm_tiled_step(A, sg));
+            return launched(xres_a ? launch_gemm_xres(A, tb, sg) : launch_gemm_stream(A, tb, sg));
+        }, sg);
+        if (!r) r = rec.run(Recorder::kQuant, qd_bytes,
+                            [&] { return launched(launch_quantize_step(qd, sg)); }, sg);
+        if (!r) r = rec.run(Recorder::kProduct, d_bytes, [&] {
+            return launched(skinny ? launch_gemm_xres(D, tb, sg) : launch_gemm_tiled_step(D, sg));
+        }, sg);
+        if (r) return r;
+        if (skinny)
+            for (int64_t c : cs)
+                if (step - start(c / ng) == L - 1) fin = c;
         return PF_OK;
     }
 
@@ -760,8 +838,16 @@ pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int
                      (hipStream_t)stream};
         Recorder rec(run.s, stats != nullptr, timed);
         const bool per_token = per_token_mode();
+        // two chunk groups on two streams when there are chunks and slots for both
+        DevStreams* ds = dev_streams();
+        const int64_t C = (P + ch - 1) / ch;
+        std::unique_lock<std::mutex> lock;
+        if (!per_token && ds && C >= 2 && lay.slots >= 2) {
+            lock = std::unique_lock<std::mutex>(ds->mu);
+            if (ensure_streams(ds) == PF_OK) run.ng = 2;
+        }
         pf_status st = rec.begin();
-        if (st == PF_OK) st = per_token ? run.per_token(rec) : run.sweep(rec);
+        if (st == PF_OK) st = per_token ? run.per_token(rec) : run.sweep(rec, ds);
         if (st == PF_OK) st = rec.end();
         if (st == PF_OK && stats) {
             std::memset(stats, 0, sizeof(*stats));
