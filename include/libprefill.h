@@ -117,8 +117,9 @@ typedef struct {
 } pf_stack;
 
 /* Statistics of one pf_prefill_stack call.  time_kernels is the only input:
- * set it to 1 to bracket every launch with HIP events on the call's stream and
- * get per-class device times (adds an event pair per launch).  Algorithmic
+ * set it to 1 to give every launch a pair of HIP events stamped when the kernel
+ * itself starts and ends (hipExtLaunchKernelGGL) and get per-class device
+ * times; kernels of the two chunk groups may overlap in time.  Algorithmic
  * bytes count each kernel's inputs read once and outputs written once: for a
  * product, weights + weight scales + quantised tokens + token scales + f32
  * outputs; for a quantisation, f32 inputs + int8 codes + scales. */

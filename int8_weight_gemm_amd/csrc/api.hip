@@ -15,6 +15,8 @@
 
 using namespace pf;
 
+thread_local pf::LaunchEvents pf::t_launch_events;
+
 namespace {
 
 constexpr int64_t kMaxK = 131072;
@@ -314,18 +316,18 @@ public:
     template <class F>
     pf_status run(Kind k, double bytes, F&& launch, hipStream_t on = nullptr)
     {
-        hipStream_t s = on ? on : s_;
+        (void)on;
         hipEvent_t e0 = nullptr, e1 = nullptr;
         if (timed_) {
             if (hipEventCreate(&e0) != hipSuccess) return fail();
             events_.push_back(e0);
             if (hipEventCreate(&e1) != hipSuccess) return fail();
             events_.push_back(e1);
-            if (hipEventRecord(e0, s) != hipSuccess) return fail();
+            t_launch_events = LaunchEvents{e0, e1};   // stamped at kernel start and end
         }
         const pf_status st = launch();
+        t_launch_events = LaunchEvents{};
         if (st) return st;
-        if (timed_ && hipEventRecord(e1, s) != hipSuccess) return fail();
         ++launches_[k];
         bytes_[k] += bytes;
         if (timed_) kinds_.push_back(k);

@@ -30,7 +30,7 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s)
     size_t blocks = (n16 + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     if (blocks == 0) blocks = 1;
-    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, s,
+    PF_LAUNCH(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, s,
                        reinterpret_cast<v4i*>(p), n16, reinterpret_cast<int8_t*>(p) + n16 * 16,
                        ntail);
     return hipGetLastError();
@@ -80,7 +80,7 @@ hipError_t launch_quantize(const float* x, int64_t ldx, int M, int K, int8_t* q,
                            hipStream_t s)
 {
     if (M <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_quantize, dim3(M), dim3(256), 0, s, x, ldx, K, q, scale);
+    PF_LAUNCH(k_quantize, dim3(M), dim3(256), 0, s, x, ldx, K, q, scale);
     return hipGetLastError();
 }
 
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void k_quantize_step(QuantStep S)
 hipError_t launch_quantize_step(const QuantStep& S, hipStream_t s)
 {
     if (S.total_rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_quantize_step, dim3(S.total_rows), dim3(256), 0, s, S);
+    PF_LAUNCH(k_quantize_step, dim3(S.total_rows), dim3(256), 0, s, S);
     return hipGetLastError();
 }
 
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemmSet set)
 hipError_t launch_gemv(const GemmSet& set, hipStream_t s)
 {
     if (set.total_tiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_gemv, dim3(set.total_tiles), dim3(256), 0, s, set);
+    PF_LAUNCH(k_gemv, dim3(set.total_tiles), dim3(256), 0, s, set);
     return hipGetLastError();
 }
 
@@ -341,10 +341,10 @@ constexpr int kSkPiece = 8;
 
 #define PF_SKINNY_CASES(KERNEL, ARG)                                                   \
     switch (token_blocks) {                                                            \
-        case 1: hipLaunchKernelGGL((KERNEL<1, kSkPiece>), g, b, 0, s, ARG); break;      \
-        case 2: hipLaunchKernelGGL((KERNEL<2, kSkPiece>), g, b, 0, s, ARG); break;      \
-        case 3: hipLaunchKernelGGL((KERNEL<3, kSkPiece>), g, b, 0, s, ARG); break;      \
-        case 4: hipLaunchKernelGGL((KERNEL<4, kSkPiece>), g, b, 0, s, ARG); break;      \
+        case 1: PF_LAUNCH((KERNEL<1, kSkPiece>), g, b, 0, s, ARG); break;      \
+        case 2: PF_LAUNCH((KERNEL<2, kSkPiece>), g, b, 0, s, ARG); break;      \
+        case 3: PF_LAUNCH((KERNEL<3, kSkPiece>), g, b, 0, s, ARG); break;      \
+        case 4: PF_LAUNCH((KERNEL<4, kSkPiece>), g, b, 0, s, ARG); break;      \
         default: return hipErrorInvalidValue;                                          \
     }
 
@@ -367,7 +367,7 @@ hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t 
     // problems without splits get no blocks: find_prob never selects them
     // because their tile_begin equals the next problem's.
     r.total_tiles = begin;
-    hipLaunchKernelGGL(k_split_reduce, dim3(begin), b, 0, s, r);
+    PF_LAUNCH(k_split_reduce, dim3(begin), b, 0, s, r);
     return hipGetLastError();
 }
 
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled_step(StackStep S)
 hipError_t launch_gemm_tiled(const GemmSet& set, hipStream_t s)
 {
     if (set.total_tiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_gemm_tiled, dim3(set.total_tiles), dim3(256), 0, s, set);
+    PF_LAUNCH(k_gemm_tiled, dim3(set.total_tiles), dim3(256), 0, s, set);
     return hipGetLastError();
 }
 
@@ -505,7 +505,7 @@ hipError_t launch_gemm_tiled_step(const StackStep& S, hipStream_t s)
 {
     const int blocks = S.npairs * S.tile_off[S.nproj];
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_gemm_tiled_step, dim3(blocks), dim3(256), 0, s, S);
+    PF_LAUNCH(k_gemm_tiled_step, dim3(blocks), dim3(256), 0, s, S);
     return hipGetLastError();
 }
 

@@ -1,11 +1,32 @@
 // kernels.hpp — kernel argument blocks and host-side launch wrappers of libprefill.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace pf {
+
+// Start/stop events for the next kernel launch of this host thread, or nulls.
+// hipExtLaunchKernelGGL stamps them when the kernel itself starts and ends (the
+// times a kernel-trace profiler reports), so a timed launch carries no
+// dispatch latency in its measured duration.
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+extern thread_local LaunchEvents t_launch_events;
+
+#define PF_LAUNCH(KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                 \
+    do {                                                                                  \
+        if (::pf::t_launch_events.start)                                                  \
+            hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM,                     \
+                                  ::pf::t_launch_events.start, ::pf::t_launch_events.stop, \
+                                  0, __VA_ARGS__);                                        \
+        else                                                                              \
+            hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);          \
+    } while (0)
 
 // One int8 product y[t][n] = epilogue(sum_k W[n][k] * X[t][k]) of a grouped launch.
 struct GemmProb {

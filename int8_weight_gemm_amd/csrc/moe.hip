@@ -60,7 +60,7 @@ hipError_t launch_router(const float* Wr, const float* x, int E, int H, int T, f
 {
     if (T <= 0) return hipSuccess;
     dim3 g((E + kRtTile - 1) / kRtTile, (T + kRtTile - 1) / kRtTile);
-    hipLaunchKernelGGL(k_router, g, dim3(256), 0, s, Wr, x, E, H, T, logits);
+    PF_LAUNCH(k_router, g, dim3(256), 0, s, Wr, x, E, H, T, logits);
     return hipGetLastError();
 }
 
@@ -179,7 +179,7 @@ hipError_t launch_expf(const float* x, int64_t n, float* y, hipStream_t s)
     if (n <= 0) return hipSuccess;
     int64_t blocks = (n + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(k_expf, dim3((unsigned)blocks), dim3(256), 0, s, x, n, y);
+    PF_LAUNCH(k_expf, dim3((unsigned)blocks), dim3(256), 0, s, x, n, y);
     return hipGetLastError();
 }
 
@@ -248,7 +248,7 @@ hipError_t launch_softmax_topk(const float* logits, int E, int T, int k, int* id
                                hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_softmax_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, E, T, k, ids, w);
+    PF_LAUNCH(k_softmax_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, E, T, k, ids, w);
     return hipGetLastError();
 }
 
@@ -315,7 +315,7 @@ hipError_t launch_group(const int* ids, const float* w, int T, int k, int E, int
                         int* pair_tok, int* comb_row, float* comb_w, hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), group_lds_bytes(T, E), s, ids, w, T, k, E,
+    PF_LAUNCH(k_group, dim3(1), dim3(1024), group_lds_bytes(T, E), s, ids, w, T, k, E,
                        off, pair_tok, comb_row, comb_w);
     return hipGetLastError();
 }
@@ -416,8 +416,8 @@ __global__ __launch_bounds__(256) void k_expert(ExpertArgs A)
 hipError_t launch_expert(const ExpertArgs& a, hipStream_t s)
 {
     const dim3 g(a.E * a.tiles_n), b(256);
-    if (a.W1) hipLaunchKernelGGL(k_expert<true>, g, b, 0, s, a);
-    else hipLaunchKernelGGL(k_expert<false>, g, b, 0, s, a);
+    if (a.W1) PF_LAUNCH(k_expert<true>, g, b, 0, s, a);
+    else PF_LAUNCH(k_expert<false>, g, b, 0, s, a);
     return hipGetLastError();
 }
 
@@ -444,7 +444,7 @@ hipError_t launch_combine(const float* ypair, const int* comb_row, const float* 
                           int k, int H, float* out, hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, ypair, comb_row, comb_w, k, H, out);
+    PF_LAUNCH(k_combine, dim3(T), dim3(256), 0, s, ypair, comb_row, comb_w, k, H, out);
     return hipGetLastError();
 }
 

@@ -187,10 +187,10 @@ hipError_t launch_gemm_stream(const StackStep& S, int token_blocks, hipStream_t 
     const int grid = ntiles < 512 ? ntiles : 512;
     const dim3 g(grid), b(256);
     switch (token_blocks) {
-        case 1: hipLaunchKernelGGL((k_gemm_stream<1, 4, 4>), g, b, 0, s, S, ntiles); break;
-        case 2: hipLaunchKernelGGL((k_gemm_stream<2, 4, 3>), g, b, 0, s, S, ntiles); break;
-        case 3: hipLaunchKernelGGL((k_gemm_stream<3, 4, 3>), g, b, 0, s, S, ntiles); break;
-        case 4: hipLaunchKernelGGL((k_gemm_stream<4, 4, 3>), g, b, 0, s, S, ntiles); break;
+        case 1: PF_LAUNCH((k_gemm_stream<1, 4, 4>), g, b, 0, s, S, ntiles); break;
+        case 2: PF_LAUNCH((k_gemm_stream<2, 4, 3>), g, b, 0, s, S, ntiles); break;
+        case 3: PF_LAUNCH((k_gemm_stream<3, 4, 3>), g, b, 0, s, S, ntiles); break;
+        case 4: PF_LAUNCH((k_gemm_stream<4, 4, 3>), g, b, 0, s, S, ntiles); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -402,10 +402,10 @@ hipError_t launch_gemm_xres(const StackStep& S, int token_blocks, hipStream_t s)
     const int per_wg = (nitems + grid - 1) / grid;
     const dim3 g((nitems + per_wg - 1) / per_wg), b(256);
     switch (token_blocks) {
-        case 1: hipLaunchKernelGGL((k_gemm_xres<1, 4, 6>), g, b, 0, s, S, nitems, per_wg); break;
-        case 2: hipLaunchKernelGGL((k_gemm_xres<2, 4, 6>), g, b, 0, s, S, nitems, per_wg); break;
-        case 3: hipLaunchKernelGGL((k_gemm_xres<3, 4, 4>), g, b, 0, s, S, nitems, per_wg); break;
-        case 4: hipLaunchKernelGGL((k_gemm_xres<4, 4, 4>), g, b, 0, s, S, nitems, per_wg); break;
+        case 1: PF_LAUNCH((k_gemm_xres<1, 4, 6>), g, b, 0, s, S, nitems, per_wg); break;
+        case 2: PF_LAUNCH((k_gemm_xres<2, 4, 6>), g, b, 0, s, S, nitems, per_wg); break;
+        case 3: PF_LAUNCH((k_gemm_xres<3, 4, 4>), g, b, 0, s, S, nitems, per_wg); break;
+        case 4: PF_LAUNCH((k_gemm_xres<4, 4, 4>), g, b, 0, s, S, nitems, per_wg); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
