@@ -197,14 +197,150 @@ hipError_t launch_gemm_stream(const StackStep& S, int token_blocks, hipStream_t 
 }
 
 // ---------------------------------------------------------------------------
+// LDS reads of DMA-filled buffers.  The compiler's wait-count pass cannot tell
+// which LDS bytes an LDS DMA writes, so in front of an LDS read that it can see
+// it may wait for every DMA still in flight (vmcnt(0)), which empties the ring
+// each stage.  These reads are inline assembly, invisible to that pass, and end
+// with their own lgkmcnt(0); that the DMA data has landed is the caller's
+// vmcnt wait (its own wave's DMAs) or a barrier after one (other waves').
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ v4f lds_read_v4f(uint32_t a)
+{
+    v4f r;
+    asm volatile("ds_read_b128 %0, %1\n"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r) : "v"(a));
+    return r;
+}
+
+__device__ __forceinline__ float lds_read_f32(uint32_t a)
+{
+    float r;
+    asm volatile("ds_read_b32 %0, %1\n"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r) : "v"(a));
+    return r;
+}
+
+// One stage's MFMA operands (4 k-blocks): the weight fragment of each k-block
+// (at wa + 1 KB i) and the token fragments of TB token blocks (at
+// xa + (16 tb + i) KB), in one assembly block.
+template <int TB>
+struct StageFrags {
+    v4i a[4];
+    v4i b[TB][4];
+};
+
+template <int TB>
+__device__ __forceinline__ void lds_stage(StageFrags<TB>& f, uint32_t wa, uint32_t xa);
+
+template <>
+__device__ __forceinline__ void lds_stage<1>(StageFrags<1>& f, uint32_t wa, uint32_t xa)
+{
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:0\n"
+        "ds_read_b128 %1, %9 offset:0\n"
+        "ds_read_b128 %2, %8 offset:1024\n"
+        "ds_read_b128 %3, %9 offset:1024\n"
+        "ds_read_b128 %4, %8 offset:2048\n"
+        "ds_read_b128 %5, %9 offset:2048\n"
+        "ds_read_b128 %6, %8 offset:3072\n"
+        "ds_read_b128 %7, %9 offset:3072\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.a[1]), "=&v"(f.b[0][1]), "=&v"(f.a[2]), "=&v"(f.b[0][2]), "=&v"(f.a[3]), "=&v"(f.b[0][3])
+        : "v"(wa), "v"(xa));
+}
+
+template <>
+__device__ __forceinline__ void lds_stage<2>(StageFrags<2>& f, uint32_t wa, uint32_t xa)
+{
+    asm volatile(
+        "ds_read_b128 %0, %12 offset:0\n"
+        "ds_read_b128 %1, %13 offset:0\n"
+        "ds_read_b128 %2, %13 offset:16384\n"
+        "ds_read_b128 %3, %12 offset:1024\n"
+        "ds_read_b128 %4, %13 offset:1024\n"
+        "ds_read_b128 %5, %13 offset:17408\n"
+        "ds_read_b128 %6, %12 offset:2048\n"
+        "ds_read_b128 %7, %13 offset:2048\n"
+        "ds_read_b128 %8, %13 offset:18432\n"
+        "ds_read_b128 %9, %12 offset:3072\n"
+        "ds_read_b128 %10, %13 offset:3072\n"
+        "ds_read_b128 %11, %13 offset:19456\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.b[1][0]), "=&v"(f.a[1]), "=&v"(f.b[0][1]), "=&v"(f.b[1][1]), "=&v"(f.a[2]), "=&v"(f.b[0][2]), "=&v"(f.b[1][2]), "=&v"(f.a[3]), "=&v"(f.b[0][3]), "=&v"(f.b[1][3])
+        : "v"(wa), "v"(xa));
+}
+
+template <>
+__device__ __forceinline__ void lds_stage<3>(StageFrags<3>& f, uint32_t wa, uint32_t xa)
+{
+    asm volatile(
+        "ds_read_b128 %0, %16 offset:0\n"
+        "ds_read_b128 %1, %17 offset:0\n"
+        "ds_read_b128 %2, %17 offset:16384\n"
+        "ds_read_b128 %3, %17 offset:32768\n"
+        "ds_read_b128 %4, %16 offset:1024\n"
+        "ds_read_b128 %5, %17 offset:1024\n"
+        "ds_read_b128 %6, %17 offset:17408\n"
+        "ds_read_b128 %7, %17 offset:33792\n"
+        "ds_read_b128 %8, %16 offset:2048\n"
+        "ds_read_b128 %9, %17 offset:2048\n"
+        "ds_read_b128 %10, %17 offset:18432\n"
+        "ds_read_b128 %11, %17 offset:34816\n"
+        "ds_read_b128 %12, %16 offset:3072\n"
+        "ds_read_b128 %13, %17 offset:3072\n"
+        "ds_read_b128 %14, %17 offset:19456\n"
+        "ds_read_b128 %15, %17 offset:35840\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.b[1][0]), "=&v"(f.b[2][0]), "=&v"(f.a[1]), "=&v"(f.b[0][1]), "=&v"(f.b[1][1]), "=&v"(f.b[2][1]), "=&v"(f.a[2]), "=&v"(f.b[0][2]), "=&v"(f.b[1][2]), "=&v"(f.b[2][2]), "=&v"(f.a[3]), "=&v"(f.b[0][3]), "=&v"(f.b[1][3]), "=&v"(f.b[2][3])
+        : "v"(wa), "v"(xa));
+}
+
+template <>
+__device__ __forceinline__ void lds_stage<4>(StageFrags<4>& f, uint32_t wa, uint32_t xa)
+{
+    asm volatile(
+        "ds_read_b128 %0, %20 offset:0\n"
+        "ds_read_b128 %1, %21 offset:0\n"
+        "ds_read_b128 %2, %21 offset:16384\n"
+        "ds_read_b128 %3, %21 offset:32768\n"
+        "ds_read_b128 %4, %21 offset:49152\n"
+        "ds_read_b128 %5, %20 offset:1024\n"
+        "ds_read_b128 %6, %21 offset:1024\n"
+        "ds_read_b128 %7, %21 offset:17408\n"
+        "ds_read_b128 %8, %21 offset:33792\n"
+        "ds_read_b128 %9, %21 offset:50176\n"
+        "ds_read_b128 %10, %20 offset:2048\n"
+        "ds_read_b128 %11, %21 offset:2048\n"
+        "ds_read_b128 %12, %21 offset:18432\n"
+        "ds_read_b128 %13, %21 offset:34816\n"
+        "ds_read_b128 %14, %21 offset:51200\n"
+        "ds_read_b128 %15, %20 offset:3072\n"
+        "ds_read_b128 %16, %21 offset:3072\n"
+        "ds_read_b128 %17, %21 offset:19456\n"
+        "ds_read_b128 %18, %21 offset:35840\n"
+        "ds_read_b128 %19, %21 offset:52224\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.b[1][0]), "=&v"(f.b[2][0]), "=&v"(f.b[3][0]), "=&v"(f.a[1]), "=&v"(f.b[0][1]), "=&v"(f.b[1][1]), "=&v"(f.b[2][1]), "=&v"(f.b[3][1]), "=&v"(f.a[2]), "=&v"(f.b[0][2]), "=&v"(f.b[1][2]), "=&v"(f.b[2][2]), "=&v"(f.b[3][2]), "=&v"(f.a[3]), "=&v"(f.b[0][3]), "=&v"(f.b[1][3]), "=&v"(f.b[2][3]), "=&v"(f.b[3][3])
+        : "v"(wa), "v"(xa));
+}
+
+// ---------------------------------------------------------------------------
 // Token-resident weight stream.  A work item is (pair, K split, projection,
 // 64-row tile); items that share a pair and split share the token slice
 // [16 TB tokens][one split of K], which sits in LDS (as MFMA B fragments) for as
-// long as a workgroup works on that slice.  Each workgroup takes a contiguous
-// run of items, so it loads a slice once per run, not once per tile.  The
-// weights need no sharing: each wave streams its own 16 rows through a private
-// ring of NS LDS slots by DMA and waits only on its own vector-memory counter,
-// so the waves never meet at a barrier except when the token slice changes.
+// long as a workgroup works on that slice.  Each workgroup takes a run of items
+// inside one slice, so it loads its slice once.  The weights need no sharing:
+// each wave streams its own 16 rows through a private ring of NS LDS slots by
+// DMA and waits only on its own vector-memory counter, so the waves meet at a
+// barrier only once, after the slice has landed.
 // Every slot also carries the 16 rows' scales (one 4-byte DMA).  An item ends
 // with the epilogue, or (S.partials) stores its int32 partial tile, which the
 // following quantisation launch sums over the splits (rebuild mode).
@@ -231,20 +367,25 @@ __device__ __forceinline__ XresItem xres_item(const StackStep& S, int item)
 }
 
 template <int TB, int KP, int NS>
-__global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int nitems, int per_wg)
+__global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int wg_per_group, int per_wg)
 {
     constexpr int kKsMax = 16;                          // k-blocks per split, at most
     constexpr int kXBytes = TB * kKsMax * 1024;         // resident token slice
     constexpr int kXPerWave = TB * kKsMax / 4;          // token DMAs per wave per slice
     constexpr int kSlot = KP * 1024 + 256;              // KP k-blocks of 16 rows + 64 scales
     constexpr int kLw = KP + 1;                         // DMAs per wave per stage
-    static_assert(kLw * (NS - 2) <= 63, "vmcnt range");
+    static_assert(kLw * (NS - 1) <= 63, "vmcnt range");
+    static_assert(KP == 4, "lds_stage reads 4 k-blocks");
     __shared__ __attribute__((aligned(16))) int8_t xl[kXBytes + 256];
     __shared__ __attribute__((aligned(16))) int8_t ring[4][NS * kSlot];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int i0 = (int)blockIdx.x * per_wg;
-    const int i1 = min(i0 + per_wg, nitems);
+    // workgroup -> a run of items inside one (pair, split) group, so the token
+    // slice is loaded once
+    const int per_group = S.tile_off[S.nproj];
+    const int grp = (int)blockIdx.x / wg_per_group, j = (int)blockIdx.x % wg_per_group;
+    const int i0 = grp * per_group + j * per_wg;
+    const int i1 = min(i0 + per_wg, (grp + 1) * per_group);
     if (i0 >= i1) return;
     const int nkb = S.K >> 6;
     const int ksb = S.kb_per_split;                     // <= kKsMax
@@ -299,25 +440,20 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int nitems, int 
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) acc[tb] = v4i{0, 0, 0, 0};
 
+    // token slice first, then the first NS - 1 weight stages; loads complete in
+    // issue order, so waiting until only the weight stages are outstanding
+    // leaves them in flight while the slice is made visible to every wave
     XresItem cur = xres_item(S, i0);
     xload(cur);
-    wait_vmcnt<0>();
-    stage_barrier();
 #pragma unroll
     for (int g = 0; g < NS - 1; ++g) issue(g);
+    if (total >= NS - 1) wait_vmcnt<(NS - 1) * kLw>();
+    else wait_vmcnt<0>();
+    stage_barrier();
 
     for (int g = 0; g < total; ++g) {
         const int item = i0 + g / ppi, piece = g - (g / ppi) * ppi;
-        if (piece == 0 && g > 0) {
-            const XresItem nx = xres_item(S, item);
-            if (nx.pair != cur.pair || nx.split != cur.split) {
-                stage_barrier();                         // every wave is done with the old slice
-                xload(nx);
-                wait_vmcnt<0>();
-                stage_barrier();
-            }
-            cur = nx;
-        }
+        if (piece == 0 && g > 0) cur = xres_item(S, item);   // same (pair, split) throughout
         const int ahead = min(NS - 2, total - 1 - g);
         if (ahead <= 0) wait_vmcnt<0>();
         else if (ahead == 1) wait_vmcnt<kLw>();
@@ -326,18 +462,19 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int nitems, int 
         else wait_vmcnt<4 * kLw>();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         issue(g + NS - 1);                               // reuses the slot of stage g - 1
-        const int8_t* slot = myring + (g % NS) * kSlot;
+        const uint32_t slot = lds_addr(myring + (g % NS) * kSlot);
         const int ks0 = piece * KP;
         const int npc = min(KP, min(ksb, nkb - cur.split * ksb) - ks0);
+        // all KP k-blocks are read (k-blocks past the split's end hold clamped
+        // copies); only the first npc enter the product
+        StageFrags<TB> f;
+        lds_stage<TB>(f, slot + lane * 16, lds_addr(xl) + ks0 * 1024 + lane * 16);
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
             if (i < npc) {
-                const v4i a = *reinterpret_cast<const v4i*>(slot + i * 1024 + lane * 16);
 #pragma unroll
-                for (int tb = 0; tb < TB; ++tb) {
-                    const v4i b = *reinterpret_cast<const v4i*>(xl + (tb * kKsMax + ks0 + i) * 1024 + lane * 16);
-                    acc[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[tb], 0, 0, 0);
-                }
+                for (int tb = 0; tb < TB; ++tb)
+                    acc[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.a[i], f.b[tb][i], acc[tb], 0, 0, 0);
             }
         }
         if (piece == ppi - 1) {
@@ -345,20 +482,20 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int nitems, int 
             const int N = S.rows[cur.proj];
             const int nw = cur.local * 64 + wave * 16;
             const int rl = (lane >> 4) << 2;             // row of acc[.][0] within the wave's 16
-            const float* wsl = reinterpret_cast<const float*>(slot + KP * 1024);
-            const float* xsl = reinterpret_cast<const float*>(xl + kXBytes);
+            v4f wsl = v4f{0.f, 0.f, 0.f, 0.f};
+            if (!S.partials) wsl = lds_read_v4f(slot + KP * 1024 + rl * 4);   // rows rl .. rl + 3
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
                 const int tok = tb * 16 + (lane & 15);
                 const int n = nw + rl;                   // first of this lane's 4 rows
                 if (tok < pp.M) {
                     if (!S.partials) {
-                        const float xs = xsl[tok];
+                        const float xs = lds_read_f32(lds_addr(xl + kXBytes) + tok * 4);
                         float4 v;
-                        v.x = epilogue(acc[tb][0], wsl[rl], xs);
-                        v.y = epilogue(acc[tb][1], wsl[rl + 1], xs);
-                        v.z = epilogue(acc[tb][2], wsl[rl + 2], xs);
-                        v.w = epilogue(acc[tb][3], wsl[rl + 3], xs);
+                        v.x = epilogue(acc[tb][0], wsl[0], xs);
+                        v.y = epilogue(acc[tb][1], wsl[1], xs);
+                        v.z = epilogue(acc[tb][2], wsl[2], xs);
+                        v.w = epilogue(acc[tb][3], wsl[3], xs);
                         float* y = pp.Y + S.yoff[cur.proj] + (int64_t)tok * S.ldy + n;
                         if (n + 3 < N) {
                             *reinterpret_cast<float4*>(y) = v;   // rows n..n+3: 16 bytes
@@ -395,17 +532,21 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int nitems, int 
 // each taking a contiguous run of work items.
 hipError_t launch_gemm_xres(const StackStep& S, int token_blocks, hipStream_t s)
 {
-    const int nitems = S.npairs * S.splits * S.tile_off[S.nproj];
-    if (nitems <= 0) return hipSuccess;
+    const int groups = S.npairs * S.splits;              // (pair, split) token slices
+    const int per_group = S.tile_off[S.nproj];           // tiles per slice
+    if (groups <= 0 || per_group <= 0) return hipSuccess;
     if (S.kb_per_split > 16 || (S.splits > 1 && !S.partials)) return hipErrorInvalidValue;
-    const int grid = nitems < 256 ? nitems : 256;
-    const int per_wg = (nitems + grid - 1) / grid;
-    const dim3 g((nitems + per_wg - 1) / per_wg), b(256);
+    // about one workgroup per compute unit, each with an equal run of one slice's tiles
+    int wpg = 256 / groups;
+    if (wpg < 1) wpg = 1;
+    if (wpg > per_group) wpg = per_group;
+    const int per_wg = (per_group + wpg - 1) / wpg;
+    const dim3 g(groups * wpg), b(256);
     switch (token_blocks) {
-        case 1: PF_LAUNCH((k_gemm_xres<1, 4, 6>), g, b, 0, s, S, nitems, per_wg); break;
-        case 2: PF_LAUNCH((k_gemm_xres<2, 4, 6>), g, b, 0, s, S, nitems, per_wg); break;
-        case 3: PF_LAUNCH((k_gemm_xres<3, 4, 4>), g, b, 0, s, S, nitems, per_wg); break;
-        case 4: PF_LAUNCH((k_gemm_xres<4, 4, 4>), g, b, 0, s, S, nitems, per_wg); break;
+        case 1: PF_LAUNCH((k_gemm_xres<1, 4, 6>), g, b, 0, s, S, wpg, per_wg); break;
+        case 2: PF_LAUNCH((k_gemm_xres<2, 4, 6>), g, b, 0, s, S, wpg, per_wg); break;
+        case 3: PF_LAUNCH((k_gemm_xres<3, 4, 4>), g, b, 0, s, S, wpg, per_wg); break;
+        case 4: PF_LAUNCH((k_gemm_xres<4, 4, 4>), g, b, 0, s, S, wpg, per_wg); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
