@@ -74,7 +74,6 @@ struct SkinnyPlan {
 };
 
 constexpr int kSkinnyRows = 64;
-constexpr int64_t kComputeUnits = 256;
 
 SkinnyPlan plan_skinny(int64_t N, int64_t K, int64_t total_tiles)
 {
@@ -161,6 +160,8 @@ pf_status run_products(GemmSet& set, int64_t M, hipStream_t s)
 // projection rows [chunk][5H+2F] used when the caller keeps none.  A chunk in
 // flight owns one slot for all of its layers.
 struct StackLayout {
+    int groups;           // chunk groups (one stream each)
+    int gslots;           // slots per group: chunks of a group in flight at once
     int slots;
     int dsplits;          // K splits of the down product (skinny path)
     size_t a, b, sa, sb, proj, part, slot_bytes, total;
@@ -172,10 +173,23 @@ int down_splits(int64_t F, int64_t chunk)
     return chunk <= 64 ? (int)((F / 64 + 15) / 16) : 1;
 }
 
+constexpr int kMaxGroups = 4;        // library streams per device
+
+// Chunk groups of the stack sweep and the slots of each: three groups (three
+// library streams; with the caller's stream that is the four hardware queues
+// a process gets by default) of up to 16 chunks in flight.  A step of a group
+// launches one product over all of its chunks in flight, so a group's slots
+// are at most kMaxPairs.
+constexpr int kStackGroups = 3;
+constexpr int kGroupSlots = 16;
+static_assert(kStackGroups <= kMaxGroups && kGroupSlots <= kMaxPairs, "stack sweep shape");
+
 StackLayout stack_layout(int64_t L, int64_t H, int64_t F, int64_t chunk)
 {
     StackLayout S{};
-    S.slots = (int)std::min<int64_t>(L, kMaxPairs);
+    S.groups = kStackGroups;
+    S.gslots = (int)std::min<int64_t>(L, kGroupSlots);
+    S.slots = S.groups * S.gslots;
     S.dsplits = down_splits(F, chunk);
     size_t o = 0;
     S.a = o; o += round_up((size_t)chunk * H, kAlign);
@@ -259,16 +273,17 @@ double product_bytes(int64_t N, int64_t K, int64_t M)
     return (double)N * K + 4.0 * N + (double)M * K + 4.0 * M + 4.0 * M * N;
 }
 
-// Two library-owned streams per device (default priority, non-blocking) and
-// the events that fork them from and join them back to the caller's stream.
+// Library-owned streams per device, one per chunk group (default priority,
+// non-blocking), and the events that fork them from and join them back to the
+// caller's stream.
 // Created on first use and kept until the process ends; the mutex serialises
 // calls that use them from several host threads.
 struct DevStreams {
     std::mutex mu;
     bool ready = false;
-    hipStream_t s[2] = {nullptr, nullptr};
+    hipStream_t s[kMaxGroups] = {};
     hipEvent_t fork = nullptr;
-    hipEvent_t join[2] = {nullptr, nullptr};
+    hipEvent_t join[kMaxGroups] = {};
 };
 DevStreams g_streams[64];
 
@@ -283,10 +298,10 @@ DevStreams* dev_streams()
 pf_status ensure_streams(DevStreams* d)
 {
     if (d->ready) return PF_OK;
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kMaxGroups; ++i)
         if (hipStreamCreateWithFlags(&d->s[i], hipStreamNonBlocking) != hipSuccess) return PF_ELAUNCH;
     if (hipEventCreateWithFlags(&d->fork, hipEventDisableTiming) != hipSuccess) return PF_ELAUNCH;
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kMaxGroups; ++i)
         if (hipEventCreateWithFlags(&d->join[i], hipEventDisableTiming) != hipSuccess) return PF_ELAUNCH;
     d->ready = true;
     return PF_OK;
@@ -403,7 +418,7 @@ struct StackRun {
     int64_t F() const { return st->ffn; }
     int64_t NT() const { return 5 * st->hidden + 2 * st->ffn; }
     int64_t L() const { return st->n_layers; }
-    int64_t gslots() const { return lay.slots / ng; }
+    int64_t gslots() const { return lay.gslots; }
     // a chunk in flight owns one slot of its group for all of its layers
     char* slot(int64_t c) const
     {
@@ -449,8 +464,9 @@ struct StackRun {
         if (hipEventRecord(ds->fork, s) != hipSuccess) return PF_ELAUNCH;
         for (int g = 0; g < ng; ++g)
             if (hipStreamWaitEvent(ds->s[g], ds->fork, 0) != hipSuccess) return PF_ELAUNCH;
-        int64_t fin[2] = {-1, -1};
-        const int64_t nst = std::max(group_steps(0), group_steps(1));
+        int64_t fin[kMaxGroups] = {-1, -1, -1, -1};
+        int64_t nst = 0;
+        for (int g = 0; g < ng; ++g) nst = std::max(nst, group_steps(g));
         for (int64_t step = 0; step <= nst; ++step)
             for (int g = 0; g < ng; ++g)
                 if (step <= group_steps(g))
@@ -840,13 +856,13 @@ pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int
                      (hipStream_t)stream};
         Recorder rec(run.s, stats != nullptr, timed);
         const bool per_token = per_token_mode();
-        // two chunk groups on two streams when there are chunks and slots for both
+        // chunk groups on library streams when there are chunks for more than one
         DevStreams* ds = dev_streams();
         const int64_t C = (P + ch - 1) / ch;
         std::unique_lock<std::mutex> lock;
-        if (!per_token && ds && C >= 2 && lay.slots >= 2) {
+        if (!per_token && ds && C >= 2 && lay.groups >= 2) {
             lock = std::unique_lock<std::mutex>(ds->mu);
-            if (ensure_streams(ds) == PF_OK) run.ng = 2;
+            if (ensure_streams(ds) == PF_OK) run.ng = (int)std::min<int64_t>(lay.groups, C);
         }
         pf_status st = rec.begin();
         if (st == PF_OK) st = per_token ? run.per_token(rec) : run.sweep(rec, ds);

@@ -59,6 +59,7 @@ struct GemmSet {
 // each multiplying its chunk's quantised tokens with the same projection slots
 // (q..up, or down) of its own layer.  Workgroup b -> pair b / tiles_per_pair.
 constexpr int kMaxPairs = 16;
+constexpr int kComputeUnits = 256;          // MI355X (gfx950)
 struct StepPair {
     const int8_t* W[6];
     const float* ws[6];

@@ -228,20 +228,88 @@ __device__ __forceinline__ float lds_read_f32(uint32_t a)
     return r;
 }
 
-// One stage's MFMA operands (4 k-blocks): the weight fragment of each k-block
+// One stage's MFMA operands (KP k-blocks): the weight fragment of each k-block
 // (at wa + 1 KB i) and the token fragments of TB token blocks (at
 // xa + (16 tb + i) KB), in one assembly block.
-template <int TB>
+template <int TB, int KP>
 struct StageFrags {
-    v4i a[4];
-    v4i b[TB][4];
+    v4i a[KP];
+    v4i b[TB][KP];
 };
 
-template <int TB>
-__device__ __forceinline__ void lds_stage(StageFrags<TB>& f, uint32_t wa, uint32_t xa);
+template <int TB, int KP>
+__device__ __forceinline__ void lds_stage(StageFrags<TB, KP>& f, uint32_t wa, uint32_t xa);
 
 template <>
-__device__ __forceinline__ void lds_stage<1>(StageFrags<1>& f, uint32_t wa, uint32_t xa)
+__device__ __forceinline__ void lds_stage<1, 2>(StageFrags<1, 2>& f, uint32_t wa, uint32_t xa)
+{
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:0\n"
+        "ds_read_b128 %1, %5 offset:0\n"
+        "ds_read_b128 %2, %4 offset:1024\n"
+        "ds_read_b128 %3, %5 offset:1024\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.a[1]), "=&v"(f.b[0][1])
+        : "v"(wa), "v"(xa));
+}
+
+template <>
+__device__ __forceinline__ void lds_stage<2, 2>(StageFrags<2, 2>& f, uint32_t wa, uint32_t xa)
+{
+    asm volatile(
+        "ds_read_b128 %0, %6 offset:0\n"
+        "ds_read_b128 %1, %7 offset:0\n"
+        "ds_read_b128 %2, %7 offset:16384\n"
+        "ds_read_b128 %3, %6 offset:1024\n"
+        "ds_read_b128 %4, %7 offset:1024\n"
+        "ds_read_b128 %5, %7 offset:17408\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.b[1][0]), "=&v"(f.a[1]),
+          "=&v"(f.b[0][1]), "=&v"(f.b[1][1])
+        : "v"(wa), "v"(xa));
+}
+
+template <>
+__device__ __forceinline__ void lds_stage<3, 2>(StageFrags<3, 2>& f, uint32_t wa, uint32_t xa)
+{
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:0\n"
+        "ds_read_b128 %1, %9 offset:0\n"
+        "ds_read_b128 %2, %9 offset:16384\n"
+        "ds_read_b128 %3, %9 offset:32768\n"
+        "ds_read_b128 %4, %8 offset:1024\n"
+        "ds_read_b128 %5, %9 offset:1024\n"
+        "ds_read_b128 %6, %9 offset:17408\n"
+        "ds_read_b128 %7, %9 offset:33792\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.b[1][0]), "=&v"(f.b[2][0]),
+          "=&v"(f.a[1]), "=&v"(f.b[0][1]), "=&v"(f.b[1][1]), "=&v"(f.b[2][1])
+        : "v"(wa), "v"(xa));
+}
+
+template <>
+__device__ __forceinline__ void lds_stage<4, 2>(StageFrags<4, 2>& f, uint32_t wa, uint32_t xa)
+{
+    asm volatile(
+        "ds_read_b128 %0, %10 offset:0\n"
+        "ds_read_b128 %1, %11 offset:0\n"
+        "ds_read_b128 %2, %11 offset:16384\n"
+        "ds_read_b128 %3, %11 offset:32768\n"
+        "ds_read_b128 %4, %11 offset:49152\n"
+        "ds_read_b128 %5, %10 offset:1024\n"
+        "ds_read_b128 %6, %11 offset:1024\n"
+        "ds_read_b128 %7, %11 offset:17408\n"
+        "ds_read_b128 %8, %11 offset:33792\n"
+        "ds_read_b128 %9, %11 offset:50176\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.b[1][0]), "=&v"(f.b[2][0]),
+          "=&v"(f.b[3][0]), "=&v"(f.a[1]), "=&v"(f.b[0][1]), "=&v"(f.b[1][1]),
+          "=&v"(f.b[2][1]), "=&v"(f.b[3][1])
+        : "v"(wa), "v"(xa));
+}
+
+template <>
+__device__ __forceinline__ void lds_stage<1, 4>(StageFrags<1, 4>& f, uint32_t wa, uint32_t xa)
 {
     asm volatile(
         "ds_read_b128 %0, %8 offset:0\n"
@@ -253,12 +321,13 @@ __device__ __forceinline__ void lds_stage<1>(StageFrags<1>& f, uint32_t wa, uint
         "ds_read_b128 %6, %8 offset:3072\n"
         "ds_read_b128 %7, %9 offset:3072\n"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.a[1]), "=&v"(f.b[0][1]), "=&v"(f.a[2]), "=&v"(f.b[0][2]), "=&v"(f.a[3]), "=&v"(f.b[0][3])
+        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.a[1]), "=&v"(f.b[0][1]),
+          "=&v"(f.a[2]), "=&v"(f.b[0][2]), "=&v"(f.a[3]), "=&v"(f.b[0][3])
         : "v"(wa), "v"(xa));
 }
 
 template <>
-__device__ __forceinline__ void lds_stage<2>(StageFrags<2>& f, uint32_t wa, uint32_t xa)
+__device__ __forceinline__ void lds_stage<2, 4>(StageFrags<2, 4>& f, uint32_t wa, uint32_t xa)
 {
     asm volatile(
         "ds_read_b128 %0, %12 offset:0\n"
@@ -274,12 +343,14 @@ __device__ __forceinline__ void lds_stage<2>(StageFrags<2>& f, uint32_t wa, uint
         "ds_read_b128 %10, %13 offset:3072\n"
         "ds_read_b128 %11, %13 offset:19456\n"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.b[1][0]), "=&v"(f.a[1]), "=&v"(f.b[0][1]), "=&v"(f.b[1][1]), "=&v"(f.a[2]), "=&v"(f.b[0][2]), "=&v"(f.b[1][2]), "=&v"(f.a[3]), "=&v"(f.b[0][3]), "=&v"(f.b[1][3])
+        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.b[1][0]), "=&v"(f.a[1]),
+          "=&v"(f.b[0][1]), "=&v"(f.b[1][1]), "=&v"(f.a[2]), "=&v"(f.b[0][2]),
+          "=&v"(f.b[1][2]), "=&v"(f.a[3]), "=&v"(f.b[0][3]), "=&v"(f.b[1][3])
         : "v"(wa), "v"(xa));
 }
 
 template <>
-__device__ __forceinline__ void lds_stage<3>(StageFrags<3>& f, uint32_t wa, uint32_t xa)
+__device__ __forceinline__ void lds_stage<3, 4>(StageFrags<3, 4>& f, uint32_t wa, uint32_t xa)
 {
     asm volatile(
         "ds_read_b128 %0, %16 offset:0\n"
@@ -299,12 +370,15 @@ __device__ __forceinline__ void lds_stage<3>(StageFrags<3>& f, uint32_t wa, uint
         "ds_read_b128 %14, %17 offset:19456\n"
         "ds_read_b128 %15, %17 offset:35840\n"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.b[1][0]), "=&v"(f.b[2][0]), "=&v"(f.a[1]), "=&v"(f.b[0][1]), "=&v"(f.b[1][1]), "=&v"(f.b[2][1]), "=&v"(f.a[2]), "=&v"(f.b[0][2]), "=&v"(f.b[1][2]), "=&v"(f.b[2][2]), "=&v"(f.a[3]), "=&v"(f.b[0][3]), "=&v"(f.b[1][3]), "=&v"(f.b[2][3])
+        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.b[1][0]), "=&v"(f.b[2][0]),
+          "=&v"(f.a[1]), "=&v"(f.b[0][1]), "=&v"(f.b[1][1]), "=&v"(f.b[2][1]),
+          "=&v"(f.a[2]), "=&v"(f.b[0][2]), "=&v"(f.b[1][2]), "=&v"(f.b[2][2]),
+          "=&v"(f.a[3]), "=&v"(f.b[0][3]), "=&v"(f.b[1][3]), "=&v"(f.b[2][3])
         : "v"(wa), "v"(xa));
 }
 
 template <>
-__device__ __forceinline__ void lds_stage<4>(StageFrags<4>& f, uint32_t wa, uint32_t xa)
+__device__ __forceinline__ void lds_stage<4, 4>(StageFrags<4, 4>& f, uint32_t wa, uint32_t xa)
 {
     asm volatile(
         "ds_read_b128 %0, %20 offset:0\n"
@@ -328,7 +402,11 @@ __device__ __forceinline__ void lds_stage<4>(StageFrags<4>& f, uint32_t wa, uint
         "ds_read_b128 %18, %21 offset:35840\n"
         "ds_read_b128 %19, %21 offset:52224\n"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.b[1][0]), "=&v"(f.b[2][0]), "=&v"(f.b[3][0]), "=&v"(f.a[1]), "=&v"(f.b[0][1]), "=&v"(f.b[1][1]), "=&v"(f.b[2][1]), "=&v"(f.b[3][1]), "=&v"(f.a[2]), "=&v"(f.b[0][2]), "=&v"(f.b[1][2]), "=&v"(f.b[2][2]), "=&v"(f.b[3][2]), "=&v"(f.a[3]), "=&v"(f.b[0][3]), "=&v"(f.b[1][3]), "=&v"(f.b[2][3]), "=&v"(f.b[3][3])
+        : "=&v"(f.a[0]), "=&v"(f.b[0][0]), "=&v"(f.b[1][0]), "=&v"(f.b[2][0]),
+          "=&v"(f.b[3][0]), "=&v"(f.a[1]), "=&v"(f.b[0][1]), "=&v"(f.b[1][1]),
+          "=&v"(f.b[2][1]), "=&v"(f.b[3][1]), "=&v"(f.a[2]), "=&v"(f.b[0][2]),
+          "=&v"(f.b[1][2]), "=&v"(f.b[2][2]), "=&v"(f.b[3][2]), "=&v"(f.a[3]),
+          "=&v"(f.b[0][3]), "=&v"(f.b[1][3]), "=&v"(f.b[2][3]), "=&v"(f.b[3][3])
         : "v"(wa), "v"(xa));
 }
 
@@ -375,7 +453,7 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int wg_per_group
     constexpr int kSlot = KP * 1024 + 256;              // KP k-blocks of 16 rows + 64 scales
     constexpr int kLw = KP + 1;                         // DMAs per wave per stage
     static_assert(kLw * (NS - 1) <= 63, "vmcnt range");
-    static_assert(KP == 4, "lds_stage reads 4 k-blocks");
+    static_assert(KP == 2 || KP == 4, "lds_stage reads 2 or 4 k-blocks");
     __shared__ __attribute__((aligned(16))) int8_t xl[kXBytes + 256];
     __shared__ __attribute__((aligned(16))) int8_t ring[4][NS * kSlot];
 
@@ -467,8 +545,8 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int wg_per_group
         const int npc = min(KP, min(ksb, nkb - cur.split * ksb) - ks0);
         // all KP k-blocks are read (k-blocks past the split's end hold clamped
         // copies); only the first npc enter the product
-        StageFrags<TB> f;
-        lds_stage<TB>(f, slot + lane * 16, lds_addr(xl) + ks0 * 1024 + lane * 16);
+        StageFrags<TB, KP> f;
+        lds_stage<TB, KP>(f, slot + lane * 16, lds_addr(xl) + ks0 * 1024 + lane * 16);
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
             if (i < npc) {
@@ -528,23 +606,27 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int wg_per_group
     }
 }
 
-// One workgroup per compute unit (the LDS holds a token slice and four rings),
-// each taking a contiguous run of work items.
+// Up to 32 tokens (TB <= 2) the LDS of a workgroup (token slice + four rings of
+// five 2-k-block stages, 79 KB at TB = 2) fits twice on a compute unit: the
+// grid targets two workgroups per CU, so while one of them waits for its first
+// data the other streams, and launches of other streams find room.  Larger
+// token slices take 4-k-block stages at one workgroup per CU.  Each workgroup
+// takes a run of tiles inside one (pair, split) slice.
 hipError_t launch_gemm_xres(const StackStep& S, int token_blocks, hipStream_t s)
 {
     const int groups = S.npairs * S.splits;              // (pair, split) token slices
     const int per_group = S.tile_off[S.nproj];           // tiles per slice
     if (groups <= 0 || per_group <= 0) return hipSuccess;
     if (S.kb_per_split > 16 || (S.splits > 1 && !S.partials)) return hipErrorInvalidValue;
-    // about one workgroup per compute unit, each with an equal run of one slice's tiles
-    int wpg = 256 / groups;
+    const int target = token_blocks <= 2 ? 2 * kComputeUnits : kComputeUnits;
+    int wpg = target / groups;
     if (wpg < 1) wpg = 1;
     if (wpg > per_group) wpg = per_group;
     const int per_wg = (per_group + wpg - 1) / wpg;
     const dim3 g(groups * wpg), b(256);
     switch (token_blocks) {
-        case 1: PF_LAUNCH((k_gemm_xres<1, 4, 6>), g, b, 0, s, S, wpg, per_wg); break;
-        case 2: PF_LAUNCH((k_gemm_xres<2, 4, 6>), g, b, 0, s, S, wpg, per_wg); break;
+        case 1: PF_LAUNCH((k_gemm_xres<1, 2, 5>), g, b, 0, s, S, wpg, per_wg); break;
+        case 2: PF_LAUNCH((k_gemm_xres<2, 2, 5>), g, b, 0, s, S, wpg, per_wg); break;
         case 3: PF_LAUNCH((k_gemm_xres<3, 4, 4>), g, b, 0, s, S, wpg, per_wg); break;
         case 4: PF_LAUNCH((k_gemm_xres<4, 4, 4>), g, b, 0, s, S, wpg, per_wg); break;
         default: return hipErrorInvalidValue;
