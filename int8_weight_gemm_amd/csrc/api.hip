@@ -125,8 +125,8 @@ void make_tiled(GemmProb& g, const int8_t* W, const float* ws, int64_t N, int64_
     g.W = W; g.ws = ws; g.X = X; g.xs = xs; g.Y = Y;
     g.ldx = ldx; g.ldy = ldy;
     g.N = (int)N; g.K = (int)K; g.M = (int)M;
-    g.tiles_n = (int)((N + 127) / 128);
-    g.tiles_m = (int)((M + 127) / 128);
+    g.tiles_n = (int)((N + kTiledRows - 1) / kTiledRows);
+    g.tiles_m = (int)((M + tiled_tokens(M) - 1) / tiled_tokens(M));
     g.splits = 1; g.kb_per_split = (int)(K / 64);
 }
 
@@ -151,7 +151,7 @@ pf_status run_products(GemmSet& set, int64_t M, hipStream_t s)
         return launched(launch_gemm_skinny(set, token_blocks(M), s));
     }
     finish_set(set, 2);
-    return launched(launch_gemm_tiled(set, s));
+    return launched(launch_gemm_tiled(set, M, s));
 }
 
 // ---------------------------------------------------------------------------
@@ -492,7 +492,7 @@ struct StackRun {
         const bool xres_a = skinny && H() / 64 <= 16;
         const int sd = lay.dsplits;
         const int64_t rowsA[6] = {H(), H(), H(), H(), F(), F()};
-        const int tm = (int)((ch + 127) / 128);
+        const int tm = (int)((ch + tiled_tokens(ch) - 1) / tiled_tokens(ch));
         const int tb = (int)((ch + 15) / 16);
         std::vector<int64_t> cs;              // global chunk indices active in this step
         if (step < group_steps(g))
@@ -526,12 +526,12 @@ struct StackRun {
             A.rows[j] = (int)rowsA[j];
             A.yoff[j] = (int)offs(j);
             const int64_t t = skinny ? (rowsA[j] + kSkinnyRows - 1) / kSkinnyRows
-                                     : ((rowsA[j] + 127) / 128) * tm;
+                                     : ((rowsA[j] + kTiledRows - 1) / kTiledRows) * tm;
             A.tile_off[j + 1] = A.tile_off[j] + (int)t;
         }
         D.rows[0] = (int)H();
         D.yoff[0] = (int)offs(6);
-        D.tile_off[1] = (int)(skinny ? (H() + kSkinnyRows - 1) / kSkinnyRows : ((H() + 127) / 128) * tm);
+        D.tile_off[1] = (int)(skinny ? (H() + kSkinnyRows - 1) / kSkinnyRows : ((H() + kTiledRows - 1) / kTiledRows) * tm);
         double qa_bytes = 0, qd_bytes = 0, a_bytes = 0, d_bytes = 0;
         int rows_a = 0, rows_d = 0;
         auto rebuild = [&](QuantPair& q, int64_t c, int64_t l_prev, bool last) {
@@ -618,13 +618,13 @@ struct StackRun {
             r = rec.run(Recorder::kQuant, qa_bytes, [&] { return launched(launch_quantize_step(qa, sg)); }, sg);
         if (r || cs.empty()) return r;
         r = rec.run(Recorder::kProduct, a_bytes, [&] {
-            if (!skinny) return launched(launch_gemm_tiled_step(A, sg));
+            if (!skinny) return launched(launch_gemm_tiled_step(A, ch, sg));
             return launched(xres_a ? launch_gemm_xres(A, tb, sg) : launch_gemm_stream(A, tb, sg));
         }, sg);
         if (!r) r = rec.run(Recorder::kQuant, qd_bytes,
                             [&] { return launched(launch_quantize_step(qd, sg)); }, sg);
         if (!r) r = rec.run(Recorder::kProduct, d_bytes, [&] {
-            return launched(skinny ? launch_gemm_xres(D, tb, sg) : launch_gemm_tiled_step(D, sg));
+            return launched(skinny ? launch_gemm_xres(D, tb, sg) : launch_gemm_tiled_step(D, ch, sg));
         }, sg);
         if (r) return r;
         if (skinny)

@@ -381,132 +381,5 @@ hipError_t launch_gemm_skinny_step(const StackStep& S, int token_blocks, hipStre
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Tiled product (M > 64): 128 weight rows x 128 tokens per workgroup, k-blocks of
-// 64 bytes double-buffered through LDS, v_mfma_i32_32x32x32_i8 with 2 x 2 tiles of
-// 32 x 32 per wave (waves arranged 2 x 2 over the 128 x 128 tile).
-constexpr int kTlStride = 80;                      // LDS bytes per row (64 + 16 pad)
-constexpr int kTlRows = 128;
-
-__device__ __forceinline__ void tiled_tile(const GemmProb& P, int local)
-{
-    __shared__ __attribute__((aligned(16))) int8_t sw[2][kTlRows * kTlStride];
-    __shared__ __attribute__((aligned(16))) int8_t sx[2][kTlRows * kTlStride];
-    const int tm = local % P.tiles_m;
-    const int tn = local / P.tiles_m;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = tn * kTlRows, t0 = tm * kTlRows;
-    const int nkb = P.K >> 6;
-
-    // global -> register mapping: rows lr and lr + 64, 16-byte column lc
-    const int lr = tid >> 2, lc = (tid & 3) << 4;
-    const int8_t* wsrc[2];
-    const int8_t* xsrc[2];
-    bool xok[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int n = min(n0 + lr + 64 * h, P.N - 1);
-        wsrc[h] = P.W + (int64_t)n * P.K + lc;
-        const int t = t0 + lr + 64 * h;
-        xok[h] = t < P.M;
-        xsrc[h] = P.X + (int64_t)(xok[h] ? t : 0) * P.ldx + lc;
-    }
-    v4i rw[2], rx[2];
-    auto gload = [&](int kb) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            rw[h] = ld16(wsrc[h] + (int64_t)kb * 64);
-            rx[h] = xok[h] ? ld16(xsrc[h] + (int64_t)kb * 64) : v4i{0, 0, 0, 0};
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            st16(&sw[buf][(lr + 64 * h) * kTlStride + lc], rw[h]);
-            st16(&sx[buf][(lr + 64 * h) * kTlStride + lc], rx[h]);
-        }
-    };
-
-    const int wn = (wave >> 1) * 64, wm = (wave & 1) * 64;
-    v16i acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int buf = kb & 1;
-        if (kb + 1 < nkb) gload(kb + 1);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int col = ks * 32 + ((lane >> 5) << 4);
-            v4i a[2], b[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                a[i] = *reinterpret_cast<const v4i*>(&sw[buf][(wn + 32 * i + (lane & 31)) * kTlStride + col]);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                b[j] = *reinterpret_cast<const v4i*>(&sx[buf][(wm + 32 * j + (lane & 31)) * kTlStride + col]);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        if (kb + 1 < nkb) lstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // Lane l, register r of a 32x32 tile: row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int t = t0 + wm + 32 * j + (lane & 31);
-            if (t >= P.M) continue;
-            const float xs = P.xs[t];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int nb = n0 + wn + 32 * i + 8 * g + ((lane >> 5) << 2);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (nb + r < P.N) store_out(P, t, nb + r, epilogue(acc[i][j][4 * g + r], P.ws[nb + r], xs));
-            }
-        }
-    }
-}
-
-__global__ __launch_bounds__(256) void k_gemm_tiled(GemmSet set)
-{
-    const GemmProb P = find_prob(set, blockIdx.x);
-    tiled_tile(P, blockIdx.x - P.tile_begin);
-}
-
-__global__ __launch_bounds__(256) void k_gemm_tiled_step(StackStep S)
-{
-    int local;
-    const GemmProb P = step_prob(S, blockIdx.x, local);
-    tiled_tile(P, local);
-}
-
-hipError_t launch_gemm_tiled(const GemmSet& set, hipStream_t s)
-{
-    if (set.total_tiles <= 0) return hipSuccess;
-    PF_LAUNCH(k_gemm_tiled, dim3(set.total_tiles), dim3(256), 0, s, set);
-    return hipGetLastError();
-}
-
-hipError_t launch_gemm_tiled_step(const StackStep& S, hipStream_t s)
-{
-    const int blocks = S.npairs * S.tile_off[S.nproj];
-    if (blocks <= 0) return hipSuccess;
-    PF_LAUNCH(k_gemm_tiled_step, dim3(blocks), dim3(256), 0, s, S);
-    return hipGetLastError();
-}
 
 }  // namespace pf

@@ -139,11 +139,14 @@ hipError_t launch_quantize(const float* x, int64_t ldx, int M, int K, int8_t* q,
 hipError_t launch_quantize_step(const QuantStep& S, hipStream_t s);
 hipError_t launch_gemv(const GemmSet& set, hipStream_t s);
 hipError_t launch_gemm_skinny_step(const StackStep& S, int token_blocks, hipStream_t s);
-hipError_t launch_gemm_tiled_step(const StackStep& S, hipStream_t s);
+hipError_t launch_gemm_tiled_step(const StackStep& S, int64_t M, hipStream_t s);
 hipError_t launch_gemm_stream(const StackStep& S, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_xres(const StackStep& S, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t s);
-hipError_t launch_gemm_tiled(const GemmSet& set, hipStream_t s);
+hipError_t launch_gemm_tiled(const GemmSet& set, int64_t M, hipStream_t s);
+// Tiled product tiles: 256 weight rows x tiled_tokens(M) tokens.
+constexpr int kTiledRows = 256;
+int tiled_tokens(int64_t M);
 
 hipError_t launch_router(const float* Wr, const float* x, int E, int H, int T, float* logits,
                          hipStream_t s);

@@ -127,6 +127,28 @@ def test_tiled_matches_oracle(M):
     np.testing.assert_array_equal(host(y), oracle.linear(W, ws, q, s))
 
 
+@pytest.mark.parametrize("K", [64, 192, 256, 320, 1088])
+@pytest.mark.parametrize("M", [65, 256])
+def test_tiled_k_blocks_around_ring_depth(M, K):
+    """k-block counts below, at and just above the stage ring's depth, and odd."""
+    N = 520                              # two full 256-row tiles and 8 rows
+    W, ws, q, s = _proj(N, K, M, 900 + M + K)
+    y = pf.gemm_i8_chunk(dev(W), dev(ws), dev(q), dev(s))
+    np.testing.assert_array_equal(host(y), oracle.linear(W, ws, q, s))
+
+
+@pytest.mark.parametrize("M", [100, 200])
+def test_tiled_unaligned_output(M):
+    """An output that is only 4-byte aligned takes the scalar stores."""
+    N, K = 300, 512
+    W, ws, q, s = _proj(N, K, M, 700 + M)
+    buf = torch.full((M * N + 1,), -1.0, dtype=torch.float32, device="cuda")
+    out = buf[1:].view(M, N)
+    pf.gemm_i8_chunk(dev(W), dev(ws), dev(q), dev(s), out=out)
+    np.testing.assert_array_equal(host(out), oracle.linear(W, ws, q, s))
+    assert host(buf)[0] == -1.0
+
+
 def test_mfma_single_tiles_extreme_values():
     """One 16x16x64 and one 32x32x32 tile region with +-127 everywhere: operand
     layout and int32 range of the MFMA paths against exact integers."""
