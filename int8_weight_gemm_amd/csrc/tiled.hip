@@ -2,18 +2,24 @@
 //
 // "Batched Prefill" (cellm), §The arithmetic: with hundreds of tokens per chunk
 // every weight byte feeds hundreds of multiply-adds, so the product is bound by
-// the matrix cores, not by HBM.  The kernel is laid out for v_mfma_i32_16x16x64_i8
-// at full rate:
-//  * a workgroup owns 256 weight rows x 32 WM tokens (WM = 8 or 4); each of its
-//    four waves owns 128 rows x 16 WM tokens, i.e. 8 x WM accumulator blocks of
-//    16 x 16 (256 or 128 accumulation registers), so each operand fragment read
-//    from LDS feeds WM or 8 MFMAs;
-//  * a stage is one k-block (64 bytes of K) of the tile's 256 weight rows and
-//    32 WM tokens, copied by global_load_lds_dwordx4 straight into LDS in MFMA
-//    operand order (fragment = 16 rows x 64 bytes, lane l's 16 bytes at 16 l);
-//    NS stages are in flight, one barrier per stage;
-//  * the fragments of stage g + 1 are read from LDS while the MFMAs of stage g
-//    run (two register sets);
+// the matrix cores, not by HBM.  The kernel is laid out for v_mfma_i32_32x32x32_i8,
+// which keeps the matrix core of a SIMD busy from a single wave with a few
+// independent accumulators (the 16x16x64 form needs many more in flight):
+//  * a workgroup of four waves (one per SIMD, 512 registers each) owns 256
+//    weight rows x 64 WJ tokens (WJ = 4 or 2); wave (wn, wm) of the 2 x 2 grid
+//    owns 128 rows x 32 WJ tokens: 4 x WJ accumulator blocks of 32 x 32 in
+//    AGPRs;
+//  * a stage is one k-block (64 bytes of K) of the tile's weight rows and
+//    tokens in LDS as 1 KB fragments of 16 rows x 64 bytes (lane l's 16 bytes,
+//    row l % 16 and bytes 16 (l / 16) .. + 15, at 16 l), so every copy reads 16
+//    rows x 64 contiguous bytes; the MFMA operands are read from it with one
+//    conflict-free ds_read_b128 each; a ring of four stages, one barrier per
+//    stage, and the reads of stage g + 1 are in flight while the MFMAs of
+//    stage g run;
+//  * the token fragments are copied by global_load_lds_dwordx4, the weight
+//    fragments by ordinary 128-bit loads into registers (three stages ahead)
+//    and ds_write_b128: the direct copy alone cannot feed a compute unit at this
+//    rate, the two paths together can;
 //  * workgroups on one XCD (blockIdx % 8) take consecutive tiles, and the token
 //    tiles of one band of weight rows are consecutive, so the band is fetched
 //    from HBM once into that XCD's L2 and shared.
@@ -26,44 +32,76 @@
 
 namespace pf {
 
-constexpr int kTlWN = 8;                     // 16-row blocks per wave (128 rows)
 
-// One stage's operand fragments of a wave: 8 weight fragments, WM token ones.
+// One stage's MFMA operands of a wave: 8 weight operands (4 row blocks x 2 k
+// halves), WM token ones (WM / 2 token blocks x 2 k halves).
 template <int WM>
 struct TlFrags {
-    v4i a[kTlWN];
+    v4i a[8];
     v4i b[WM];
 };
 
-// Issue the wave's LDS reads of one stage (weight fragments at a + 1 KB i,
-// token fragments at b + 1 KB j) without waiting; tl_wait waits for them.  The
-// wait names every destination register, so no use of one can be placed
-// before it.
+// Issue the wave's LDS reads of one stage without waiting; tl_wait waits for
+// them.  Operand q = 2 i + kh (32-row block i, k half kh) is read at
+// a + 2 KB i + 512 kh (weights) or b + 2 KB i + 512 kh (tokens), a and b
+// carrying the lane's own offset in the block.  The wait names every
+// destination register, so no use of one can be placed before it.
 template <int WM>
 __device__ __forceinline__ void tl_issue(TlFrags<WM>& f, uint32_t a, uint32_t b);
 template <int WM>
 __device__ __forceinline__ void tl_wait(TlFrags<WM>& f);
 
 template <>
+__device__ __forceinline__ void tl_issue<4>(TlFrags<4>& f, uint32_t a, uint32_t b)
+{
+    asm volatile(
+        "ds_read_b128 %0, %12 offset:0\n"
+        "ds_read_b128 %1, %12 offset:512\n"
+        "ds_read_b128 %2, %12 offset:2048\n"
+        "ds_read_b128 %3, %12 offset:2560\n"
+        "ds_read_b128 %4, %12 offset:4096\n"
+        "ds_read_b128 %5, %12 offset:4608\n"
+        "ds_read_b128 %6, %12 offset:6144\n"
+        "ds_read_b128 %7, %12 offset:6656\n"
+        "ds_read_b128 %8, %13 offset:0\n"
+        "ds_read_b128 %9, %13 offset:512\n"
+        "ds_read_b128 %10, %13 offset:2048\n"
+        "ds_read_b128 %11, %13 offset:2560\n"
+        : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.a[2]), "=&v"(f.a[3]),
+          "=&v"(f.a[4]), "=&v"(f.a[5]), "=&v"(f.a[6]), "=&v"(f.a[7]),
+          "=&v"(f.b[0]), "=&v"(f.b[1]), "=&v"(f.b[2]), "=&v"(f.b[3])
+        : "v"(a), "v"(b));
+}
+
+template <>
+__device__ __forceinline__ void tl_wait<4>(TlFrags<4>& f)
+{
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]),
+                 "+v"(f.a[4]), "+v"(f.a[5]), "+v"(f.a[6]), "+v"(f.a[7]),
+                 "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]));
+}
+
+template <>
 __device__ __forceinline__ void tl_issue<8>(TlFrags<8>& f, uint32_t a, uint32_t b)
 {
     asm volatile(
         "ds_read_b128 %0, %16 offset:0\n"
-        "ds_read_b128 %1, %16 offset:1024\n"
+        "ds_read_b128 %1, %16 offset:512\n"
         "ds_read_b128 %2, %16 offset:2048\n"
-        "ds_read_b128 %3, %16 offset:3072\n"
+        "ds_read_b128 %3, %16 offset:2560\n"
         "ds_read_b128 %4, %16 offset:4096\n"
-        "ds_read_b128 %5, %16 offset:5120\n"
+        "ds_read_b128 %5, %16 offset:4608\n"
         "ds_read_b128 %6, %16 offset:6144\n"
-        "ds_read_b128 %7, %16 offset:7168\n"
+        "ds_read_b128 %7, %16 offset:6656\n"
         "ds_read_b128 %8, %17 offset:0\n"
-        "ds_read_b128 %9, %17 offset:1024\n"
+        "ds_read_b128 %9, %17 offset:512\n"
         "ds_read_b128 %10, %17 offset:2048\n"
-        "ds_read_b128 %11, %17 offset:3072\n"
+        "ds_read_b128 %11, %17 offset:2560\n"
         "ds_read_b128 %12, %17 offset:4096\n"
-        "ds_read_b128 %13, %17 offset:5120\n"
+        "ds_read_b128 %13, %17 offset:4608\n"
         "ds_read_b128 %14, %17 offset:6144\n"
-        "ds_read_b128 %15, %17 offset:7168\n"
+        "ds_read_b128 %15, %17 offset:6656\n"
         : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.a[2]), "=&v"(f.a[3]),
           "=&v"(f.a[4]), "=&v"(f.a[5]), "=&v"(f.a[6]), "=&v"(f.a[7]),
           "=&v"(f.b[0]), "=&v"(f.b[1]), "=&v"(f.b[2]), "=&v"(f.b[3]),
@@ -81,169 +119,219 @@ __device__ __forceinline__ void tl_wait<8>(TlFrags<8>& f)
                  "+v"(f.b[4]), "+v"(f.b[5]), "+v"(f.b[6]), "+v"(f.b[7]));
 }
 
-template <>
-__device__ __forceinline__ void tl_issue<4>(TlFrags<4>& f, uint32_t a, uint32_t b)
+// Four weight fragments of a stage into LDS (at a, a + 4 KB, a + 8 KB,
+// a + 12 KB); returns once they are written, so the source registers may be
+// reloaded.
+__device__ __forceinline__ void lds_write4(uint32_t a, v4i d0, v4i d1, v4i d2, v4i d3)
 {
-    asm volatile(
-        "ds_read_b128 %0, %12 offset:0\n"
-        "ds_read_b128 %1, %12 offset:1024\n"
-        "ds_read_b128 %2, %12 offset:2048\n"
-        "ds_read_b128 %3, %12 offset:3072\n"
-        "ds_read_b128 %4, %12 offset:4096\n"
-        "ds_read_b128 %5, %12 offset:5120\n"
-        "ds_read_b128 %6, %12 offset:6144\n"
-        "ds_read_b128 %7, %12 offset:7168\n"
-        "ds_read_b128 %8, %13 offset:0\n"
-        "ds_read_b128 %9, %13 offset:1024\n"
-        "ds_read_b128 %10, %13 offset:2048\n"
-        "ds_read_b128 %11, %13 offset:3072\n"
-        : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.a[2]), "=&v"(f.a[3]),
-          "=&v"(f.a[4]), "=&v"(f.a[5]), "=&v"(f.a[6]), "=&v"(f.a[7]),
-          "=&v"(f.b[0]), "=&v"(f.b[1]), "=&v"(f.b[2]), "=&v"(f.b[3])
-        : "v"(a), "v"(b));
+    asm volatile("ds_write_b128 %0, %1\n"
+                 "ds_write_b128 %0, %2 offset:4096\n"
+                 "ds_write_b128 %0, %3 offset:8192\n"
+                 "ds_write_b128 %0, %4 offset:12288\n"
+                 "s_waitcnt lgkmcnt(0)"
+                 :: "v"(a), "v"(d0), "v"(d1), "v"(d2), "v"(d3) : "memory");
 }
 
-template <>
-__device__ __forceinline__ void tl_wait<4>(TlFrags<4>& f)
-{
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]),
-                 "+v"(f.a[4]), "+v"(f.a[5]), "+v"(f.a[6]), "+v"(f.a[7]),
-                 "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]));
-}
-
-// vmcnt limited to `stages` whole stages of kL DMAs (stages <= NS - 1 <= 7).
-template <int kL>
-__device__ __forceinline__ void wait_stages(int stages)
-{
-    switch (stages) {
-        case 0: wait_vmcnt<0>(); break;
-        case 1: wait_vmcnt<kL>(); break;
-        case 2: wait_vmcnt<(2 * kL > 63 ? 63 : 2 * kL)>(); break;
-        case 3: wait_vmcnt<(3 * kL > 63 ? 63 : 3 * kL)>(); break;
-        case 4: wait_vmcnt<(4 * kL > 63 ? 63 : 4 * kL)>(); break;
-        default: wait_vmcnt<(5 * kL > 63 ? 63 : 5 * kL)>(); break;
-    }
-}
-
-// One 256 x 32 WM output tile of problem P (tile index `local`, token tiles
-// fastest).
-template <int WM, int NS>
+// One 256 x 64 WJ output tile of problem P (tile index `local`, token tiles
+// fastest).  Four waves in a 2 x 2 grid; wave (wn, wm) owns rows
+// 128 wn .. + 127 and tokens 32 WJ wm .. + 32 WJ - 1 of the tile: 4 x WJ
+// accumulator blocks of 32 x 32.  Stage s (one k-block) sits in ring slot
+// s % 4: weight fragments 0 .. 15 (16 rows x 64 bytes each), then token
+// fragments 0 .. 4 WJ - 1.  Per stage wave w loads weight fragments
+// w, w + 4, w + 8, w + 12 into registers (three stages ahead) and writes them
+// into the slot, and copies token fragments w + 4 h by DMA.  Iteration g:
+//   wait for stage g's fragments (read in iteration g - 1); wait for this
+//   wave's copies of stage g + 1 and its weight loads of stage g + 4;
+//   barrier (stage g + 1 published, stage g read by all); fill the slot of
+//   stage g with stage g + 4 and load the weights of stage g + 7; issue the
+//   reads of stage g + 1; the MFMAs of stage g, which overlap those reads and
+//   the copies.
+// Every iteration issues the same copies (k-blocks past the end are clamped
+// to the last one and land in free slots, never read), so every wait is a
+// constant.
+template <int WJ>
 __device__ __forceinline__ void tiled_block(const GemmProb& P, int local)
 {
-    constexpr int kFa = 2 * kTlWN, kFb = 2 * WM;          // fragments per stage
+    constexpr int NS = 4;
+    constexpr int WB = 2 * WJ;                           // token fragments per wave
+    constexpr int kFa = 16, kFb = 2 * WB;                // fragments per stage
     constexpr int kStage = (kFa + kFb) * 1024;
-    constexpr int kL = (kFa + kFb) / 4;                   // DMAs per wave per stage
-    static_assert((kFa + kFb) % 4 == 0, "fragments must split evenly over the waves");
-    static_assert(kL * (NS - 1) <= 63 && NS <= 6, "vmcnt range");
+    constexpr int ka = 4, kb = kFb / 4;                  // loads / DMAs per wave per stage
+    constexpr int kOps = ka + kb;                        // vector-memory ops per wave per stage
+    static_assert(3 * kOps <= 63, "vmcnt range");
     __shared__ __attribute__((aligned(16))) int8_t ring[NS * kStage];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;   // four waves
     const int tm = local % P.tiles_m, tn = local / P.tiles_m;
-    const int n0 = tn * 32 * kTlWN, t0 = tm * 32 * WM;
+    const int n0 = tn * 256, t0 = tm * 64 * WJ;
     const int nkb = P.K >> 6;
-    const int koff = (lane >> 4) << 4;
-
-    // this wave copies fragments wave, wave + 4, ...: weight rows, then tokens
-    // (rows and tokens past the end repeat the last one; their results are
-    // never stored)
-    const int8_t* src[kL];
+    // fragment f: rows (or tokens) 16 f .. + 15 of the k-block, lane l's 16
+    // bytes (row l % 16, bytes 16 (l / 16) .. + 15) at 16 l: each copy reads 16
+    // rows x 64 contiguous bytes.  Rows and tokens past the end repeat the last
+    // one; their results are never stored.
+    const int lrow = lane & 31;
+    const int kof = 16 * (lane >> 4);
+    const int8_t* asrc[ka];
 #pragma unroll
-    for (int u = 0; u < kL; ++u) {
-        const int f = wave + 4 * u;
-        if (f < kFa) {
-            const int n = min(n0 + 16 * f + (lane & 15), P.N - 1);
-            src[u] = P.W + (int64_t)n * P.K + koff;
-        } else {
-            const int t = min(t0 + 16 * (f - kFa) + (lane & 15), P.M - 1);
-            src[u] = P.X + (int64_t)t * P.ldx + koff;
-        }
+    for (int h = 0; h < ka; ++h) {
+        const int f = wave + 4 * h;
+        asrc[h] = P.W + (int64_t)min(n0 + 16 * f + (lane & 15), P.N - 1) * P.K + kof;
     }
-    auto issue = [&](int g) {                             // stage g -> slot g % NS
-        if (g >= nkb) return;
-        int8_t* slot = ring + (g % NS) * kStage;
+    const int8_t* bsrc[kb];
 #pragma unroll
-        for (int u = 0; u < kL; ++u) dma16(src[u] + (int64_t)g * 64, slot + (wave + 4 * u) * 1024);
+    for (int h = 0; h < kb; ++h) {
+        const int f = wave + 4 * h;
+        bsrc[h] = P.X + (int64_t)min(t0 + 16 * f + (lane & 15), P.M - 1) * P.ldx + kof;
+    }
+    const uint32_t ring0 = lds_addr(ring);
+    const uint32_t awr = ring0 + wave * 1024 + lane * 16;
+
+    auto kbo = [&](int s) { return (int64_t)min(s, nkb - 1) * 64; };
+    auto load_a = [&](int s, v4i (&r)[ka]) {
+#pragma unroll
+        for (int h = 0; h < ka; ++h) r[h] = ld16(asrc[h] + kbo(s));
+    };
+    auto put = [&](int s, const v4i (&r)[ka]) {         // stage s: weights from r, tokens by DMA
+        lds_write4(awr + (uint32_t)((s % NS) * kStage), r[0], r[1], r[2], r[3]);
+        int8_t* slot = ring + (s % NS) * kStage;
+#pragma unroll
+        for (int h = 0; h < kb; ++h) dma16(bsrc[h] + kbo(s), slot + (kFa + wave + 4 * h) * 1024);
     };
 
+    // The 32 x 32 x 32 operand of rows 32 i .. + 31, k half kh: lane l needs
+    // row l % 32, bytes 32 kh + 16 (l / 32) .. + 15, which sit in fragment
+    // 2 i + (l / 16) % 2 at 16 (l % 16 + 16 (2 kh + l / 32)).  Per 16-lane group
+    // the 16-byte reads are consecutive: no bank conflicts.
+    const uint32_t lofs = (uint32_t)(((lane >> 4) & 1) * 1024 + 16 * (lane & 15) + 256 * (lane >> 5));
     const int wn = wave >> 1, wm = wave & 1;
-    const uint32_t ra = lds_addr(ring) + wn * kTlWN * 1024 + lane * 16;
-    const uint32_t rb = lds_addr(ring) + (kFa + wm * WM) * 1024 + lane * 16;
+    const uint32_t ra = ring0 + wn * 8 * 1024 + lofs;
+    const uint32_t rb = ring0 + (kFa + wm * WB) * 1024 + lofs;
 
-    v4i acc[kTlWN][WM];
+    v16i acc[4][WJ];
 #pragma unroll
-    for (int i = 0; i < kTlWN; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < WM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+        for (int j = 0; j < WJ; ++j) acc[i][j] = v16i{};
 
+    // stages 0 .. 3 in the ring; weights of stages 4 .. 6 in the three register
+    // sets, issued in the loop's order (tokens of stage s, then weights of
+    // stage s + 3), one stage per fenced group
+    v4i rs[3][ka];
+    {
+        v4i first[NS][ka];                               // all loads in flight at once
 #pragma unroll
-    for (int g = 0; g < NS; ++g) issue(g);
-    wait_stages<kL>(min(nkb, NS) - 1);                   // own copies of stage 0
+        for (int s = 0; s < NS; ++s) load_a(s, first[s]);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            lds_write4(awr + (uint32_t)(s * kStage), first[s][0], first[s][1], first[s][2], first[s][3]);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        int8_t* slot = ring + s * kStage;
+#pragma unroll
+        for (int h = 0; h < kb; ++h) dma16(bsrc[h] + kbo(s), slot + (kFa + wave + 4 * h) * 1024);
+        if (s > 0) load_a(s + NS - 1, rs[s - 1]);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+    wait_vmcnt<3 * kOps>();                              // own copies of stage 0
     stage_barrier();
-    TlFrags<WM> f0, f1;
-    tl_issue<WM>(f0, ra, rb);
+    TlFrags<WB> fr[2];
+    tl_issue<WB>(fr[0], ra, rb);
 
-    // stage g: its fragments are in `cur`; stage g + 1 goes to `nxt`
-    auto step = [&](int g, TlFrags<WM>& cur, TlFrags<WM>& nxt) {
-        tl_wait<WM>(cur);
+    // tail: a step after the unrolled loop, whose weight loads may feed nothing
+    // and be dropped by the compiler, so its wait cannot count on them
+    auto step = [&](int g, v4i (&r)[ka], TlFrags<WB>& cur, TlFrags<WB>& nxt, bool tail) {
+        tl_wait<WB>(cur);
         if (g + 1 < nkb) {
-            wait_stages<kL>(min(nkb - g - 2, NS - 2));   // own copies of stage g + 1
-            stage_barrier();                             // ... and every wave's; stage g read by all
-            issue(g + NS);                               // refills stage g's slot
+            if (tail) wait_vmcnt<0>();
+            else wait_vmcnt<2 * kOps>();                 // own copies of stage g + 1, weights of g + 4
+            stage_barrier();                             // stage g + 1 published; stage g read by all
+            put(g + NS, r);                              // into the slot of stage g
+            load_a(g + NS + 3, r);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);     // this stage's copies stay in it
             const uint32_t so = (uint32_t)(((g + 1) % NS) * kStage);
-            tl_issue<WM>(nxt, ra + so, rb + so);
+            tl_issue<WB>(nxt, ra + so, rb + so);
         }
-        __builtin_amdgcn_sched_barrier(0);               // reads go out before the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < kTlWN; ++i)
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int j = 0; j < WM; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0);
-        // keep the next stage's waits behind these MFMAs (they overlap its reads)
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < WJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[2 * i + kh], cur.b[2 * j + kh],
+                                                                     acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     int g = 0;
-    for (; g + 1 < nkb; g += 2) {                        // the same registers every pass
-        step(g, f0, f1);
-        step(g + 1, f1, f0);
+    for (; g + 5 < nkb; g += 6) {                        // the same registers every pass
+        step(g, rs[0], fr[0], fr[1], false);
+        step(g + 1, rs[1], fr[1], fr[0], false);
+        step(g + 2, rs[2], fr[0], fr[1], false);
+        step(g + 3, rs[0], fr[1], fr[0], false);
+        step(g + 4, rs[1], fr[0], fr[1], false);
+        step(g + 5, rs[2], fr[1], fr[0], false);
     }
-    if (g < nkb) step(g, f0, f1);
+    if (g < nkb) step(g, rs[0], fr[0], fr[1], true);
+    if (g + 1 < nkb) step(g + 1, rs[1], fr[1], fr[0], true);
+    if (g + 2 < nkb) step(g + 2, rs[2], fr[0], fr[1], true);
+    if (g + 3 < nkb) step(g + 3, rs[0], fr[1], fr[0], true);
+    if (g + 4 < nkb) step(g + 4, rs[1], fr[0], fr[1], true);
+    wait_vmcnt<0>();                                     // no copy outlives the workgroup's LDS
+    stage_barrier();                                     // every wave is done with the ring
 
-    // Lane l of a 16 x 16 block holds rows 4 (l / 16) .. + 3 of token l % 16.
+    // The tile's 256 weight scales and 64 WJ token scales, staged once through
+    // LDS (one load each per thread, all in flight together).
+    float* const sws = reinterpret_cast<float*>(ring);
+    float* const sxs = sws + 256;
+    {
+        const int t = (int)threadIdx.x;
+        const float wv = P.ws[min(n0 + t, P.N - 1)];
+        const float xv = t < 64 * WJ ? P.xs[min(t0 + t, P.M - 1)] : 0.0f;
+        sws[t] = wv;
+        if (t < 64 * WJ) sxs[t] = xv;
+    }
+    __syncthreads();
+
+    // Lane l, register 4 q + r of a 32 x 32 block: token l % 32, row
+    // 8 q + 4 (l / 32) + r.
     const bool vec = (((uintptr_t)P.Y & 15) == 0) && ((P.ldy & 3) == 0) &&
                      (!P.Y2 || ((((uintptr_t)P.Y2 & 15) == 0) && ((P.ldy2 & 3) == 0)));
-    float xs[WM];
+    float xs[WJ];
 #pragma unroll
-    for (int j = 0; j < WM; ++j) xs[j] = P.xs[min(t0 + wm * 16 * WM + 16 * j + (lane & 15), P.M - 1)];
+    for (int j = 0; j < WJ; ++j) xs[j] = sxs[wm * 32 * WJ + 32 * j + lrow];
 #pragma unroll
-    for (int i = 0; i < kTlWN; ++i) {
-        const int n = n0 + wn * 16 * kTlWN + 16 * i + ((lane >> 4) << 2);
-        if (n >= P.N) continue;
-        float w[4];
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = P.ws[min(n + r, P.N - 1)];
+        for (int q = 0; q < 4; ++q) {
+            const int nl = wn * 128 + 32 * i + 8 * q + ((lane >> 5) << 2);   // row in the tile
+            const int n = n0 + nl;
+            if (n >= P.N) continue;
+            const float4 w4 = *reinterpret_cast<const float4*>(sws + nl);
+            const float w[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-        for (int j = 0; j < WM; ++j) {
-            const int t = t0 + wm * 16 * WM + 16 * j + (lane & 15);
-            if (t >= P.M) continue;
-            float4 v;
-            v.x = epilogue(acc[i][j][0], w[0], xs[j]);
-            v.y = epilogue(acc[i][j][1], w[1], xs[j]);
-            v.z = epilogue(acc[i][j][2], w[2], xs[j]);
-            v.w = epilogue(acc[i][j][3], w[3], xs[j]);
-            float* y = P.Y + (int64_t)t * P.ldy + n;
-            float* y2 = P.Y2 ? P.Y2 + (int64_t)t * P.ldy2 + n : nullptr;
-            if (vec && n + 3 < P.N) {
-                *reinterpret_cast<float4*>(y) = v;
-                if (y2) *reinterpret_cast<float4*>(y2) = v;
-            } else {
-                const float e[4] = {v.x, v.y, v.z, v.w};
+            for (int j = 0; j < WJ; ++j) {
+                const int t = t0 + wm * 32 * WJ + 32 * j + lrow;
+                if (t >= P.M) continue;
+                float4 v;
+                v.x = epilogue(acc[i][j][4 * q + 0], w[0], xs[j]);
+                v.y = epilogue(acc[i][j][4 * q + 1], w[1], xs[j]);
+                v.z = epilogue(acc[i][j][4 * q + 2], w[2], xs[j]);
+                v.w = epilogue(acc[i][j][4 * q + 3], w[3], xs[j]);
+                float* y = P.Y + (int64_t)t * P.ldy + n;
+                float* y2 = P.Y2 ? P.Y2 + (int64_t)t * P.ldy2 + n : nullptr;
+                if (vec && n + 3 < P.N) {
+                    *reinterpret_cast<float4*>(y) = v;
+                    if (y2) *reinterpret_cast<float4*>(y2) = v;
+                } else {
+                    const float e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (n + r < P.N) {
-                        y[r] = e[r];
-                        if (y2) y2[r] = e[r];
-                    }
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < P.N) {
+                            y[r] = e[r];
+                            if (y2) y2[r] = e[r];
+                        }
+                }
             }
         }
     }
@@ -257,17 +345,17 @@ __device__ __forceinline__ int xcd_tile(int per_xcd)
     return ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
 }
 
-template <int WM, int NS>
+template <int WJ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_tiled(GemmSet set, int per_xcd)
 {
     const int j = xcd_tile(per_xcd);
     if (j >= set.total_tiles) return;
     const GemmProb P = find_prob(set, j);
-    tiled_block<WM, NS>(P, j - P.tile_begin);
+    tiled_block<WJ>(P, j - P.tile_begin);
 }
 
-template <int WM, int NS>
+template <int WJ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_tiled_step(StackStep S, int per_xcd)
 {
@@ -275,18 +363,18 @@ void k_gemm_tiled_step(StackStep S, int per_xcd)
     if (j >= S.npairs * S.tile_off[S.nproj]) return;
     int local;
     const GemmProb P = step_prob(S, j, local);
-    tiled_block<WM, NS>(P, local);
+    tiled_block<WJ>(P, local);
 }
 
-int tiled_tokens(int64_t M) { return M > 128 ? 32 * 8 : 32 * 4; }
+int tiled_tokens(int64_t M) { return M > 128 ? 256 : 128; }
 
 hipError_t launch_gemm_tiled(const GemmSet& set, int64_t M, hipStream_t s)
 {
     if (set.total_tiles <= 0) return hipSuccess;
     const int per_xcd = (set.total_tiles + 7) / 8;
     const dim3 g(8 * per_xcd), b(256);
-    if (tiled_tokens(M) == 256) PF_LAUNCH((k_gemm_tiled<8, 4>), g, b, 0, s, set, per_xcd);
-    else PF_LAUNCH((k_gemm_tiled<4, 6>), g, b, 0, s, set, per_xcd);
+    if (tiled_tokens(M) == 256) PF_LAUNCH((k_gemm_tiled<4>), g, b, 0, s, set, per_xcd);
+    else PF_LAUNCH((k_gemm_tiled<2>), g, b, 0, s, set, per_xcd);
     return hipGetLastError();
 }
 
@@ -296,8 +384,8 @@ hipError_t launch_gemm_tiled_step(const StackStep& S, int64_t M, hipStream_t s)
     if (tiles <= 0) return hipSuccess;
     const int per_xcd = (tiles + 7) / 8;
     const dim3 g(8 * per_xcd), b(256);
-    if (tiled_tokens(M) == 256) PF_LAUNCH((k_gemm_tiled_step<8, 4>), g, b, 0, s, S, per_xcd);
-    else PF_LAUNCH((k_gemm_tiled_step<4, 6>), g, b, 0, s, S, per_xcd);
+    if (tiled_tokens(M) == 256) PF_LAUNCH((k_gemm_tiled_step<4>), g, b, 0, s, S, per_xcd);
+    else PF_LAUNCH((k_gemm_tiled_step<2>), g, b, 0, s, S, per_xcd);
     return hipGetLastError();
 }
 
