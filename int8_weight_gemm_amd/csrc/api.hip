@@ -114,20 +114,62 @@ void make_skinny(GemmProb& g, const int8_t* W, const float* ws, int64_t N, int64
     g.splits = p.splits; g.kb_per_split = p.kb_per_split;
     if (p.splits > 1) {
         g.acc = reinterpret_cast<int*>(scratch);
+        g.acc_ld = N;
+        g.acc_split = M * N;
         scratch += split_bytes(N, m_alloc, p);
     }
 }
 
+// Tiled product plan: the K range may also be split across workgroups (each
+// split at least 8 k-blocks), the splits' int32 partials summed by
+// k_split_reduce.  The split count minimises a cost estimate: rounds of work
+// units over the compute units x (k-blocks per split + the ~6 stages a unit
+// spends filling and draining its pipeline) x ~1.3 us per stage, plus the
+// partials' write and read at ~4 TB/s and one more launch.
+SkinnyPlan plan_tiled(int64_t N, int64_t K, int64_t M)
+{
+    SkinnyPlan p;
+    p.tiles_n = (int)((N + kTiledRows - 1) / kTiledRows);
+    const int64_t tiles = p.tiles_n * ((M + tiled_tokens(M) - 1) / tiled_tokens(M));
+    const int nkb = (int)(K / 64);
+    auto cost = [&](int s) {
+        const int64_t rounds = (tiles * s + kComputeUnits - 1) / kComputeUnits;
+        double us = (double)rounds * ((nkb + s - 1) / s + 6) * 1.3;
+        if (s > 1) us += 2.0 * s * (double)M * (double)N * 4 / 4.0e6 + 3.0;
+        return us;
+    };
+    int best = 1;
+    for (int s = 2; nkb / s >= 8 && s <= 16; s *= 2)
+        if (cost(s) < cost(best)) best = s;
+    p.kb_per_split = (nkb + best - 1) / best;
+    p.splits = (nkb + p.kb_per_split - 1) / p.kb_per_split;
+    return p;
+}
+
+SkinnyPlan unsplit_tiled(int64_t N, int64_t K)
+{
+    return SkinnyPlan{(int)((N + kTiledRows - 1) / kTiledRows), 1, (int)(K / 64)};
+}
+
+// Fills a tiled problem; with a split plan its partials ([splits][M][N]) are
+// carved from `scratch`, which then advances.
 void make_tiled(GemmProb& g, const int8_t* W, const float* ws, int64_t N, int64_t K,
-                const int8_t* X, int64_t ldx, const float* xs, int64_t M, float* Y, int64_t ldy)
+                const int8_t* X, int64_t ldx, const float* xs, int64_t M, float* Y, int64_t ldy,
+                const SkinnyPlan& p, char*& scratch)
 {
     std::memset(&g, 0, sizeof(g));
     g.W = W; g.ws = ws; g.X = X; g.xs = xs; g.Y = Y;
     g.ldx = ldx; g.ldy = ldy;
     g.N = (int)N; g.K = (int)K; g.M = (int)M;
-    g.tiles_n = (int)((N + kTiledRows - 1) / kTiledRows);
+    g.tiles_n = p.tiles_n;
     g.tiles_m = (int)((M + tiled_tokens(M) - 1) / tiled_tokens(M));
-    g.splits = 1; g.kb_per_split = (int)(K / 64);
+    g.splits = p.splits; g.kb_per_split = p.kb_per_split;
+    if (p.splits > 1) {
+        g.acc = reinterpret_cast<int*>(scratch);
+        g.acc_ld = N;
+        g.acc_split = M * N;
+        scratch += split_bytes(N, M, p);
+    }
 }
 
 void finish_set(GemmSet& set, int kind)  // kind 0 gemv, 1 skinny, 2 tiled
@@ -138,7 +180,7 @@ void finish_set(GemmSet& set, int kind)  // kind 0 gemv, 1 skinny, 2 tiled
         g.tile_begin = begin;
         if (kind == 0) begin += (g.N + 15) / 16;
         else if (kind == 1) begin += g.tiles_n * g.splits;
-        else begin += g.tiles_n * g.tiles_m;
+        else begin += g.tiles_n * g.tiles_m * g.splits;
     }
     set.total_tiles = begin;
 }
@@ -163,15 +205,11 @@ struct StackLayout {
     int groups;           // chunk groups (one stream each)
     int gslots;           // slots per group: chunks of a group in flight at once
     int slots;
-    int dsplits;          // K splits of the down product (skinny path)
+    int dsplits;          // K splits of the down product
+    int dkb;              // k-blocks per down-product split
     size_t a, b, sa, sb, proj, part, slot_bytes, total;
 };
 
-// Down-product K splits on the skinny path: at most 16 k-blocks (1 KB of K) each.
-int down_splits(int64_t F, int64_t chunk)
-{
-    return chunk <= 64 ? (int)((F / 64 + 15) / 16) : 1;
-}
 
 constexpr int kMaxGroups = 4;        // library streams per device
 
@@ -182,22 +220,30 @@ constexpr int kMaxGroups = 4;        // library streams per device
 // are at most kMaxPairs.
 constexpr int kStackGroups = 3;
 constexpr int kGroupSlots = 16;
+constexpr int kGroupSlotsTiled = 4;  // chunks over 64 tokens: each product fills the chip
 static_assert(kStackGroups <= kMaxGroups && kGroupSlots <= kMaxPairs, "stack sweep shape");
 
 StackLayout stack_layout(int64_t L, int64_t H, int64_t F, int64_t chunk)
 {
     StackLayout S{};
     S.groups = kStackGroups;
-    S.gslots = (int)std::min<int64_t>(L, kGroupSlots);
+    S.gslots = (int)std::min<int64_t>(L, chunk <= 64 ? kGroupSlots : kGroupSlotsTiled);
     S.slots = S.groups * S.gslots;
-    S.dsplits = down_splits(F, chunk);
+    // down-product K splits: on the skinny path at most 16 k-blocks (the
+    // token slice in LDS) each.  The tiled path does not split: at hundreds
+    // of tokens the partials' traffic costs more than the idle compute units
+    // it would fill, which the other chunk groups' launches fill anyway.
+    const int nkb = (int)(F / 64);
+    const int want = chunk <= 64 ? (nkb + 15) / 16 : 1;
+    S.dkb = (nkb + want - 1) / want;
+    S.dsplits = (nkb + S.dkb - 1) / S.dkb;
     size_t o = 0;
     S.a = o; o += round_up((size_t)chunk * H, kAlign);
     S.b = o; o += round_up((size_t)chunk * F, kAlign);
     S.sa = o; o += round_up((size_t)chunk * 4, kAlign);
     S.sb = o; o += round_up((size_t)chunk * 4, kAlign);
     S.proj = o; o += round_up((size_t)chunk * (5 * H + 2 * F) * 4, kAlign);
-    S.part = o; o += chunk <= 64 ? round_up((size_t)S.dsplits * chunk * H * 4, kAlign) : 0;
+    S.part = o; o += (chunk <= 64 || S.dsplits > 1) ? round_up((size_t)S.dsplits * chunk * H * 4, kAlign) : 0;
     S.slot_bytes = o;
     S.total = o * S.slots;
     return S;
@@ -491,6 +537,9 @@ struct StackRun {
         // token-resident kernel for the six K = H products when a split of H fits
         const bool xres_a = skinny && H() / 64 <= 16;
         const int sd = lay.dsplits;
+        // the down product leaves int32 split partials that the next
+        // quantisation launch sums (always on the skinny path)
+        const bool rebuild_d = skinny || sd > 1;
         const int64_t rowsA[6] = {H(), H(), H(), H(), F(), F()};
         const int tm = (int)((ch + tiled_tokens(ch) - 1) / tiled_tokens(ch));
         const int tb = (int)((ch + 15) / 16);
@@ -512,9 +561,9 @@ struct StackRun {
         A.kb_per_split = (int)(H() / 64);
         D.nproj = 1;
         D.K = (int)F();
-        D.splits = skinny ? sd : 1;
-        D.partials = skinny ? 1 : 0;
-        D.kb_per_split = (int)((F() / 64 + D.splits - 1) / D.splits);
+        D.splits = sd;
+        D.partials = rebuild_d ? 1 : 0;
+        D.kb_per_split = lay.dkb;
         A.tiles_m = D.tiles_m = tm;
         A.ldx = H();
         D.ldx = F();
@@ -560,7 +609,7 @@ struct StackRun {
             if (l == 0) {
                 q0.src = x + c0 * H();
                 q0.ld = H();
-            } else if (skinny) {
+            } else if (rebuild_d) {
                 rebuild(q0, c, l - 1, false);
                 qa_bytes += (double)M * H() * 4 * sd + (double)M * H() * 4;
             } else {
@@ -594,7 +643,7 @@ struct StackRun {
             pd.X = b;
             pd.xs = sb;
             pd.Y = out;
-            pd.Y2 = (!skinny && l == L - 1) ? y + c0 * H() : nullptr;
+            pd.Y2 = (!rebuild_d && l == L - 1) ? y + c0 * H() : nullptr;
             pd.part = reinterpret_cast<int*>(sl + lay.part);
             pd.M = (int)M;
             d_bytes += product_bytes(H(), F(), M);
@@ -627,7 +676,7 @@ struct StackRun {
             return launched(skinny ? launch_gemm_xres(D, tb, sg) : launch_gemm_tiled_step(D, ch, sg));
         }, sg);
         if (r) return r;
-        if (skinny)
+        if (rebuild_d)
             for (int64_t c : cs)
                 if (step - start(c / ng) == L - 1) fin = c;
         return PF_OK;
@@ -750,7 +799,8 @@ pf_status pf_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int
 
 size_t pf_gemm_i8_chunk_workspace(int64_t N, int64_t K, int64_t M)
 {
-    if (N <= 0 || !valid_k(K) || M <= 0 || M > 64) return 0;
+    if (N <= 0 || N > INT32_MAX || !valid_k(K) || M <= 0 || M > INT32_MAX) return 0;
+    if (M > 64) return split_bytes(N, M, plan_tiled(N, K, M));
     const SkinnyPlan p = plan_skinny(N, K, (N + kSkinnyRows - 1) / kSkinnyRows);
     return split_bytes(N, M, p);
 }
@@ -782,7 +832,11 @@ pf_status pf_gemm_i8_chunk(const int8_t* W, const float* w_scale, int64_t N, int
             char* scratch = static_cast<char*>(workspace);
             make_skinny(set.p[0], W, w_scale, N, K, xq, K, a_scale, M, y, N, p, scratch, M);
         } else {
-            make_tiled(set.p[0], W, w_scale, N, K, xq, K, a_scale, M, y, N);
+            SkinnyPlan p = plan_tiled(N, K, M);
+            if (!workspace || ws_bytes < split_bytes(N, M, p)) p = unsplit_tiled(N, K);
+            if (workspace && overlap(workspace, ws_bytes, y, yb)) return PF_EINVAL;
+            char* scratch = static_cast<char*>(workspace);
+            make_tiled(set.p[0], W, w_scale, N, K, xq, K, a_scale, M, y, N, p, scratch);
         }
         return run_products(set, M, (hipStream_t)stream);
     } catch (...) {

@@ -299,7 +299,7 @@ __device__ __forceinline__ void skinny_tile(const GemmProb& P, int local)
             for (int r = 0; r < 4; ++r)
                 if (nr + r < P.N) store_out(P, t, nr + r, epilogue(acc[tb][r], P.ws[nr + r], xs));
         } else {
-            int* part = P.acc + ((int64_t)split * P.M + t) * P.N;
+            int* part = P.acc + (int64_t)split * P.acc_split + (int64_t)t * P.acc_ld;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (nr + r < P.N) part[nr + r] = acc[tb][r];
@@ -322,17 +322,35 @@ __global__ __launch_bounds__(256) void k_gemm_skinny_step(StackStep S)
     skinny_tile<TB, KP>(P, local);
 }
 
-// Sum of the split partials [splits][M][N] and the epilogue; one thread per
-// output.  Here tile_begin counts blocks of 256 outputs.
+// Sum of the split partials and the epilogue; one thread per output.  Here
+// tile_begin counts blocks of 256 outputs.
 __global__ __launch_bounds__(256) void k_split_reduce(GemmSet set)
 {
     const GemmProb P = find_prob(set, blockIdx.x);
     const int64_t idx = (int64_t)(blockIdx.x - P.tile_begin) * 256 + threadIdx.x;
     if (idx >= (int64_t)P.M * P.N) return;
     const int t = (int)(idx / P.N), n = (int)(idx - (int64_t)t * P.N);
+    const int* a = P.acc + (int64_t)t * P.acc_ld + n;
     int v = 0;
-    for (int sp = 0; sp < P.splits; ++sp) v += P.acc[((int64_t)sp * P.M + t) * P.N + n];
+    for (int sp = 0; sp < P.splits; ++sp) v += a[(int64_t)sp * P.acc_split];
     store_out(P, t, n, epilogue(v, P.ws[n], P.xs[t]));
+}
+
+hipError_t launch_split_reduce(const GemmSet& set, hipStream_t s)
+{
+    // reduce launch over the split problems only; problems without splits get
+    // no blocks (find_prob never selects them: their tile_begin equals the
+    // next problem's)
+    GemmSet r = set;
+    int begin = 0;
+    for (int i = 0; i < r.nprob; ++i) {
+        r.p[i].tile_begin = begin;
+        if (r.p[i].splits > 1) begin += (int)(((int64_t)r.p[i].M * r.p[i].N + 255) / 256);
+    }
+    if (begin == 0) return hipSuccess;
+    r.total_tiles = begin;
+    PF_LAUNCH(k_split_reduce, dim3(begin), dim3(256), 0, s, r);
+    return hipGetLastError();
 }
 
 // Token pieces of 8 k-blocks (512 bytes): with the weight double buffer that is
@@ -356,19 +374,7 @@ hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t 
     PF_SKINNY_CASES(k_gemm_skinny, set)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // reduce launch over the split problems only
-    GemmSet r = set;
-    int begin = 0;
-    for (int i = 0; i < r.nprob; ++i) {
-        r.p[i].tile_begin = begin;
-        if (r.p[i].splits > 1) begin += (int)(((int64_t)r.p[i].M * r.p[i].N + 255) / 256);
-    }
-    if (begin == 0) return hipSuccess;
-    // problems without splits get no blocks: find_prob never selects them
-    // because their tile_begin equals the next problem's.
-    r.total_tiles = begin;
-    PF_LAUNCH(k_split_reduce, dim3(begin), b, 0, s, r);
-    return hipGetLastError();
+    return launch_split_reduce(set, s);
 }
 
 hipError_t launch_gemm_skinny_step(const StackStep& S, int token_blocks, hipStream_t s)

@@ -36,7 +36,10 @@ struct GemmProb {
     const float* xs;      // [M]
     float* Y;             // [M][ldy]
     float* Y2;            // optional second copy of the output [M][ldy2] (or null)
-    int* acc;             // split-K int32 partials [splits][M][N] (or null)
+    int* acc;             // split-K int32 partials (or null): split s, token t, row n at
+                          // acc[s * acc_split + t * acc_ld + n]
+    int64_t acc_ld;       // ints between token rows of a split's partials
+    int64_t acc_split;    // ints between splits
     int64_t ldx;          // bytes between token rows of X
     int64_t ldy;          // floats between token rows of Y
     int64_t ldy2;         // floats between token rows of Y2
@@ -144,6 +147,7 @@ hipError_t launch_gemm_stream(const StackStep& S, int token_blocks, hipStream_t 
 hipError_t launch_gemm_xres(const StackStep& S, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_tiled(const GemmSet& set, int64_t M, hipStream_t s);
+hipError_t launch_split_reduce(const GemmSet& set, hipStream_t s);
 // Tiled product tiles: 256 weight rows x tiled_tokens(M) tokens.
 constexpr int kTiledRows = 256;
 int tiled_tokens(int64_t M);

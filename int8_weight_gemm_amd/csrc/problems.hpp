@@ -37,6 +37,8 @@ __device__ __forceinline__ GemmProb step_prob(const StackStep& S, int bid, int& 
     P.Y = pp.Y + S.yoff[j];
     P.Y2 = pp.Y2;
     P.acc = nullptr;
+    P.acc_ld = 0;
+    P.acc_split = 0;
     P.ldx = S.ldx;
     P.ldy = S.ldy;
     P.ldy2 = S.ldy2;

@@ -150,7 +150,7 @@ __device__ __forceinline__ void lds_write4(uint32_t a, v4i d0, v4i d1, v4i d2, v
 // to the last one and land in free slots, never read), so every wait is a
 // constant.
 template <int WJ>
-__device__ __forceinline__ void tiled_block(const GemmProb& P, int local)
+__device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int split)
 {
     constexpr int NS = 4;
     constexpr int WB = 2 * WJ;                           // token fragments per wave
@@ -164,7 +164,9 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;   // four waves
     const int tm = local % P.tiles_m, tn = local / P.tiles_m;
     const int n0 = tn * 256, t0 = tm * 64 * WJ;
-    const int nkb = P.K >> 6;
+    // this split's k-blocks: kb0 .. kb0 + nkb - 1 (all of K when unsplit)
+    const int kb0 = split * P.kb_per_split;
+    const int nkb = min(P.kb_per_split, (P.K >> 6) - kb0);
     // fragment f: rows (or tokens) 16 f .. + 15 of the k-block, lane l's 16
     // bytes (row l % 16, bytes 16 (l / 16) .. + 15) at 16 l: each copy reads 16
     // rows x 64 contiguous bytes.  Rows and tokens past the end repeat the last
@@ -186,7 +188,7 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local)
     const uint32_t ring0 = lds_addr(ring);
     const uint32_t awr = ring0 + wave * 1024 + lane * 16;
 
-    auto kbo = [&](int s) { return (int64_t)min(s, nkb - 1) * 64; };
+    auto kbo = [&](int s) { return (int64_t)(kb0 + min(s, nkb - 1)) * 64; };
     auto load_a = [&](int s, v4i (&r)[ka]) {
 #pragma unroll
         for (int h = 0; h < ka; ++h) r[h] = ld16(asrc[h] + kbo(s));
@@ -278,6 +280,35 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local)
     if (g + 3 < nkb) step(g + 3, rs[0], fr[1], fr[0], true);
     if (g + 4 < nkb) step(g + 4, rs[1], fr[0], fr[1], true);
     wait_vmcnt<0>();                                     // no copy outlives the workgroup's LDS
+
+    // Lane l, register 4 q + r of a 32 x 32 block: token l % 32, row
+    // 8 q + 4 (l / 32) + r.
+    if (P.splits > 1) {                                  // int32 partials of this split
+        int* const part = P.acc + (int64_t)split * P.acc_split;
+        const bool v4 = ((P.acc_ld & 3) == 0) && ((P.acc_split & 3) == 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * 128 + 32 * i + 8 * q + ((lane >> 5) << 2);
+                if (n >= P.N) continue;
+#pragma unroll
+                for (int j = 0; j < WJ; ++j) {
+                    const int t = t0 + wm * 32 * WJ + 32 * j + lrow;
+                    if (t >= P.M) continue;
+                    int* p = part + (int64_t)t * P.acc_ld + n;
+                    const v4i v = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    if (v4 && n + 3 < P.N) {
+                        *reinterpret_cast<v4i*>(p) = v;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (n + r < P.N) p[r] = v[r];
+                    }
+                }
+            }
+        return;
+    }
     stage_barrier();                                     // every wave is done with the ring
 
     // The tile's 256 weight scales and 64 WJ token scales, staged once through
@@ -293,8 +324,6 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local)
     }
     __syncthreads();
 
-    // Lane l, register 4 q + r of a 32 x 32 block: token l % 32, row
-    // 8 q + 4 (l / 32) + r.
     const bool vec = (((uintptr_t)P.Y & 15) == 0) && ((P.ldy & 3) == 0) &&
                      (!P.Y2 || ((((uintptr_t)P.Y2 & 15) == 0) && ((P.ldy2 & 3) == 0)));
     float xs[WJ];
@@ -345,6 +374,7 @@ __device__ __forceinline__ int xcd_tile(int per_xcd)
     return ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
 }
 
+// A work unit is (tile, K split), splits fastest.
 template <int WJ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_tiled(GemmSet set, int per_xcd)
@@ -352,18 +382,28 @@ void k_gemm_tiled(GemmSet set, int per_xcd)
     const int j = xcd_tile(per_xcd);
     if (j >= set.total_tiles) return;
     const GemmProb P = find_prob(set, j);
-    tiled_block<WJ>(P, j - P.tile_begin);
+    const int u = j - P.tile_begin;
+    tiled_block<WJ>(P, u / P.splits, u % P.splits);
 }
 
+// Stack step: with S.partials the K range is split S.splits ways and each unit
+// writes its int32 partial tile to the pair's partial buffer.
 template <int WJ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_tiled_step(StackStep S, int per_xcd)
 {
     const int j = xcd_tile(per_xcd);
-    if (j >= S.npairs * S.tile_off[S.nproj]) return;
+    if (j >= S.npairs * S.tile_off[S.nproj] * S.splits) return;
     int local;
-    const GemmProb P = step_prob(S, j, local);
-    tiled_block<WJ>(P, local);
+    GemmProb P = step_prob(S, j / S.splits, local);
+    P.splits = S.splits;
+    P.kb_per_split = S.kb_per_split;
+    if (S.partials) {
+        P.acc = S.pair[(j / S.splits) / S.tile_off[S.nproj]].part;
+        P.acc_ld = S.ldp;
+        P.acc_split = S.part_stride;
+    }
+    tiled_block<WJ>(P, local, j % S.splits);
 }
 
 int tiled_tokens(int64_t M) { return M > 128 ? 256 : 128; }
@@ -375,12 +415,15 @@ hipError_t launch_gemm_tiled(const GemmSet& set, int64_t M, hipStream_t s)
     const dim3 g(8 * per_xcd), b(256);
     if (tiled_tokens(M) == 256) PF_LAUNCH((k_gemm_tiled<4>), g, b, 0, s, set, per_xcd);
     else PF_LAUNCH((k_gemm_tiled<2>), g, b, 0, s, set, per_xcd);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_split_reduce(set, s);
 }
 
 hipError_t launch_gemm_tiled_step(const StackStep& S, int64_t M, hipStream_t s)
 {
-    const int tiles = S.npairs * S.tile_off[S.nproj];
+    if (S.splits < 1 || (S.splits > 1 && !S.partials)) return hipErrorInvalidValue;
+    const int tiles = S.npairs * S.tile_off[S.nproj] * S.splits;
     if (tiles <= 0) return hipSuccess;
     const int per_xcd = (tiles + 7) / 8;
     const dim3 g(8 * per_xcd), b(256);

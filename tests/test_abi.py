@@ -79,7 +79,8 @@ def test_workspace_queries():
     lib = pf.lib()
     assert lib.pf_gemm_i8_chunk_workspace(1024, 4096, 32) > 0      # 16 row tiles: K split
     assert lib.pf_gemm_i8_chunk_workspace(16384, 4096, 32) == 0    # 256 row tiles fill the chip
-    assert lib.pf_gemm_i8_chunk_workspace(4096, 4096, 128) == 0     # tiled path: no split
+    assert lib.pf_gemm_i8_chunk_workspace(4096, 4096, 128) > 0      # 16 tiles: K split
+    assert lib.pf_gemm_i8_chunk_workspace(65536, 4096, 512) == 0    # 512 tiles fill the chip
     assert lib.pf_gemm_i8_chunk_workspace(4096, 100, 32) == 0
     layers = (pf._Layer * 2)()
     st = pf._Stack(2, 1024, 4096, ctypes.cast(layers, ctypes.POINTER(pf._Layer)))

@@ -149,6 +149,20 @@ def test_tiled_unaligned_output(M):
     assert host(buf)[0] == -1.0
 
 
+@pytest.mark.parametrize("N,K,M", [(520, 2048, 100), (300, 4096, 256), (1024, 1088, 300)])
+def test_tiled_split_k_with_garbage_workspace(N, K, M):
+    """Few tiles: the K range is split and the int32 partials are summed by a
+    second launch; workspace contents on entry do not matter."""
+    W, ws, q, s = _proj(N, K, M, 1300 + N + M)
+    nb = pf.gemm_i8_chunk_workspace(N, K, M)
+    assert nb > 0
+    wsp = torch.randint(0, 255, (nb,), dtype=torch.uint8, device="cuda")
+    args = (dev(W), dev(ws), dev(q), dev(s))
+    ref = oracle.linear(W, ws, q, s)
+    for _ in range(3):
+        np.testing.assert_array_equal(host(pf.gemm_i8_chunk(*args, ws=wsp)), ref)
+
+
 def test_mfma_single_tiles_extreme_values():
     """One 16x16x64 and one 32x32x32 tile region with +-127 everywhere: operand
     layout and int32 range of the MFMA paths against exact integers."""

@@ -70,6 +70,20 @@ def test_small_stack_full_compare(chunk):
     np.testing.assert_array_equal(host(y2), y_ref)
 
 
+@pytest.mark.parametrize("chunk", [96, 160])
+def test_tiled_stack_full_compare(chunk):
+    """Chunks over 64 tokens on the tiled path with a longer down product
+    (F = 2048, 32 k-blocks) and a ragged last chunk."""
+    st = prefill_inputs.stack(L=3, H=256, F=2048, P=300, seed=23)
+    y_ref, proj_ref = oracle.stack(st["weights"], st["scales"], st["x"], return_proj=True)
+    stack = to_stack(st)
+    x = dev(st["x"])
+    proj = torch.empty((3, 300, 5 * 256 + 2 * 2048), dtype=torch.float32, device="cuda")
+    y = run(stack, x, chunk, proj=proj)
+    np.testing.assert_array_equal(host(y), y_ref)
+    np.testing.assert_array_equal(host(proj), proj_ref)
+
+
 def test_small_stack_per_token_mode_identical():
     st = prefill_inputs.stack(L=2, H=256, F=512, P=40, seed=22)
     stack = to_stack(st)
