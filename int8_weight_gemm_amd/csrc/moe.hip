@@ -14,7 +14,9 @@ namespace pf {
 // Router logits: l[t][e] = sum over k ascending of fl(Wr[e][k] * x[t][k]), each
 // product and each partial sum rounded on its own (no fused multiply-add: the
 // library is compiled with -ffp-contract=off).  32 tokens x 32 experts per
-// workgroup, 64-wide k pieces staged in LDS, 4 independent chains per thread.
+// workgroup, 4 independent chains per thread; 64-wide k pieces staged in LDS,
+// double-buffered: the next piece is loaded into registers (two 16-byte loads
+// per operand per thread) while the current one is consumed.
 constexpr int kRtTile = 32;
 constexpr int kRtK = 64;
 
@@ -22,27 +24,59 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ Wr,
                                                 const float* __restrict__ x, int E, int H, int T,
                                                 float* __restrict__ logits)
 {
-    __shared__ float sx[kRtTile][kRtK + 1];
-    __shared__ float sw[kRtTile][kRtK + 1];
+    // rows padded to 68 floats: 16-byte aligned, and the 16 rows a quarter-wave
+    // reads at one k sit in distinct banks
+    __shared__ __attribute__((aligned(16))) float sx[2][kRtTile][kRtK + 4];
+    __shared__ __attribute__((aligned(16))) float sw[2][kRtTile][kRtK + 4];
     const int e0 = blockIdx.x * kRtTile, t0 = blockIdx.y * kRtTile;
     const int ti = threadIdx.x >> 4, ei = threadIdx.x & 15;
+    // staging: float4 f = threadIdx.x + 256 u of a [32][64] piece -> row f / 16,
+    // column 4 (f % 16); this thread's two rows and column
+    const int r0 = threadIdx.x >> 4, r1 = r0 + 16, c4 = (threadIdx.x & 15) << 2;
+    const float* xr0 = x + (int64_t)min(t0 + r0, T - 1) * H + c4;
+    const float* xr1 = x + (int64_t)min(t0 + r1, T - 1) * H + c4;
+    const float* wr0 = Wr + (int64_t)min(e0 + r0, E - 1) * H + c4;
+    const float* wr1 = Wr + (int64_t)min(e0 + r1, E - 1) * H + c4;
+    float4 px0 = *reinterpret_cast<const float4*>(xr0), px1 = *reinterpret_cast<const float4*>(xr1);
+    float4 pw0 = *reinterpret_cast<const float4*>(wr0), pw1 = *reinterpret_cast<const float4*>(wr1);
+    *reinterpret_cast<float4*>(&sx[0][r0][c4]) = px0;
+    *reinterpret_cast<float4*>(&sx[0][r1][c4]) = px1;
+    *reinterpret_cast<float4*>(&sw[0][r0][c4]) = pw0;
+    *reinterpret_cast<float4*>(&sw[0][r1][c4]) = pw1;
     float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-    for (int k0 = 0; k0 < H; k0 += kRtK) {
-        for (int idx = threadIdx.x; idx < kRtTile * kRtK; idx += 256) {
-            const int r = idx / kRtK, c = idx % kRtK;
-            const int t = t0 + r, e = e0 + r;
-            sx[r][c] = t < T ? x[(int64_t)t * H + k0 + c] : 0.0f;
-            sw[r][c] = e < E ? Wr[(int64_t)e * H + k0 + c] : 0.0f;
+    const int npieces = H / kRtK;
+    __syncthreads();
+    for (int pc = 0; pc < npieces; ++pc) {
+        const int b = pc & 1;
+        const bool more = pc + 1 < npieces;
+        if (more) {
+            const int k1 = (pc + 1) * kRtK;
+            px0 = *reinterpret_cast<const float4*>(xr0 + k1);
+            px1 = *reinterpret_cast<const float4*>(xr1 + k1);
+            pw0 = *reinterpret_cast<const float4*>(wr0 + k1);
+            pw1 = *reinterpret_cast<const float4*>(wr1 + k1);
         }
-        __syncthreads();
-        for (int kk = 0; kk < kRtK; ++kk) {
+#pragma unroll 4
+        for (int kk = 0; kk < kRtK; kk += 4) {
+            const float4 w0 = *reinterpret_cast<const float4*>(&sw[b][ei][kk]);
+            const float4 w1 = *reinterpret_cast<const float4*>(&sw[b][ei + 16][kk]);
+            const float4 x0 = *reinterpret_cast<const float4*>(&sx[b][ti][kk]);
+            const float4 x1 = *reinterpret_cast<const float4*>(&sx[b][ti + 16][kk]);
+            const float wa[4] = {w0.x, w0.y, w0.z, w0.w}, wb[4] = {w1.x, w1.y, w1.z, w1.w};
+            const float xa[4] = {x0.x, x0.y, x0.z, x0.w}, xb[4] = {x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const float p = sw[ei + 16 * j][kk] * sx[ti + 16 * i][kk];
-                    acc[i][j] = acc[i][j] + p;
-                }
+            for (int c = 0; c < 4; ++c) {                // k ascending within each chain
+                acc[0][0] = acc[0][0] + wa[c] * xa[c];
+                acc[0][1] = acc[0][1] + wb[c] * xa[c];
+                acc[1][0] = acc[1][0] + wa[c] * xb[c];
+                acc[1][1] = acc[1][1] + wb[c] * xb[c];
+            }
+        }
+        if (more) {
+            *reinterpret_cast<float4*>(&sx[b ^ 1][r0][c4]) = px0;
+            *reinterpret_cast<float4*>(&sx[b ^ 1][r1][c4]) = px1;
+            *reinterpret_cast<float4*>(&sw[b ^ 1][r0][c4]) = pw0;
+            *reinterpret_cast<float4*>(&sw[b ^ 1][r1][c4]) = pw1;
         }
         __syncthreads();
     }
@@ -184,45 +218,53 @@ hipError_t launch_expf(const float* x, int64_t n, float* y, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
-// Softmax and top-k, one wave per token.  m = max l (exact); z_e = expf_cr(l_e - m);
-// S = z_0 + z_1 + ... in ascending e (one lane, sequential); p_e = z_e / S;
-// then k rounds of a wave-wide maximum over the key (p, -e): ties go to the
-// lower expert id.
+// Softmax and top-k, one wave per token, values in registers (lane l holds
+// e = l + 64 i).  m = max l (exact); z_e = expf_cr(l_e - m); S = z_0 + z_1 + ...
+// in ascending e (each z read across the wave in turn, sequential additions);
+// p_e = z_e / S; then k rounds of a wave-wide maximum over the key (p, -e):
+// ties go to the lower expert id.
 constexpr int kSmMaxE = 1024;
 
+template <int kC>                                       // values per lane: e = lane + 64 i, E <= 64 kC
 __global__ __launch_bounds__(256) void k_softmax_topk(const float* __restrict__ logits, int E, int T,
                                                       int k, int* __restrict__ ids,
                                                       float* __restrict__ w)
 {
-    __shared__ float sp[4][kSmMaxE];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
-    const bool valid = t < T;
-    const float* row = logits + (int64_t)(valid ? t : 0) * E;
+    if (t >= T) return;                                 // whole wave; no workgroup barrier below
+    const float* row = logits + (int64_t)t * E;
+    float v[kC];
     float m = -__builtin_huge_valf();
-    for (int e = lane; e < E; e += 64) m = fmaxf(m, row[e]);
-    m = wave_max(m);
-    for (int e = lane; e < E; e += 64) sp[wave][e] = expf_cr(row[e] - m);
-    __syncthreads();
-    float S = 0.0f;
-    if (lane == 0)
-        for (int e = 0; e < E; ++e) S = S + sp[wave][e];
-    S = __shfl(S, 0);
-    for (int e = lane; e < E; e += 64) sp[wave][e] = sp[wave][e] / S;
-    __syncthreads();
-    // each round: the lane-local best untaken (p, -e), then the wave maximum
-    unsigned taken[kSmMaxE / 64];
 #pragma unroll
-    for (int i = 0; i < kSmMaxE / 64; ++i) taken[i] = 0;
+    for (int i = 0; i < kC; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? row[e] : -__builtin_huge_valf();
+        m = fmaxf(m, v[i]);
+    }
+    m = wave_max(m);
+#pragma unroll
+    for (int i = 0; i < kC; ++i) v[i] = lane + 64 * i < E ? expf_cr(v[i] - m) : 0.0f;
+    // S = z_0 + z_1 + ... in ascending e, one rounding per addition
+    float S = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kC; ++i) {
+        const int n = min(64, E - 64 * i);
+        for (int l = 0; l < n; ++l)
+            S = S + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), l));
+    }
+#pragma unroll
+    for (int i = 0; i < kC; ++i) v[i] = v[i] / S;
+    // each round: the lane-local best untaken (p, -e), then the wave maximum
+    unsigned taken = 0;                                  // bit i: e = lane + 64 i taken
     for (int j = 0; j < k; ++j) {
         unsigned long long best = 0;
 #pragma unroll
-        for (int i = 0; i < kSmMaxE / 64; ++i) {
+        for (int i = 0; i < kC; ++i) {
             const int e = lane + 64 * i;
-            if (e < E && !taken[i]) {
-                const unsigned pb = __float_as_uint(sp[wave][e]);
+            if (e < E && !((taken >> i) & 1u)) {
                 const unsigned long long key =
-                    ((unsigned long long)pb << 32) | (unsigned long long)(0xffffffffu - (unsigned)e);
+                    ((unsigned long long)__float_as_uint(v[i]) << 32) | (unsigned long long)(0xffffffffu - (unsigned)e);
                 best = key > best ? key : best;
             }
         }
@@ -232,12 +274,8 @@ __global__ __launch_bounds__(256) void k_softmax_topk(const float* __restrict__ 
             best = o > best ? o : best;
         }
         const int e = (int)(0xffffffffu - (unsigned)(best & 0xffffffffu));
-        if ((e & 63) == lane) {
-#pragma unroll
-            for (int i = 0; i < kSmMaxE / 64; ++i)
-                if (i == (e >> 6)) taken[i] = 1;
-        }
-        if (lane == 0 && valid) {
+        if ((e & 63) == lane) taken |= 1u << (e >> 6);
+        if (lane == 0) {
             ids[(int64_t)t * k + j] = e;
             w[(int64_t)t * k + j] = __uint_as_float((unsigned)(best >> 32));
         }
@@ -248,15 +286,24 @@ hipError_t launch_softmax_topk(const float* logits, int E, int T, int k, int* id
                                hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
-    PF_LAUNCH(k_softmax_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, E, T, k, ids, w);
+    const dim3 g((T + 3) / 4), b(256);
+    if (E <= 64) PF_LAUNCH(k_softmax_topk<1>, g, b, 0, s, logits, E, T, k, ids, w);
+    else if (E <= 128) PF_LAUNCH(k_softmax_topk<2>, g, b, 0, s, logits, E, T, k, ids, w);
+    else if (E <= 256) PF_LAUNCH(k_softmax_topk<4>, g, b, 0, s, logits, E, T, k, ids, w);
+    else if (E <= 512) PF_LAUNCH(k_softmax_topk<8>, g, b, 0, s, logits, E, T, k, ids, w);
+    else if (E <= kSmMaxE) PF_LAUNCH(k_softmax_topk<16>, g, b, 0, s, logits, E, T, k, ids, w);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Grouping by the union of selected experts (one workgroup): a bitmap of
 // (expert, token) selections in LDS, per-expert counts, an exclusive scan into
-// offsets, then each expert lists its tokens in ascending order.  The combine
-// table gets, per token, its pair rows in ascending expert id.
+// offsets.  Then every selected pair (t, e) independently: its row in the
+// expert's group is off[e] + the number of tokens below t that chose e (a
+// popcount over e's bitmap words), so each expert lists its tokens in
+// ascending order; its rank among t's selections is the number of t's ids
+// below e, which orders the combine table by ascending expert id.
 __global__ __launch_bounds__(1024) void k_group(const int* __restrict__ ids,
                                                 const float* __restrict__ w, int T, int k, int E,
                                                 int* __restrict__ off, int* __restrict__ pair_tok,
@@ -288,26 +335,17 @@ __global__ __launch_bounds__(1024) void k_group(const int* __restrict__ ids,
     }
     if (tid < E) off[tid + 1] = scan[tid];
     if (tid == 0) off[0] = 0;
-    for (int e = tid; e < E; e += 1024) {
-        int pos = scan[e] - cnt[e];
-        for (int wd = 0; wd < words; ++wd) {
-            unsigned bits = sel[e * words + wd];
-            while (bits) {
-                const int t = (wd << 5) + (__ffs(bits) - 1);
-                bits &= bits - 1;
-                pair_tok[pos] = t;
-                int rank = 0;
-                float we = 0.0f;
-                for (int j = 0; j < k; ++j) {
-                    const int ej = ids[t * k + j];
-                    rank += ej < e;
-                    if (ej == e) we = w[t * k + j];
-                }
-                comb_row[t * k + rank] = pos;
-                comb_w[t * k + rank] = we;
-                ++pos;
-            }
-        }
+    for (int p = tid; p < T * k; p += 1024) {
+        const int t = p / k, e = ids[p];
+        const unsigned* se = sel + e * words;
+        int below = __popc(se[t >> 5] & ((1u << (t & 31)) - 1u));
+        for (int wd = 0; wd < (t >> 5); ++wd) below += __popc(se[wd]);
+        const int pos = scan[e] - cnt[e] + below;
+        int rank = 0;
+        for (int j = 0; j < k; ++j) rank += ids[t * k + j] < e;
+        pair_tok[pos] = t;
+        comb_row[t * k + rank] = pos;
+        comb_w[t * k + rank] = w[p];
     }
 }
 
@@ -430,13 +468,29 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ypair
                                                  float* __restrict__ out)
 {
     const int t = blockIdx.x;
+    float* o_row = out + (int64_t)t * H;
+    if (((uintptr_t)o_row & 15) == 0) {                 // four outputs per lane, 16-byte accesses
+        for (int j = threadIdx.x * 4; j < H; j += 1024) {
+            float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            for (int r = 0; r < k; ++r) {
+                const float wr = comb_w[t * k + r];
+                const float4 y = *reinterpret_cast<const float4*>(ypair + (int64_t)comb_row[t * k + r] * H + j);
+                o.x = o.x + wr * y.x;
+                o.y = o.y + wr * y.y;
+                o.z = o.z + wr * y.z;
+                o.w = o.w + wr * y.w;
+            }
+            *reinterpret_cast<float4*>(o_row + j) = o;
+        }
+        return;
+    }
     for (int j = threadIdx.x; j < H; j += 256) {
         float o = 0.0f;
         for (int r = 0; r < k; ++r) {
             const float c = comb_w[t * k + r] * ypair[(int64_t)comb_row[t * k + r] * H + j];
             o = o + c;
         }
-        out[(int64_t)t * H + j] = o;
+        o_row[j] = o;
     }
 }
 

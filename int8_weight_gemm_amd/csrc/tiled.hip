@@ -150,7 +150,7 @@ __device__ __forceinline__ void lds_write4(uint32_t a, v4i d0, v4i d1, v4i d2, v
 // to the last one and land in free slots, never read), so every wait is a
 // constant.
 template <int WJ>
-__device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int split)
+__device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int kidx)
 {
     constexpr int NS = 4;
     constexpr int WB = 2 * WJ;                           // token fragments per wave
@@ -165,7 +165,7 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int sp
     const int tm = local % P.tiles_m, tn = local / P.tiles_m;
     const int n0 = tn * 256, t0 = tm * 64 * WJ;
     // this split's k-blocks: kb0 .. kb0 + nkb - 1 (all of K when unsplit)
-    const int kb0 = split * P.kb_per_split;
+    const int kb0 = kidx * P.kb_per_split;
     const int nkb = min(P.kb_per_split, (P.K >> 6) - kb0);
     // fragment f: rows (or tokens) 16 f .. + 15 of the k-block, lane l's 16
     // bytes (row l % 16, bytes 16 (l / 16) .. + 15) at 16 l: each copy reads 16
@@ -282,53 +282,24 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int sp
     wait_vmcnt<0>();                                     // no copy outlives the workgroup's LDS
 
     // Lane l, register 4 q + r of a 32 x 32 block: token l % 32, row
-    // 8 q + 4 (l / 32) + r.
-    if (P.splits > 1) {                                  // int32 partials of this split
-        int* const part = P.acc + (int64_t)split * P.acc_split;
-        const bool v4 = ((P.acc_ld & 3) == 0) && ((P.acc_split & 3) == 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * 128 + 32 * i + 8 * q + ((lane >> 5) << 2);
-                if (n >= P.N) continue;
-#pragma unroll
-                for (int j = 0; j < WJ; ++j) {
-                    const int t = t0 + wm * 32 * WJ + 32 * j + lrow;
-                    if (t >= P.M) continue;
-                    int* p = part + (int64_t)t * P.acc_ld + n;
-                    const v4i v = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    if (v4 && n + 3 < P.N) {
-                        *reinterpret_cast<v4i*>(p) = v;
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (n + r < P.N) p[r] = v[r];
-                    }
-                }
-            }
-        return;
-    }
-    stage_barrier();                                     // every wave is done with the ring
-
-    // The tile's 256 weight scales and 64 WJ token scales, staged once through
-    // LDS (one load each per thread, all in flight together).
+    // 8 q + 4 (l / 32) + r.  Split: this split's int32 partials; unsplit:
+    // the epilogue with the tile's scales staged once through LDS.
+    const bool split = P.splits > 1;
+    int* const part = split ? P.acc + (int64_t)kidx * P.acc_split : nullptr;
     float* const sws = reinterpret_cast<float*>(ring);
     float* const sxs = sws + 256;
-    {
+    if (!split) {
+        stage_barrier();                                 // every wave is done with the ring
         const int t = (int)threadIdx.x;
         const float wv = P.ws[min(n0 + t, P.N - 1)];
         const float xv = t < 64 * WJ ? P.xs[min(t0 + t, P.M - 1)] : 0.0f;
         sws[t] = wv;
         if (t < 64 * WJ) sxs[t] = xv;
+        __syncthreads();
     }
-    __syncthreads();
-
-    const bool vec = (((uintptr_t)P.Y & 15) == 0) && ((P.ldy & 3) == 0) &&
+    const bool pv4 = split && ((P.acc_ld & 3) == 0) && ((P.acc_split & 3) == 0);
+    const bool vec = !split && (((uintptr_t)P.Y & 15) == 0) && ((P.ldy & 3) == 0) &&
                      (!P.Y2 || ((((uintptr_t)P.Y2 & 15) == 0) && ((P.ldy2 & 3) == 0)));
-    float xs[WJ];
-#pragma unroll
-    for (int j = 0; j < WJ; ++j) xs[j] = sxs[wm * 32 * WJ + 32 * j + lrow];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -336,17 +307,31 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int sp
             const int nl = wn * 128 + 32 * i + 8 * q + ((lane >> 5) << 2);   // row in the tile
             const int n = n0 + nl;
             if (n >= P.N) continue;
-            const float4 w4 = *reinterpret_cast<const float4*>(sws + nl);
-            const float w[4] = {w4.x, w4.y, w4.z, w4.w};
+            float4 w4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (!split) w4 = *reinterpret_cast<const float4*>(sws + nl);
 #pragma unroll
             for (int j = 0; j < WJ; ++j) {
-                const int t = t0 + wm * 32 * WJ + 32 * j + lrow;
+                const int tl = wm * 32 * WJ + 32 * j + lrow;                 // token in the tile
+                const int t = t0 + tl;
                 if (t >= P.M) continue;
+                const v4i a = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                if (split) {
+                    int* p = part + (int64_t)t * P.acc_ld + n;
+                    if (pv4 && n + 3 < P.N) {
+                        *reinterpret_cast<v4i*>(p) = a;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (n + r < P.N) p[r] = a[r];
+                    }
+                    continue;
+                }
+                const float xs = sxs[tl];
                 float4 v;
-                v.x = epilogue(acc[i][j][4 * q + 0], w[0], xs[j]);
-                v.y = epilogue(acc[i][j][4 * q + 1], w[1], xs[j]);
-                v.z = epilogue(acc[i][j][4 * q + 2], w[2], xs[j]);
-                v.w = epilogue(acc[i][j][4 * q + 3], w[3], xs[j]);
+                v.x = epilogue(a[0], w4.x, xs);
+                v.y = epilogue(a[1], w4.y, xs);
+                v.z = epilogue(a[2], w4.z, xs);
+                v.w = epilogue(a[3], w4.w, xs);
                 float* y = P.Y + (int64_t)t * P.ldy + n;
                 float* y2 = P.Y2 ? P.Y2 + (int64_t)t * P.ldy2 + n : nullptr;
                 if (vec && n + 3 < P.N) {
