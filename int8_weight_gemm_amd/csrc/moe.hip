@@ -218,65 +218,82 @@ hipError_t launch_expf(const float* x, int64_t n, float* y, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
-// Softmax and top-k, one wave per token, values in registers (lane l holds
-// e = l + 64 i).  m = max l (exact); z_e = expf_cr(l_e - m); S = z_0 + z_1 + ...
-// in ascending e (each z read across the wave in turn, sequential additions);
-// p_e = z_e / S; then k rounds of a wave-wide maximum over the key (p, -e):
-// ties go to the lower expert id.
+// Softmax and top-k, one workgroup per token, one thread per expert.
+// m = max l (exact, any order); z_e = expf_cr(l_e - m); S = z_0 + z_1 + ... in
+// ascending e (one lane, sequential, over LDS); p_e = z_e / S.  Each wave then
+// takes the k best keys (p, -e) of its 64 experts by k rounds of a wave-wide
+// maximum; wave 0 takes the k best of those candidates the same way, so ties
+// go to the lower expert id.
 constexpr int kSmMaxE = 1024;
+constexpr int kSmMaxK = 32;
 
-template <int kC>                                       // values per lane: e = lane + 64 i, E <= 64 kC
-__global__ __launch_bounds__(256) void k_softmax_topk(const float* __restrict__ logits, int E, int T,
-                                                      int k, int* __restrict__ ids,
-                                                      float* __restrict__ w)
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t = blockIdx.x * 4 + wave;
-    if (t >= T) return;                                 // whole wave; no workgroup barrier below
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const unsigned long long o = __shfl_xor(v, off);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(1024) void k_softmax_topk(const float* __restrict__ logits, int E, int T,
+                                                       int k, int* __restrict__ ids,
+                                                       float* __restrict__ w)
+{
+    __shared__ __attribute__((aligned(16))) float zs[kSmMaxE];
+    __shared__ float wmax[kSmMaxE / 64];
+    __shared__ float sS;
+    __shared__ unsigned long long cand[kSmMaxE / 64 * kSmMaxK];
+    const int t = blockIdx.x;
+    const int e = threadIdx.x, lane = e & 63, wave = e >> 6, nw = blockDim.x >> 6;
     const float* row = logits + (int64_t)t * E;
-    float v[kC];
-    float m = -__builtin_huge_valf();
-#pragma unroll
-    for (int i = 0; i < kC; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? row[e] : -__builtin_huge_valf();
-        m = fmaxf(m, v[i]);
+    const float l = e < E ? row[e] : -__builtin_huge_valf();
+    float m = wave_max(l);
+    if (lane == 0) wmax[wave] = m;
+    __syncthreads();
+    m = wmax[0];
+    for (int i = 1; i < nw; ++i) m = fmaxf(m, wmax[i]);
+    const float z = e < E ? expf_cr(l - m) : 0.0f;
+    zs[e] = z;                                           // zeros past E add nothing below
+    __syncthreads();
+    if (e == 0) {
+        float S = 0.0f;
+        for (int i = 0; i < (int)blockDim.x; i += 4) {
+            const float4 q = *reinterpret_cast<const float4*>(zs + i);
+            S = S + q.x;
+            S = S + q.y;
+            S = S + q.z;
+            S = S + q.w;
+        }
+        sS = S;
     }
-    m = wave_max(m);
-#pragma unroll
-    for (int i = 0; i < kC; ++i) v[i] = lane + 64 * i < E ? expf_cr(v[i] - m) : 0.0f;
-    // S = z_0 + z_1 + ... in ascending e, one rounding per addition
-    float S = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kC; ++i) {
-        const int n = min(64, E - 64 * i);
-        for (int l = 0; l < n; ++l)
-            S = S + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), l));
+    __syncthreads();
+    const float p = z / sS;
+    const int kw = min(k, 64);                           // candidates per wave
+    unsigned long long key =
+        e < E ? ((unsigned long long)__float_as_uint(p) << 32) | (unsigned long long)(0xffffffffu - (unsigned)e) : 0ull;
+    for (int j = 0; j < kw; ++j) {
+        const unsigned long long best = wave_max_u64(key);
+        if (key == best) key = 0ull;                     // keys are distinct (distinct e)
+        if (lane == 0) cand[wave * kw + j] = best;
     }
+    __syncthreads();
+    if (wave != 0) return;
+    const int nc = nw * kw;                              // <= 512: up to 8 per lane
+    unsigned long long c[kSmMaxE / 64 * kSmMaxK / 64];
 #pragma unroll
-    for (int i = 0; i < kC; ++i) v[i] = v[i] / S;
-    // each round: the lane-local best untaken (p, -e), then the wave maximum
-    unsigned taken = 0;                                  // bit i: e = lane + 64 i taken
+    for (int i = 0; i < kSmMaxE / 64 * kSmMaxK / 64; ++i) c[i] = lane + 64 * i < nc ? cand[lane + 64 * i] : 0ull;
     for (int j = 0; j < k; ++j) {
-        unsigned long long best = 0;
+        unsigned long long mine = 0ull;
 #pragma unroll
-        for (int i = 0; i < kC; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E && !((taken >> i) & 1u)) {
-                const unsigned long long key =
-                    ((unsigned long long)__float_as_uint(v[i]) << 32) | (unsigned long long)(0xffffffffu - (unsigned)e);
-                best = key > best ? key : best;
-            }
-        }
+        for (int i = 0; i < kSmMaxE / 64 * kSmMaxK / 64; ++i) mine = c[i] > mine ? c[i] : mine;
+        const unsigned long long best = wave_max_u64(mine);
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const unsigned long long o = __shfl_xor(best, off);
-            best = o > best ? o : best;
-        }
-        const int e = (int)(0xffffffffu - (unsigned)(best & 0xffffffffu));
-        if ((e & 63) == lane) taken |= 1u << (e >> 6);
+        for (int i = 0; i < kSmMaxE / 64 * kSmMaxK / 64; ++i)
+            if (c[i] == best) c[i] = 0ull;
         if (lane == 0) {
-            ids[(int64_t)t * k + j] = e;
+            ids[(int64_t)t * k + j] = (int)(0xffffffffu - (unsigned)(best & 0xffffffffu));
             w[(int64_t)t * k + j] = __uint_as_float((unsigned)(best >> 32));
         }
     }
@@ -286,13 +303,8 @@ hipError_t launch_softmax_topk(const float* logits, int E, int T, int k, int* id
                                hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
-    const dim3 g((T + 3) / 4), b(256);
-    if (E <= 64) PF_LAUNCH(k_softmax_topk<1>, g, b, 0, s, logits, E, T, k, ids, w);
-    else if (E <= 128) PF_LAUNCH(k_softmax_topk<2>, g, b, 0, s, logits, E, T, k, ids, w);
-    else if (E <= 256) PF_LAUNCH(k_softmax_topk<4>, g, b, 0, s, logits, E, T, k, ids, w);
-    else if (E <= 512) PF_LAUNCH(k_softmax_topk<8>, g, b, 0, s, logits, E, T, k, ids, w);
-    else if (E <= kSmMaxE) PF_LAUNCH(k_softmax_topk<16>, g, b, 0, s, logits, E, T, k, ids, w);
-    else return hipErrorInvalidValue;
+    if (E > kSmMaxE || k > kSmMaxK) return hipErrorInvalidValue;
+    PF_LAUNCH(k_softmax_topk, dim3(T), dim3(64 * ((E + 63) / 64)), 0, s, logits, E, T, k, ids, w);
     return hipGetLastError();
 }
 
