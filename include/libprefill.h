@@ -76,7 +76,8 @@ pf_status pf_init(void);
 pf_status pf_workspace_clear(void* workspace, size_t bytes, void* stream);
 
 /* Per-token symmetric int8 quantisation of a chunk, done once per chunk
- * ("Batched Prefill", §The Solution, "quantize activations once per batch").
+ * ("Batched Prefill", §The Solution: activations are quantised once per batch,
+ * not once per weight row).
  * x [M][ldx] f32 (first K of each row used) -> xq [M][K] int8, a_scale [M] f32.
  * M = 0 is a no-op.  ldx >= K, ldx % 4 == 0. */
 pf_status pf_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx,

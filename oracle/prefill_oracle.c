@@ -18,7 +18,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-/* Quantise one token row.  Reading of "quantize activations once per batch"
+/* Quantise one token row.  Reading of the per-batch activation quantisation
  * ("Batched Prefill", §The Solution): symmetric, scale s = absmax/127, values
  * divided by s (IEEE division) and rounded half away from zero (C roundf),
  * clamped to [-127, 127]; an all-zero row gets s = 0 and q = 0. */

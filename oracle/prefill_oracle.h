@@ -31,8 +31,8 @@ extern "C" {
 
 /* Return codes: 0 ok, -1 bad argument, -2 non-finite input value. */
 
-/* Per-token symmetric quantisation, once per token row [cellm §The Solution,
- * "quantize activations once per batch"]: amax = max|x_k| (exact),
+/* Per-token symmetric quantisation, once per token row [cellm §The Solution:
+ * activations quantised once per batch]: amax = max|x_k| (exact),
  * s = fl(amax / 127), q_k = clamp(roundf(fl(x_k / s)), -127, 127) with roundf
  * rounding halves away from zero; s == 0 gives q = 0.  x [M][K] -> q [M][K],
  * s [M]. */
