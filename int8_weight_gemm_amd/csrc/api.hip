@@ -211,11 +211,11 @@ struct StackLayout {
 };
 
 
-constexpr int kMaxGroups = 4;        // library streams per device
+constexpr int kMaxGroups = 4;
 
-// Chunk groups of the stack sweep and the slots of each: three groups (three
-// library streams; with the caller's stream that is the four hardware queues
-// a process gets by default) of up to 16 chunks in flight.  A step of a group
+// Chunk groups of the stack sweep and the slots of each: three groups (the
+// caller's stream and two library streams, within the four hardware queues a
+// process gets by default) of up to 16 chunks in flight.  A step of a group
 // launches one product over all of its chunks in flight, so a group's slots
 // are at most kMaxPairs.
 constexpr int kStackGroups = 3;
@@ -319,9 +319,9 @@ double product_bytes(int64_t N, int64_t K, int64_t M)
     return (double)N * K + 4.0 * N + (double)M * K + 4.0 * M + 4.0 * M * N;
 }
 
-// Library-owned streams per device, one per chunk group (default priority,
-// non-blocking), and the events that fork them from and join them back to the
-// caller's stream.
+// Library-owned streams per device, one per chunk group after the first, which
+// runs on the caller's stream (default priority, non-blocking), and the events
+// that fork them from and join them back to the caller's stream.
 // Created on first use and kept until the process ends; the mutex serialises
 // calls that use them from several host threads.
 struct DevStreams {
@@ -344,10 +344,10 @@ DevStreams* dev_streams()
 pf_status ensure_streams(DevStreams* d)
 {
     if (d->ready) return PF_OK;
-    for (int i = 0; i < kMaxGroups; ++i)
+    for (int i = 1; i < kStackGroups; ++i)
         if (hipStreamCreateWithFlags(&d->s[i], hipStreamNonBlocking) != hipSuccess) return PF_ELAUNCH;
     if (hipEventCreateWithFlags(&d->fork, hipEventDisableTiming) != hipSuccess) return PF_ELAUNCH;
-    for (int i = 0; i < kMaxGroups; ++i)
+    for (int i = 1; i < kStackGroups; ++i)
         if (hipEventCreateWithFlags(&d->join[i], hipEventDisableTiming) != hipSuccess) return PF_ELAUNCH;
     d->ready = true;
     return PF_OK;
@@ -507,18 +507,21 @@ struct StackRun {
                 if (pf_status r = group_step(rec, 0, step, fin, s)) return r;
             return PF_OK;
         }
+        // group 0 runs on the caller's stream, the others on library streams
+        hipStream_t gs[kMaxGroups] = {s};
+        for (int g = 1; g < ng; ++g) gs[g] = ds->s[g];
         if (hipEventRecord(ds->fork, s) != hipSuccess) return PF_ELAUNCH;
-        for (int g = 0; g < ng; ++g)
-            if (hipStreamWaitEvent(ds->s[g], ds->fork, 0) != hipSuccess) return PF_ELAUNCH;
+        for (int g = 1; g < ng; ++g)
+            if (hipStreamWaitEvent(gs[g], ds->fork, 0) != hipSuccess) return PF_ELAUNCH;
         int64_t fin[kMaxGroups] = {-1, -1, -1, -1};
         int64_t nst = 0;
         for (int g = 0; g < ng; ++g) nst = std::max(nst, group_steps(g));
         for (int64_t step = 0; step <= nst; ++step)
             for (int g = 0; g < ng; ++g)
                 if (step <= group_steps(g))
-                    if (pf_status r = group_step(rec, g, step, fin[g], ds->s[g])) return r;
-        for (int g = 0; g < ng; ++g) {
-            if (hipEventRecord(ds->join[g], ds->s[g]) != hipSuccess) return PF_ELAUNCH;
+                    if (pf_status r = group_step(rec, g, step, fin[g], gs[g])) return r;
+        for (int g = 1; g < ng; ++g) {
+            if (hipEventRecord(ds->join[g], gs[g]) != hipSuccess) return PF_ELAUNCH;
             if (hipStreamWaitEvent(s, ds->join[g], 0) != hipSuccess) return PF_ELAUNCH;
         }
         return PF_OK;
