@@ -16,10 +16,12 @@
 //    conflict-free ds_read_b128 each; a ring of four stages, one barrier per
 //    stage, and the reads of stage g + 1 are in flight while the MFMAs of
 //    stage g run;
-//  * the token fragments are copied by global_load_lds_dwordx4, the weight
-//    fragments by ordinary 128-bit loads into registers (three stages ahead)
-//    and ds_write_b128: the direct copy alone cannot feed a compute unit at this
-//    rate, the two paths together can;
+//  * every fragment, weights and tokens, is copied by global_load_lds_dwordx4,
+//    three stages ahead.  (Weights through registers and ds_write_b128 issue
+//    about twice as slowly per fragment.)  The copies of a stage take the
+//    compute unit's address unit about 0.75 of the stage's MFMA time, and a
+//    wave that issues them cannot issue MFMAs meanwhile: that, not latency,
+//    is what holds this kernel below the matrix-core rate;
 //  * workgroups on one XCD (blockIdx % 8) take consecutive tiles, and the token
 //    tiles of one band of weight rows are consecutive, so the band is fetched
 //    from HBM once into that XCD's L2 and shared.
@@ -119,19 +121,6 @@ __device__ __forceinline__ void tl_wait<8>(TlFrags<8>& f)
                  "+v"(f.b[4]), "+v"(f.b[5]), "+v"(f.b[6]), "+v"(f.b[7]));
 }
 
-// Four weight fragments of a stage into LDS (at a, a + 4 KB, a + 8 KB,
-// a + 12 KB); returns once they are written, so the source registers may be
-// reloaded.
-__device__ __forceinline__ void lds_write4(uint32_t a, v4i d0, v4i d1, v4i d2, v4i d3)
-{
-    asm volatile("ds_write_b128 %0, %1\n"
-                 "ds_write_b128 %0, %2 offset:4096\n"
-                 "ds_write_b128 %0, %3 offset:8192\n"
-                 "ds_write_b128 %0, %4 offset:12288\n"
-                 "s_waitcnt lgkmcnt(0)"
-                 :: "v"(a), "v"(d0), "v"(d1), "v"(d2), "v"(d3) : "memory");
-}
-
 // One 256 x 64 WJ output tile of problem P (tile index `local`, token tiles
 // fastest).  Four waves in a 2 x 2 grid; wave (wn, wm) owns rows
 // 128 wn .. + 127 and tokens 32 WJ wm .. + 32 WJ - 1 of the tile: 4 x WJ
@@ -186,16 +175,14 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
         bsrc[h] = P.X + (int64_t)min(t0 + 16 * f + (lane & 15), P.M - 1) * P.ldx + kof;
     }
     const uint32_t ring0 = lds_addr(ring);
-    const uint32_t awr = ring0 + wave * 1024 + lane * 16;
 
     auto kbo = [&](int s) { return (int64_t)(kb0 + min(s, nkb - 1)) * 64; };
-    auto load_a = [&](int s, v4i (&r)[ka]) {
-#pragma unroll
-        for (int h = 0; h < ka; ++h) r[h] = ld16(asrc[h] + kbo(s));
-    };
-    auto put = [&](int s, const v4i (&r)[ka]) {         // stage s: weights from r, tokens by DMA
-        lds_write4(awr + (uint32_t)((s % NS) * kStage), r[0], r[1], r[2], r[3]);
+    // stage s into its slot: this wave's weight fragments w, w + 4, w + 8,
+    // w + 12 and token fragments kFa + w + 4 h, all by DMA (kOps copies)
+    auto put = [&](int s) {
         int8_t* slot = ring + (s % NS) * kStage;
+#pragma unroll
+        for (int h = 0; h < ka; ++h) dma16(asrc[h] + kbo(s), slot + (wave + 4 * h) * 1024);
 #pragma unroll
         for (int h = 0; h < kb; ++h) dma16(bsrc[h] + kbo(s), slot + (kFa + wave + 4 * h) * 1024);
     };
@@ -215,41 +202,28 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
 #pragma unroll
         for (int j = 0; j < WJ; ++j) acc[i][j] = v16i{};
 
-    // stages 0 .. 3 in the ring; weights of stages 4 .. 6 in the three register
-    // sets, issued in the loop's order (tokens of stage s, then weights of
-    // stage s + 3), one stage per fenced group
-    v4i rs[3][ka];
-    {
-        v4i first[NS][ka];                               // all loads in flight at once
-#pragma unroll
-        for (int s = 0; s < NS; ++s) load_a(s, first[s]);
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-            lds_write4(awr + (uint32_t)(s * kStage), first[s][0], first[s][1], first[s][2], first[s][3]);
-    }
+    // stages 0 .. NS - 1 into the ring, one stage per fenced group
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        int8_t* slot = ring + s * kStage;
-#pragma unroll
-        for (int h = 0; h < kb; ++h) dma16(bsrc[h] + kbo(s), slot + (kFa + wave + 4 * h) * 1024);
-        if (s > 0) load_a(s + NS - 1, rs[s - 1]);
+        put(s);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
-    wait_vmcnt<3 * kOps>();                              // own copies of stage 0
+    wait_vmcnt<(NS - 1) * kOps>();                       // own copies of stage 0
     stage_barrier();
     TlFrags<WB> fr[2];
     tl_issue<WB>(fr[0], ra, rb);
 
-    // tail: a step after the unrolled loop, whose weight loads may feed nothing
-    // and be dropped by the compiler, so its wait cannot count on them
-    auto step = [&](int g, v4i (&r)[ka], TlFrags<WB>& cur, TlFrags<WB>& nxt, bool tail) {
+    // Iteration g: wait for stage g's operands (read in iteration g - 1) and
+    // this wave's copies of stage g + 1; barrier (stage g + 1 published, stage
+    // g read by all); copy stage g + NS into the slot of stage g; issue the
+    // reads of stage g + 1; the MFMAs of stage g.  A tail step is the last
+    // stage (g = nkb - 1) and reads and copies nothing.
+    auto step = [&](int g, TlFrags<WB>& cur, TlFrags<WB>& nxt, bool tail) {
         tl_wait<WB>(cur);
-        if (g + 1 < nkb) {
-            if (tail) wait_vmcnt<0>();
-            else wait_vmcnt<2 * kOps>();                 // own copies of stage g + 1, weights of g + 4
+        if (!tail && g + 1 < nkb) {
+            wait_vmcnt<(NS - 2) * kOps>();               // own copies of stage g + 1
             stage_barrier();                             // stage g + 1 published; stage g read by all
-            put(g + NS, r);                              // into the slot of stage g
-            load_a(g + NS + 3, r);
+            put(g + NS);                                 // into the slot of stage g
             __atomic_signal_fence(__ATOMIC_SEQ_CST);     // this stage's copies stay in it
             const uint32_t so = (uint32_t)(((g + 1) % NS) * kStage);
             tl_issue<WB>(nxt, ra + so, rb + so);
@@ -266,19 +240,11 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
         __builtin_amdgcn_sched_barrier(0);
     };
     int g = 0;
-    for (; g + 5 < nkb; g += 6) {                        // the same registers every pass
-        step(g, rs[0], fr[0], fr[1], false);
-        step(g + 1, rs[1], fr[1], fr[0], false);
-        step(g + 2, rs[2], fr[0], fr[1], false);
-        step(g + 3, rs[0], fr[1], fr[0], false);
-        step(g + 4, rs[1], fr[0], fr[1], false);
-        step(g + 5, rs[2], fr[1], fr[0], false);
+    for (; g + 1 < nkb; g += 2) {                        // the same registers every pass
+        step(g, fr[0], fr[1], false);
+        step(g + 1, fr[1], fr[0], false);
     }
-    if (g < nkb) step(g, rs[0], fr[0], fr[1], true);
-    if (g + 1 < nkb) step(g + 1, rs[1], fr[1], fr[0], true);
-    if (g + 2 < nkb) step(g + 2, rs[2], fr[0], fr[1], true);
-    if (g + 3 < nkb) step(g + 3, rs[0], fr[1], fr[0], true);
-    if (g + 4 < nkb) step(g + 4, rs[1], fr[0], fr[1], true);
+    if (g < nkb) step(g, fr[0], fr[1], true);
     wait_vmcnt<0>();                                     // no copy outlives the workgroup's LDS
 
     // Lane l, register 4 q + r of a 32 x 32 block: token l % 32, row
