@@ -76,6 +76,35 @@ __device__ __forceinline__ void tl_issue<4>(TlFrags<4>& f, uint32_t a, uint32_t 
 }
 
 template <>
+__device__ __forceinline__ void tl_issue<2>(TlFrags<2>& f, uint32_t a, uint32_t b)
+{
+    asm volatile(
+        "ds_read_b128 %0, %10 offset:0\n"
+        "ds_read_b128 %1, %10 offset:512\n"
+        "ds_read_b128 %2, %10 offset:2048\n"
+        "ds_read_b128 %3, %10 offset:2560\n"
+        "ds_read_b128 %4, %10 offset:4096\n"
+        "ds_read_b128 %5, %10 offset:4608\n"
+        "ds_read_b128 %6, %10 offset:6144\n"
+        "ds_read_b128 %7, %10 offset:6656\n"
+        "ds_read_b128 %8, %11 offset:0\n"
+        "ds_read_b128 %9, %11 offset:512\n"
+        : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.a[2]), "=&v"(f.a[3]),
+          "=&v"(f.a[4]), "=&v"(f.a[5]), "=&v"(f.a[6]), "=&v"(f.a[7]),
+          "=&v"(f.b[0]), "=&v"(f.b[1])
+        : "v"(a), "v"(b));
+}
+
+template <>
+__device__ __forceinline__ void tl_wait<2>(TlFrags<2>& f)
+{
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]),
+                 "+v"(f.a[4]), "+v"(f.a[5]), "+v"(f.a[6]), "+v"(f.a[7]),
+                 "+v"(f.b[0]), "+v"(f.b[1]));
+}
+
+template <>
 __device__ __forceinline__ void tl_wait<4>(TlFrags<4>& f)
 {
     asm volatile("s_waitcnt lgkmcnt(0)"
@@ -122,35 +151,39 @@ __device__ __forceinline__ void tl_wait<8>(TlFrags<8>& f)
 }
 
 // One 256 x 64 WJ output tile of problem P (tile index `local`, token tiles
-// fastest).  Four waves in a 2 x 2 grid; wave (wn, wm) owns rows
-// 128 wn .. + 127 and tokens 32 WJ wm .. + 32 WJ - 1 of the tile: 4 x WJ
-// accumulator blocks of 32 x 32.  Stage s (one k-block) sits in ring slot
-// s % 4: weight fragments 0 .. 15 (16 rows x 64 bytes each), then token
-// fragments 0 .. 4 WJ - 1.  Per stage wave w loads weight fragments
-// w, w + 4, w + 8, w + 12 into registers (three stages ahead) and writes them
-// into the slot, and copies token fragments w + 4 h by DMA.  Iteration g:
-//   wait for stage g's fragments (read in iteration g - 1); wait for this
-//   wave's copies of stage g + 1 and its weight loads of stage g + 4;
-//   barrier (stage g + 1 published, stage g read by all); fill the slot of
-//   stage g with stage g + 4 and load the weights of stage g + 7; issue the
-//   reads of stage g + 1; the MFMAs of stage g, which overlap those reads and
-//   the copies.
+// fastest), by NW waves (4: one per SIMD; 8: two per SIMD) in a 2 x NW/2 grid:
+// wave (wn, wm) owns rows 128 wn .. + 127 and JB = 4 WJ / NW token blocks of
+// 32 from token 32 JB wm: 4 x JB accumulator blocks of 32 x 32.  Stage s (one
+// k-block) sits in ring slot s % 4: weight fragments 0 .. 15 (16 rows x 64
+// bytes each), then token fragments 0 .. 4 WJ - 1; wave w copies fragments
+// w + NW h of each by DMA.  Iteration g:
+//   wait for stage g's fragments (read in iteration g - 1) and this wave's
+//   copies of stage g + 1; barrier (stage g + 1 published, stage g read by
+//   all); copy stage g + 4 into the slot of stage g; issue the reads of stage
+//   g + 1; the MFMAs of stage g.
+// With two waves per SIMD, the waves of the second row half copy after their
+// first k half of MFMAs instead: a wave issuing copies issues no MFMA, and
+// its SIMD's other wave then does.
 // Every iteration issues the same copies (k-blocks past the end are clamped
 // to the last one and land in free slots, never read), so every wait is a
 // constant.
-template <int WJ>
+template <int WJ, int NW>
 __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int kidx)
 {
     constexpr int NS = 4;
-    constexpr int WB = 2 * WJ;                           // token fragments per wave
-    constexpr int kFa = 16, kFb = 2 * WB;                // fragments per stage
+    constexpr int WMT = NW / 2;                          // token parts of the wave grid
+    constexpr int JB = 2 * WJ / WMT;                     // 32-token blocks per wave
+    constexpr int WB = 2 * JB;                           // token operands per wave per stage
+    constexpr int kFa = 16, kFb = 4 * WJ;                // fragments per stage
     constexpr int kStage = (kFa + kFb) * 1024;
-    constexpr int ka = 4, kb = kFb / 4;                  // loads / DMAs per wave per stage
+    constexpr int ka = kFa / NW, kb = kFb / NW;          // copies per wave per stage
     constexpr int kOps = ka + kb;                        // vector-memory ops per wave per stage
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
+    static_assert(kb * NW == kFb && JB >= 1, "tile shape");
     static_assert(3 * kOps <= 63, "vmcnt range");
     __shared__ __attribute__((aligned(16))) int8_t ring[NS * kStage];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;   // four waves
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int tm = local % P.tiles_m, tn = local / P.tiles_m;
     const int n0 = tn * 256, t0 = tm * 64 * WJ;
     // this split's k-blocks: kb0 .. kb0 + nkb - 1 (all of K when unsplit)
@@ -165,26 +198,26 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
     const int8_t* asrc[ka];
 #pragma unroll
     for (int h = 0; h < ka; ++h) {
-        const int f = wave + 4 * h;
+        const int f = wave + NW * h;
         asrc[h] = P.W + (int64_t)min(n0 + 16 * f + (lane & 15), P.N - 1) * P.K + kof;
     }
     const int8_t* bsrc[kb];
 #pragma unroll
     for (int h = 0; h < kb; ++h) {
-        const int f = wave + 4 * h;
+        const int f = wave + NW * h;
         bsrc[h] = P.X + (int64_t)min(t0 + 16 * f + (lane & 15), P.M - 1) * P.ldx + kof;
     }
     const uint32_t ring0 = lds_addr(ring);
 
     auto kbo = [&](int s) { return (int64_t)(kb0 + min(s, nkb - 1)) * 64; };
-    // stage s into its slot: this wave's weight fragments w, w + 4, w + 8,
-    // w + 12 and token fragments kFa + w + 4 h, all by DMA (kOps copies)
+    // stage s into its slot: this wave's weight fragments w + NW h and token
+    // fragments kFa + w + NW h, all by DMA (kOps copies)
     auto put = [&](int s) {
         int8_t* slot = ring + (s % NS) * kStage;
 #pragma unroll
-        for (int h = 0; h < ka; ++h) dma16(asrc[h] + kbo(s), slot + (wave + 4 * h) * 1024);
+        for (int h = 0; h < ka; ++h) dma16(asrc[h] + kbo(s), slot + (wave + NW * h) * 1024);
 #pragma unroll
-        for (int h = 0; h < kb; ++h) dma16(bsrc[h] + kbo(s), slot + (kFa + wave + 4 * h) * 1024);
+        for (int h = 0; h < kb; ++h) dma16(bsrc[h] + kbo(s), slot + (kFa + wave + NW * h) * 1024);
     };
 
     // The 32 x 32 x 32 operand of rows 32 i .. + 31, k half kh: lane l needs
@@ -192,15 +225,16 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
     // 2 i + (l / 16) % 2 at 16 (l % 16 + 16 (2 kh + l / 32)).  Per 16-lane group
     // the 16-byte reads are consecutive: no bank conflicts.
     const uint32_t lofs = (uint32_t)(((lane >> 4) & 1) * 1024 + 16 * (lane & 15) + 256 * (lane >> 5));
-    const int wn = wave >> 1, wm = wave & 1;
+    const int wn = wave / WMT, wm = wave % WMT;
     const uint32_t ra = ring0 + wn * 8 * 1024 + lofs;
     const uint32_t rb = ring0 + (kFa + wm * WB) * 1024 + lofs;
+    const bool late_copy = NW == 8 && wn == 1;           // copies after the first k half
 
-    v16i acc[4][WJ];
+    v16i acc[4][JB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < WJ; ++j) acc[i][j] = v16i{};
+        for (int j = 0; j < JB; ++j) acc[i][j] = v16i{};
 
     // stages 0 .. NS - 1 into the ring, one stage per fenced group
 #pragma unroll
@@ -220,24 +254,28 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
     // stage (g = nkb - 1) and reads and copies nothing.
     auto step = [&](int g, TlFrags<WB>& cur, TlFrags<WB>& nxt, bool tail) {
         tl_wait<WB>(cur);
-        if (!tail && g + 1 < nkb) {
+        const bool more = !tail && g + 1 < nkb;
+        if (more) {
             wait_vmcnt<(NS - 2) * kOps>();               // own copies of stage g + 1
             stage_barrier();                             // stage g + 1 published; stage g read by all
-            put(g + NS);                                 // into the slot of stage g
+            if (!late_copy) put(g + NS);                 // into the slot of stage g
             __atomic_signal_fence(__ATOMIC_SEQ_CST);     // this stage's copies stay in it
             const uint32_t so = (uint32_t)(((g + 1) % NS) * kStage);
             tl_issue<WB>(nxt, ra + so, rb + so);
         }
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int kh = 0; kh < 2; ++kh) {
+            if (kh == 1 && more && late_copy) put(g + NS);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < WJ; ++j)
+                for (int j = 0; j < JB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[2 * i + kh], cur.b[2 * j + kh],
                                                                      acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
     int g = 0;
     for (; g + 1 < nkb; g += 2) {                        // the same registers every pass
@@ -257,10 +295,8 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
     if (!split) {
         stage_barrier();                                 // every wave is done with the ring
         const int t = (int)threadIdx.x;
-        const float wv = P.ws[min(n0 + t, P.N - 1)];
-        const float xv = t < 64 * WJ ? P.xs[min(t0 + t, P.M - 1)] : 0.0f;
-        sws[t] = wv;
-        if (t < 64 * WJ) sxs[t] = xv;
+        if (t < 256) sws[t] = P.ws[min(n0 + t, P.N - 1)];
+        if (t < 64 * WJ) sxs[t] = P.xs[min(t0 + t, P.M - 1)];
         __syncthreads();
     }
     const bool pv4 = split && ((P.acc_ld & 3) == 0) && ((P.acc_split & 3) == 0);
@@ -276,8 +312,8 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
             float4 w4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             if (!split) w4 = *reinterpret_cast<const float4*>(sws + nl);
 #pragma unroll
-            for (int j = 0; j < WJ; ++j) {
-                const int tl = wm * 32 * WJ + 32 * j + lrow;                 // token in the tile
+            for (int j = 0; j < JB; ++j) {
+                const int tl = wm * 32 * JB + 32 * j + lrow;                 // token in the tile
                 const int t = t0 + tl;
                 if (t >= P.M) continue;
                 const v4i a = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
@@ -325,22 +361,25 @@ __device__ __forceinline__ int xcd_tile(int per_xcd)
     return ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
 }
 
+// Waves per tiled workgroup (see tiled_block).
+constexpr int kTiledWaves = 8;
+
 // A work unit is (tile, K split), splits fastest.
 template <int WJ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * kTiledWaves) __attribute__((amdgpu_waves_per_eu(kTiledWaves / 4, kTiledWaves / 4)))
 void k_gemm_tiled(GemmSet set, int per_xcd)
 {
     const int j = xcd_tile(per_xcd);
     if (j >= set.total_tiles) return;
     const GemmProb P = find_prob(set, j);
     const int u = j - P.tile_begin;
-    tiled_block<WJ>(P, u / P.splits, u % P.splits);
+    tiled_block<WJ, kTiledWaves>(P, u / P.splits, u % P.splits);
 }
 
 // Stack step: with S.partials the K range is split S.splits ways and each unit
 // writes its int32 partial tile to the pair's partial buffer.
 template <int WJ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * kTiledWaves) __attribute__((amdgpu_waves_per_eu(kTiledWaves / 4, kTiledWaves / 4)))
 void k_gemm_tiled_step(StackStep S, int per_xcd)
 {
     const int j = xcd_tile(per_xcd);
@@ -354,7 +393,7 @@ void k_gemm_tiled_step(StackStep S, int per_xcd)
         P.acc_ld = S.ldp;
         P.acc_split = S.part_stride;
     }
-    tiled_block<WJ>(P, local, j % S.splits);
+    tiled_block<WJ, kTiledWaves>(P, local, j % S.splits);
 }
 
 int tiled_tokens(int64_t M) { return M > 128 ? 256 : 128; }
@@ -363,7 +402,7 @@ hipError_t launch_gemm_tiled(const GemmSet& set, int64_t M, hipStream_t s)
 {
     if (set.total_tiles <= 0) return hipSuccess;
     const int per_xcd = (set.total_tiles + 7) / 8;
-    const dim3 g(8 * per_xcd), b(256);
+    const dim3 g(8 * per_xcd), b(64 * kTiledWaves);
     if (tiled_tokens(M) == 256) PF_LAUNCH((k_gemm_tiled<4>), g, b, 0, s, set, per_xcd);
     else PF_LAUNCH((k_gemm_tiled<2>), g, b, 0, s, set, per_xcd);
     const hipError_t e = hipGetLastError();
@@ -377,7 +416,7 @@ hipError_t launch_gemm_tiled_step(const StackStep& S, int64_t M, hipStream_t s)
     const int tiles = S.npairs * S.tile_off[S.nproj] * S.splits;
     if (tiles <= 0) return hipSuccess;
     const int per_xcd = (tiles + 7) / 8;
-    const dim3 g(8 * per_xcd), b(256);
+    const dim3 g(8 * per_xcd), b(64 * kTiledWaves);
     if (tiled_tokens(M) == 256) PF_LAUNCH((k_gemm_tiled_step<4>), g, b, 0, s, S, per_xcd);
     else PF_LAUNCH((k_gemm_tiled_step<2>), g, b, 0, s, S, per_xcd);
     return hipGetLastError();
