@@ -146,9 +146,10 @@ hipError_t launch_gemm_tiled_step(const StackStep& S, int64_t M, hipStream_t s);
 hipError_t launch_gemm_stream(const StackStep& S, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_xres(const StackStep& S, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t s);
-hipError_t launch_gemm_tiled(const GemmSet& set, int64_t M, hipStream_t s);
+hipError_t launch_gemm_tiled(const GemmSet& set, int tile_tokens, hipStream_t s);
 hipError_t launch_split_reduce(const GemmSet& set, hipStream_t s);
-// Tiled product tiles: 256 weight rows x tiled_tokens(M) tokens.
+// Tiled product tiles: 256 weight rows x 256 or 128 tokens; tiled_tokens(M) is
+// the stack sweep's choice (pf_gemm_i8_chunk plans its own).
 constexpr int kTiledRows = 256;
 int tiled_tokens(int64_t M);
 

@@ -398,12 +398,13 @@ void k_gemm_tiled_step(StackStep S, int per_xcd)
 
 int tiled_tokens(int64_t M) { return M > 128 ? 256 : 128; }
 
-hipError_t launch_gemm_tiled(const GemmSet& set, int64_t M, hipStream_t s)
+hipError_t launch_gemm_tiled(const GemmSet& set, int tile_tokens, hipStream_t s)
 {
     if (set.total_tiles <= 0) return hipSuccess;
+    if (tile_tokens != 256 && tile_tokens != 128) return hipErrorInvalidValue;
     const int per_xcd = (set.total_tiles + 7) / 8;
     const dim3 g(8 * per_xcd), b(64 * kTiledWaves);
-    if (tiled_tokens(M) == 256) PF_LAUNCH((k_gemm_tiled<4>), g, b, 0, s, set, per_xcd);
+    if (tile_tokens == 256) PF_LAUNCH((k_gemm_tiled<4>), g, b, 0, s, set, per_xcd);
     else PF_LAUNCH((k_gemm_tiled<2>), g, b, 0, s, set, per_xcd);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
