@@ -7,6 +7,7 @@
 // No host round trip: the expert plan stays in device memory.
 #include "device.hpp"
 #include "kernels.hpp"
+#include "lds_dma.hpp"
 
 namespace pf {
 
@@ -463,9 +464,175 @@ __global__ __launch_bounds__(256) void k_expert(ExpertArgs A)
     }
 }
 
+// Streaming form for K = 64 KB.  Workgroup = (expert e, band of 64 RB weight
+// rows; with two weights, 64 rows of each).  Per token group of up to 32:
+// the group's token rows are copied once into LDS, as 1 KB fragments (token
+// block tb, k-block kb) laid out as the MFMA B operand wants them.  Each wave
+// then streams its weight rows straight into registers: RB row blocks of 16
+// rows one after the other, each over all KB k-blocks, D fragments (16 rows x
+// 64 bytes of each weight) ahead across row-block boundaries, with no barrier
+// inside the stream.  The stream is unrolled, so every ring slot and wait is
+// fixed at compile time.
+template <bool kPair, int RB, int D, int KB>
+__global__ __launch_bounds__(256) void k_expert_stream(ExpertArgs A)
+{
+    constexpr int M = kPair ? 2 : 1;              // weights read per fragment
+    constexpr int NF = RB * KB;                   // fragments per wave
+    static_assert(D <= NF, "ring within the stream");
+    __shared__ __attribute__((aligned(16))) int8_t xl[2 * KB * 1024];
+    __shared__ int rows[32];
+    const int e = blockIdx.x / A.tiles_n, tn = blockIdx.x % A.tiles_n;
+    const int p0 = A.off[e], p1 = A.off[e + 1];
+    if (p0 == p1) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int koff = (lane >> 4) << 4;
+    const int r0 = tn * 64 * RB + wave * 16 * RB; // this wave's first weight row
+    // weight pointers of row block 0 (row clamped into the matrix; rows past
+    // N are never stored); row block rb is rb * 16 rows further
+    const int8_t* wp[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        wp[m] = (kPair && m == 1 ? A.W1 : A.W0) + (int64_t)e * A.N * A.K + koff;
+    auto frag = [&](int m, int f) {               // fragment f = (rb, kb) of weight m
+        const int rb = f / KB, kb = f % KB;
+        const int row = min(r0 + rb * 16 + (lane & 15), A.N - 1);
+        return ld16(wp[m] + (int64_t)row * A.K + kb * 64);
+    };
+
+    for (int g0 = p0; g0 < p1; g0 += 32) {
+        const int gm = min(32, p1 - g0);
+        __syncthreads();                           // the previous group's LDS reads are done
+        if (threadIdx.x < 32)
+            rows[threadIdx.x] = (int)threadIdx.x < gm
+                                    ? (A.gather ? A.gather[g0 + threadIdx.x] : g0 + threadIdx.x)
+                                    : -1;
+        __syncthreads();
+        // the epilogues' scales, loaded before the stream (a load issued inside
+        // it would be waited for together with every weight load before it)
+        float xsv[2], ws0[RB][4], ws1[RB][4];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const int j = tb * 16 + (lane & 15);
+            xsv[tb] = A.xs[rows[j] >= 0 ? rows[j] : rows[0]];
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = min(r0 + rb * 16 + ((lane >> 4) << 2) + q, A.N - 1);
+                ws0[rb][q] = A.s0[(int64_t)e * A.N + n];
+                if (kPair) ws1[rb][q] = A.s1[(int64_t)e * A.N + n];
+            }
+        // token fragments: (tb, kb) at (tb * KB + kb) KB; lane l brings token
+        // (l & 15) of the block, bytes (l >> 4) * 16 .. + 15 of the k-block;
+        // wave w brings fragments w, w + 4, ...  Token slots past the group
+        // read row rows[0] and are never stored.  Loaded into registers first,
+        // then the first D weight fragments are issued, so both are in flight
+        // together.
+        v4i xv[2 * KB / 4];
+        {
+            const int rl = rows[lane & 15], rh = rows[16 + (lane & 15)];
+            const int8_t* x0 = A.X + (int64_t)(rl >= 0 ? rl : rows[0]) * A.ldx + koff;
+            const int8_t* x1 = A.X + (int64_t)(rh >= 0 ? rh : rows[0]) * A.ldx + koff;
+#pragma unroll
+            for (int i = 0; i < 2 * KB / 4; ++i) {
+                const int f = wave + 4 * i;
+                xv[i] = ld16(f < KB ? x0 + (int64_t)f * 64 : x1 + (int64_t)(f - KB) * 64);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        v4i ring[D][M];
+#pragma unroll
+        for (int f = 0; f < D; ++f)
+#pragma unroll
+            for (int m = 0; m < M; ++m) ring[f][m] = frag(m, f);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 2 * KB / 4; ++i) st16(xl + (wave + 4 * i) * 1024 + lane * 16, xv[i]);
+        // the LDS writes are complete (lgkmcnt 0; the loads stay in flight),
+        // then every wave's are visible after the barrier
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        stage_barrier();
+
+        v4i acc[M][2];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const int rb = f / KB, kb = f % KB;
+            if (kb == 0) {
+#pragma unroll
+                for (int m = 0; m < M; ++m) acc[m][0] = acc[m][1] = v4i{0, 0, 0, 0};
+            }
+            const v4i b0 = *reinterpret_cast<const v4i*>(xl + kb * 1024 + lane * 16);
+            const v4i b1 = *reinterpret_cast<const v4i*>(xl + (KB + kb) * 1024 + lane * 16);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                acc[m][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ring[f % D][m], b0, acc[m][0], 0, 0, 0);
+                acc[m][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ring[f % D][m], b1, acc[m][1], 0, 0, 0);
+            }
+            if (f + D < NF) {
+#pragma unroll
+                for (int m = 0; m < M; ++m) ring[f % D][m] = frag(m, f + D);
+            }
+            __builtin_amdgcn_sched_barrier(0);     // keep each refill D fragments ahead of its use
+            if (kb == KB - 1) {
+                // epilogue of row block rb: acc[m][tb][q] is weight row
+                // r0 + rb * 16 + (lane >> 4) * 4 + q, token tb * 16 + (lane & 15)
+                const int nr = r0 + rb * 16 + ((lane >> 4) << 2);
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    const int j = tb * 16 + (lane & 15);
+                    if (j >= gm) continue;
+                    float* yrow = A.Y + (int64_t)(g0 + j) * A.ldy;
+                    float4 v;
+                    float* vp = &v.x;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float g = epilogue(acc[0][tb][q], ws0[rb][q], xsv[tb]);
+                        if (kPair) {
+                            const float u = epilogue(acc[M - 1][tb][q], ws1[rb][q], xsv[tb]);
+                            vp[q] = g * u;
+                        } else {
+                            vp[q] = g;
+                        }
+                    }
+                    if (nr + 3 < A.N) {
+                        *reinterpret_cast<float4*>(yrow + nr) = v;
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 3; ++q)
+                            if (nr + q < A.N) yrow[nr + q] = vp[q];
+                    }
+                }
+            }
+        }
+    }
+}
+
+// The streaming form for K of 512, 1024 or 2048 and 16-byte aligned output
+// rows; the piecewise form otherwise.
 hipError_t launch_expert(const ExpertArgs& a, hipStream_t s)
 {
-    const dim3 g(a.E * a.tiles_n), b(256);
+    const dim3 b(256);
+    const bool aligned = a.ldy % 4 == 0 && (reinterpret_cast<uintptr_t>(a.Y) & 15) == 0;
+    if (aligned && (a.K == 512 || a.K == 1024 || a.K == 2048)) {
+        // gate/up: 64 rows of each weight per workgroup; down: 64 RB rows, RB = 4
+        // (2 at K = 2048), so that a wave streams 32 to 64 fragments
+        ExpertArgs c = a;
+        const int rb = a.W1 ? 1 : (a.K == 2048 ? 2 : 4);
+        c.tiles_n = (a.N + 64 * rb - 1) / (64 * rb);
+        const dim3 g(a.E * c.tiles_n);
+        if (a.W1) {
+            if (a.K == 512) PF_LAUNCH((k_expert_stream<true, 1, 8, 8>), g, b, 0, s, c);
+            else if (a.K == 1024) PF_LAUNCH((k_expert_stream<true, 1, 8, 16>), g, b, 0, s, c);
+            else PF_LAUNCH((k_expert_stream<true, 1, 8, 32>), g, b, 0, s, c);
+        } else {
+            if (a.K == 512) PF_LAUNCH((k_expert_stream<false, 4, 16, 8>), g, b, 0, s, c);
+            else if (a.K == 1024) PF_LAUNCH((k_expert_stream<false, 4, 16, 16>), g, b, 0, s, c);
+            else PF_LAUNCH((k_expert_stream<false, 2, 16, 32>), g, b, 0, s, c);
+        }
+        return hipGetLastError();
+    }
+    const dim3 g(a.E * a.tiles_n);
     if (a.W1) PF_LAUNCH(k_expert<true>, g, b, 0, s, a);
     else PF_LAUNCH(k_expert<false>, g, b, 0, s, a);
     return hipGetLastError();

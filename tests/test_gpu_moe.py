@@ -44,6 +44,17 @@ def test_small_moe_matches_oracle(E, k, H, I, T):
     check(prefill_inputs.moe(E, k, H, I, T, seed=E + T))
 
 
+# Shapes for the streaming expert kernel (K of 512, 1024 or 2048 in both
+# products): expert groups over 32 tokens (150 tokens, top-2 of 8), a down
+# projection whose 576 output rows end inside a 256-row band (its gate/up,
+# K = 576, take the piecewise kernel), and K = 2048 in both products.
+@pytest.mark.parametrize("E,k,H,I,T", [(16, 4, 512, 1024, 70), (8, 2, 1024, 512, 150),
+                                       (8, 2, 576, 512, 40), (4, 1, 2048, 2048, 33)])
+def test_streaming_expert_shapes_match_oracle(E, k, H, I, T):
+    print(f"moe E={E} k={k} H={H} I={I} T={T}", file=sys.stderr, flush=True)
+    check(prefill_inputs.moe(E, k, H, I, T, seed=100 + E + T))
+
+
 def test_moe_concentrated_routing():
     # A router with one dominant expert sends every token to the same experts:
     # groups larger than 32 tokens take the multi-group path.
