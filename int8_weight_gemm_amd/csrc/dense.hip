@@ -116,6 +116,93 @@ __device__ __forceinline__ void rebuild_row(const QuantPair& P, int t, int K)
     }
 }
 
+// A row of at most 1024 U values with the values held in registers (U
+// float4 pieces per thread, pieces i = threadIdx.x + 256 u): every load of the
+// row is issued before any is used (the split partials four splits at a
+// time), and the codes come from the registers, so the row is read once.
+// Same arithmetic as rebuild_row followed by quantize_row.
+template <int U>
+__device__ __forceinline__ void quant_row_regs(const QuantPair& P, int t, int K)
+{
+    const int n4 = K >> 2;
+    int idx[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) idx[u] = min((int)threadIdx.x + 256 * u, n4 - 1);
+    float4 v[U];
+    if (P.part) {
+        const int4* prow = reinterpret_cast<const int4*>(P.part + (int64_t)t * K);
+        const int64_t sstride = P.part_stride / 4;
+        int4 a[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[u] = prow[idx[u]];
+        for (int sp0 = 1; sp0 < P.splits; sp0 += 4) {
+            int4 w[U][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t off = (int64_t)min(sp0 + j, P.splits - 1) * sstride;
+#pragma unroll
+                for (int u = 0; u < U; ++u) w[u][j] = prow[idx[u] + off];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (sp0 + j < P.splits)
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        a[u].x += w[u][j].x; a[u].y += w[u][j].y; a[u].z += w[u][j].z; a[u].w += w[u][j].w;
+                    }
+        }
+        const float as = P.as[t];
+        float4* hrow = reinterpret_cast<float4*>(P.h + (int64_t)t * P.ldh);
+        float* yrow = P.y ? P.y + (int64_t)t * K : nullptr;    // 4-byte aligned only
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = (int)threadIdx.x + 256 * u;
+            const float* ws = P.ws + 4 * idx[u];
+            v[u].x = epilogue(a[u].x, ws[0], as);
+            v[u].y = epilogue(a[u].y, ws[1], as);
+            v[u].z = epilogue(a[u].z, ws[2], as);
+            v[u].w = epilogue(a[u].w, ws[3], as);
+            if (i < n4) {
+                hrow[i] = v[u];
+                if (yrow) {
+                    yrow[4 * i] = v[u].x;
+                    yrow[4 * i + 1] = v[u].y;
+                    yrow[4 * i + 2] = v[u].z;
+                    yrow[4 * i + 3] = v[u].w;
+                }
+            }
+        }
+        if (!P.q) return;
+    } else {
+        const float4* row = reinterpret_cast<const float4*>(P.src + (int64_t)t * P.ld);
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = row[idx[u]];
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if ((int)threadIdx.x + 256 * u < n4)
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
+    amax = wave_max(amax);
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = amax / 127.0f;
+    if (threadIdx.x == 0) P.s[t] = s;
+    int* qrow = reinterpret_cast<int*>(P.q + (int64_t)t * K);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = (int)threadIdx.x + 256 * u;
+        if (i >= n4) continue;
+        int packed = 0;
+        if (s != 0.0f)
+            packed = (quant_code(v[u].x, s) & 0xff) | ((quant_code(v[u].y, s) & 0xff) << 8) |
+                     ((quant_code(v[u].z, s) & 0xff) << 16) | ((quant_code(v[u].w, s) & 0xff) << 24);
+        qrow[i] = packed;
+    }
+}
+
 __global__ __launch_bounds__(256) void k_quantize_step(QuantStep S)
 {
     const int bid = blockIdx.x;
@@ -125,6 +212,10 @@ __global__ __launch_bounds__(256) void k_quantize_step(QuantStep S)
         if (q < S.npairs && bid >= S.pair[q].row0) pi = q;
     const QuantPair& P = S.pair[pi];
     const int t = bid - P.row0;
+    const int n4 = S.K >> 2;
+    if (n4 <= 256) return quant_row_regs<1>(P, t, S.K);
+    if (n4 <= 512) return quant_row_regs<2>(P, t, S.K);
+    if (n4 <= 1024) return quant_row_regs<4>(P, t, S.K);
     if (P.part) {
         rebuild_row(P, t, S.K);
         if (!P.q) return;
