@@ -189,11 +189,59 @@ void finish_set(GemmSet& set, int kind)  // kind 0 gemv, 1 skinny, 2 tiled
     set.total_tiles = begin;
 }
 
+// One skinny problem through the token-resident kernel: the same work items
+// (64-row tiles x K splits of at most 16 k-blocks); with a split its int32
+// partials go to the problem's accumulator and k_split_reduce applies the
+// epilogue.  Needs 16-byte aligned output rows (four-row stores).
+bool xres_fits_shape(int64_t N, const float* y)
+{
+    return (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+}
+
+bool xres_fits(const GemmProb& g)
+{
+    return g.kb_per_split <= 16 && (g.N & 3) == 0 && ((reinterpret_cast<uintptr_t>(g.Y) & 15) == 0) &&
+           (g.ldy & 3) == 0 && !g.Y2;
+}
+
+pf_status run_skinny_xres(GemmSet& set, int64_t M, hipStream_t s)
+{
+    const GemmProb& g = set.p[0];
+    StackStep S;
+    std::memset(&S, 0, sizeof(S));
+    S.npairs = 1;
+    S.nproj = 1;
+    S.K = g.K;
+    S.rows[0] = g.N;
+    S.tile_off[1] = (g.N + kSkinnyRows - 1) / kSkinnyRows;
+    S.tiles_m = 1;
+    S.splits = g.splits;
+    S.partials = g.splits > 1 ? 1 : 0;
+    S.kb_per_split = g.kb_per_split;
+    S.ldx = g.ldx;
+    S.ldy = g.ldy;
+    S.ldp = g.acc_ld;
+    S.part_stride = g.acc_split;
+    StepPair& p = S.pair[0];
+    p.W[0] = g.W;
+    p.ws[0] = g.ws;
+    p.X = g.X;
+    p.xs = g.xs;
+    p.Y = g.Y;
+    p.part = g.acc;
+    p.M = g.M;
+    if (pf_status st = launched(launch_gemm_xres(S, token_blocks(M), s))) return st;
+    if (g.splits <= 1) return PF_OK;
+    finish_set(set, 1);
+    return launched(launch_split_reduce(set, s));
+}
+
 // Runs a set of products that share M (skinny for M <= 64, tiled above, with
 // tiles of `tile_tokens` tokens).
 pf_status run_products(GemmSet& set, int64_t M, int tile_tokens, hipStream_t s)
 {
     if (M <= 64) {
+        if (set.nprob == 1 && xres_fits(set.p[0])) return run_skinny_xres(set, M, s);
         finish_set(set, 1);
         return launched(launch_gemm_skinny(set, token_blocks(M), s));
     }
@@ -836,6 +884,15 @@ pf_status pf_gemm_i8_chunk(const int8_t* W, const float* w_scale, int64_t N, int
         int tile_tokens = 0;
         if (M <= 64) {
             SkinnyPlan p = plan_skinny(N, K, (N + kSkinnyRows - 1) / kSkinnyRows);
+            // a product of at most a few MB is over before a second launch (the
+            // split's reduction) would start: split only as far as the
+            // token-resident kernel needs (16 k-blocks per split)
+            if (N * K <= (8 << 20) && xres_fits_shape(N, y)) {
+                const int nkb = (int)(K / 64);
+                const int sp = (nkb + 15) / 16;
+                p.kb_per_split = (nkb + sp - 1) / sp;
+                p.splits = (nkb + p.kb_per_split - 1) / p.kb_per_split;
+            }
             if (!workspace || ws_bytes < split_bytes(N, M, p)) p = unsplit(N, K);
             if (workspace && overlap(workspace, ws_bytes, y, yb)) return PF_EINVAL;
             char* scratch = static_cast<char*>(workspace);
