@@ -405,7 +405,17 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int wg_per_group
     const int ksb = S.kb_per_split;                     // <= kKsMax
     const int ppi = (ksb + KP - 1) / KP;                // stages per item
     const int total = (i1 - i0) * ppi;
-    const int koff = (lane >> 4) << 4;
+    // Copies take a fragment as 16 rows x 64 bytes with lane l on row l / 4,
+    // so that four consecutive lanes read one row's 64 contiguous bytes (the
+    // address unit serves that ~2.5x faster than one 16-byte piece of each of
+    // 16 rows per lane group).  Lane l fetches row r = l / 4, piece
+    // (l % 4) ^ ((r / 2) % 4), and lands at 16 l: piece c of row r sits at
+    // 64 r + 16 (c ^ ((r / 2) % 4)).  The MFMA operand of lane l (row l % 16,
+    // piece l / 16) is then at `lofs`, and the reads of 8 consecutive lanes hit
+    // 8 different 16-byte bank groups.
+    const int crow = lane >> 2;                         // row (or token) this lane copies
+    const int koff = ((lane & 3) ^ ((lane >> 3) & 3)) << 4;
+    const uint32_t lofs = (uint32_t)((lane & 15) * 64 + (((lane >> 4) ^ ((lane >> 1) & 3)) << 4));
     int8_t* myring = ring[wave];
 
     // ---- token slice of (pair, split) into LDS: fragment (tb, i) at (tb*kKsMax + i) KB
@@ -416,7 +426,7 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int wg_per_group
 #pragma unroll
         for (int u = 0; u < kXPerWave; ++u) {
             const int q = wave + 4 * u, tb = q / kKsMax, i = q % kKsMax;
-            const int tok = tb * 16 + (lane & 15);
+            const int tok = tb * 16 + crow;
             const int kb = min(kb0 + i, kbl);
             dma16(pp.X + (int64_t)(tok < pp.M ? tok : 0) * S.ldx + (int64_t)kb * 64 + koff,
                   xl + q * 1024);
@@ -438,8 +448,8 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int wg_per_group
             const StepPair& pp = S.pair[it.pair];
             const int N = S.rows[it.proj];
             const int row0 = it.local * 64 + wave * 16;
-            iw = pp.W[it.proj] + (int64_t)min(row0 + (lane & 15), N - 1) * S.K + koff;
-            isc = pp.ws[it.proj] + min(row0 + (lane & 15), N - 1);
+            iw = pp.W[it.proj] + (int64_t)min(row0 + crow, N - 1) * S.K + koff;
+            isc = pp.ws[it.proj] + min(row0 + (lane & 15), N - 1);    // scale l at 4 l
             ikb0 = it.split * ksb;
             ikbl = min(ikb0 + ksb, nkb) - 1;
         }
@@ -482,7 +492,7 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int wg_per_group
         // all KP k-blocks are read (k-blocks past the split's end hold clamped
         // copies); only the first npc enter the product
         StageFrags<TB, KP> f;
-        lds_stage<TB, KP>(f, slot + lane * 16, lds_addr(xl) + ks0 * 1024 + lane * 16);
+        lds_stage<TB, KP>(f, slot + lofs, lds_addr(xl) + ks0 * 1024 + lofs);
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
             if (i < npc) {
