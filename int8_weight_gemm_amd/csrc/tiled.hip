@@ -10,12 +10,14 @@
 //    owns 128 rows x 32 WJ tokens: 4 x WJ accumulator blocks of 32 x 32 in
 //    AGPRs;
 //  * a stage is one k-block (64 bytes of K) of the tile's weight rows and
-//    tokens in LDS as 1 KB fragments of 16 rows x 64 bytes (lane l's 16 bytes,
-//    row l % 16 and bytes 16 (l / 16) .. + 15, at 16 l), so every copy reads 16
-//    rows x 64 contiguous bytes; the MFMA operands are read from it with one
-//    conflict-free ds_read_b128 each; a ring of four stages, one barrier per
-//    stage, and the reads of stage g + 1 are in flight while the MFMAs of
-//    stage g run;
+//    tokens in LDS as 1 KB fragments of 16 rows x 64 bytes.  A copy gives four
+//    consecutive lanes one row's 64 contiguous bytes (lane l: row l / 4), the
+//    order in which the address unit serves a fragment ~2.5x faster than one
+//    16-byte piece of each of 16 rows per lane group; lane l lands at 16 l, so
+//    piece c of row r sits at 64 r + 16 (c ^ ((r / 2) % 4)), and the MFMA
+//    operands are read with one conflict-free ds_read_b128 each; a ring of
+//    four stages, one barrier per stage, and the reads of stage g + 1 are in
+//    flight while the MFMAs of stage g run;
 //  * every fragment, weights and tokens, is copied by global_load_lds_dwordx4,
 //    three stages ahead.  (Weights through registers and ds_write_b128 issue
 //    about twice as slowly per fragment.)  The copies of a stage take the
@@ -45,54 +47,54 @@ struct TlFrags {
 
 // Issue the wave's LDS reads of one stage without waiting; tl_wait waits for
 // them.  Operand q = 2 i + kh (32-row block i, k half kh) is read at
-// a + 2 KB i + 512 kh (weights) or b + 2 KB i + 512 kh (tokens), a and b
-// carrying the lane's own offset in the block.  The wait names every
+// a_kh + 2 KB i (weights) or b_kh + 2 KB i (tokens), a_kh and b_kh carrying
+// the lane's own offset in the block for k half kh.  The wait names every
 // destination register, so no use of one can be placed before it.
 template <int WM>
-__device__ __forceinline__ void tl_issue(TlFrags<WM>& f, uint32_t a, uint32_t b);
+__device__ __forceinline__ void tl_issue(TlFrags<WM>& f, uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1);
 template <int WM>
 __device__ __forceinline__ void tl_wait(TlFrags<WM>& f);
 
 template <>
-__device__ __forceinline__ void tl_issue<4>(TlFrags<4>& f, uint32_t a, uint32_t b)
+__device__ __forceinline__ void tl_issue<4>(TlFrags<4>& f, uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1)
 {
     asm volatile(
         "ds_read_b128 %0, %12 offset:0\n"
-        "ds_read_b128 %1, %12 offset:512\n"
+        "ds_read_b128 %1, %13 offset:0\n"
         "ds_read_b128 %2, %12 offset:2048\n"
-        "ds_read_b128 %3, %12 offset:2560\n"
+        "ds_read_b128 %3, %13 offset:2048\n"
         "ds_read_b128 %4, %12 offset:4096\n"
-        "ds_read_b128 %5, %12 offset:4608\n"
+        "ds_read_b128 %5, %13 offset:4096\n"
         "ds_read_b128 %6, %12 offset:6144\n"
-        "ds_read_b128 %7, %12 offset:6656\n"
-        "ds_read_b128 %8, %13 offset:0\n"
-        "ds_read_b128 %9, %13 offset:512\n"
-        "ds_read_b128 %10, %13 offset:2048\n"
-        "ds_read_b128 %11, %13 offset:2560\n"
+        "ds_read_b128 %7, %13 offset:6144\n"
+        "ds_read_b128 %8, %14 offset:0\n"
+        "ds_read_b128 %9, %15 offset:0\n"
+        "ds_read_b128 %10, %14 offset:2048\n"
+        "ds_read_b128 %11, %15 offset:2048\n"
         : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.a[2]), "=&v"(f.a[3]),
           "=&v"(f.a[4]), "=&v"(f.a[5]), "=&v"(f.a[6]), "=&v"(f.a[7]),
           "=&v"(f.b[0]), "=&v"(f.b[1]), "=&v"(f.b[2]), "=&v"(f.b[3])
-        : "v"(a), "v"(b));
+        : "v"(a0), "v"(a1), "v"(b0), "v"(b1));
 }
 
 template <>
-__device__ __forceinline__ void tl_issue<2>(TlFrags<2>& f, uint32_t a, uint32_t b)
+__device__ __forceinline__ void tl_issue<2>(TlFrags<2>& f, uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1)
 {
     asm volatile(
         "ds_read_b128 %0, %10 offset:0\n"
-        "ds_read_b128 %1, %10 offset:512\n"
+        "ds_read_b128 %1, %11 offset:0\n"
         "ds_read_b128 %2, %10 offset:2048\n"
-        "ds_read_b128 %3, %10 offset:2560\n"
+        "ds_read_b128 %3, %11 offset:2048\n"
         "ds_read_b128 %4, %10 offset:4096\n"
-        "ds_read_b128 %5, %10 offset:4608\n"
+        "ds_read_b128 %5, %11 offset:4096\n"
         "ds_read_b128 %6, %10 offset:6144\n"
-        "ds_read_b128 %7, %10 offset:6656\n"
-        "ds_read_b128 %8, %11 offset:0\n"
-        "ds_read_b128 %9, %11 offset:512\n"
+        "ds_read_b128 %7, %11 offset:6144\n"
+        "ds_read_b128 %8, %12 offset:0\n"
+        "ds_read_b128 %9, %13 offset:0\n"
         : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.a[2]), "=&v"(f.a[3]),
           "=&v"(f.a[4]), "=&v"(f.a[5]), "=&v"(f.a[6]), "=&v"(f.a[7]),
           "=&v"(f.b[0]), "=&v"(f.b[1])
-        : "v"(a), "v"(b));
+        : "v"(a0), "v"(a1), "v"(b0), "v"(b1));
 }
 
 template <>
@@ -114,30 +116,30 @@ __device__ __forceinline__ void tl_wait<4>(TlFrags<4>& f)
 }
 
 template <>
-__device__ __forceinline__ void tl_issue<8>(TlFrags<8>& f, uint32_t a, uint32_t b)
+__device__ __forceinline__ void tl_issue<8>(TlFrags<8>& f, uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1)
 {
     asm volatile(
         "ds_read_b128 %0, %16 offset:0\n"
-        "ds_read_b128 %1, %16 offset:512\n"
+        "ds_read_b128 %1, %17 offset:0\n"
         "ds_read_b128 %2, %16 offset:2048\n"
-        "ds_read_b128 %3, %16 offset:2560\n"
+        "ds_read_b128 %3, %17 offset:2048\n"
         "ds_read_b128 %4, %16 offset:4096\n"
-        "ds_read_b128 %5, %16 offset:4608\n"
+        "ds_read_b128 %5, %17 offset:4096\n"
         "ds_read_b128 %6, %16 offset:6144\n"
-        "ds_read_b128 %7, %16 offset:6656\n"
-        "ds_read_b128 %8, %17 offset:0\n"
-        "ds_read_b128 %9, %17 offset:512\n"
-        "ds_read_b128 %10, %17 offset:2048\n"
-        "ds_read_b128 %11, %17 offset:2560\n"
-        "ds_read_b128 %12, %17 offset:4096\n"
-        "ds_read_b128 %13, %17 offset:4608\n"
-        "ds_read_b128 %14, %17 offset:6144\n"
-        "ds_read_b128 %15, %17 offset:6656\n"
+        "ds_read_b128 %7, %17 offset:6144\n"
+        "ds_read_b128 %8, %18 offset:0\n"
+        "ds_read_b128 %9, %19 offset:0\n"
+        "ds_read_b128 %10, %18 offset:2048\n"
+        "ds_read_b128 %11, %19 offset:2048\n"
+        "ds_read_b128 %12, %18 offset:4096\n"
+        "ds_read_b128 %13, %19 offset:4096\n"
+        "ds_read_b128 %14, %18 offset:6144\n"
+        "ds_read_b128 %15, %19 offset:6144\n"
         : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.a[2]), "=&v"(f.a[3]),
           "=&v"(f.a[4]), "=&v"(f.a[5]), "=&v"(f.a[6]), "=&v"(f.a[7]),
           "=&v"(f.b[0]), "=&v"(f.b[1]), "=&v"(f.b[2]), "=&v"(f.b[3]),
           "=&v"(f.b[4]), "=&v"(f.b[5]), "=&v"(f.b[6]), "=&v"(f.b[7])
-        : "v"(a), "v"(b));
+        : "v"(a0), "v"(a1), "v"(b0), "v"(b1));
 }
 
 template <>
@@ -189,23 +191,23 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
     // this split's k-blocks: kb0 .. kb0 + nkb - 1 (all of K when unsplit)
     const int kb0 = kidx * P.kb_per_split;
     const int nkb = min(P.kb_per_split, (P.K >> 6) - kb0);
-    // fragment f: rows (or tokens) 16 f .. + 15 of the k-block, lane l's 16
-    // bytes (row l % 16, bytes 16 (l / 16) .. + 15) at 16 l: each copy reads 16
-    // rows x 64 contiguous bytes.  Rows and tokens past the end repeat the last
-    // one; their results are never stored.
+    // fragment f: rows (or tokens) 16 f .. + 15 of the k-block; lane l copies
+    // row l / 4, piece (l % 4) ^ ((l / 8) % 4), to 16 l.  Rows and tokens past
+    // the end repeat the last one; their results are never stored.
     const int lrow = lane & 31;
-    const int kof = 16 * (lane >> 4);
+    const int crow = lane >> 2;                          // row this lane copies
+    const int kof = ((lane & 3) ^ ((lane >> 3) & 3)) << 4;
     const int8_t* asrc[ka];
 #pragma unroll
     for (int h = 0; h < ka; ++h) {
         const int f = wave + NW * h;
-        asrc[h] = P.W + (int64_t)min(n0 + 16 * f + (lane & 15), P.N - 1) * P.K + kof;
+        asrc[h] = P.W + (int64_t)min(n0 + 16 * f + crow, P.N - 1) * P.K + kof;
     }
     const int8_t* bsrc[kb];
 #pragma unroll
     for (int h = 0; h < kb; ++h) {
         const int f = wave + NW * h;
-        bsrc[h] = P.X + (int64_t)min(t0 + 16 * f + (lane & 15), P.M - 1) * P.ldx + kof;
+        bsrc[h] = P.X + (int64_t)min(t0 + 16 * f + crow, P.M - 1) * P.ldx + kof;
     }
     const uint32_t ring0 = lds_addr(ring);
 
@@ -221,13 +223,15 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
     };
 
     // The 32 x 32 x 32 operand of rows 32 i .. + 31, k half kh: lane l needs
-    // row l % 32, bytes 32 kh + 16 (l / 32) .. + 15, which sit in fragment
-    // 2 i + (l / 16) % 2 at 16 (l % 16 + 16 (2 kh + l / 32)).  Per 16-lane group
-    // the 16-byte reads are consecutive: no bank conflicts.
-    const uint32_t lofs = (uint32_t)(((lane >> 4) & 1) * 1024 + 16 * (lane & 15) + 256 * (lane >> 5));
+    // row r = l % 32, piece c = 2 kh + l / 32, which sits in fragment
+    // 2 i + r / 16 at 64 (r % 16) + 16 (c ^ ((r % 16 / 2) % 4)); for k half 1
+    // that is the half-0 offset with bit 5 flipped.  Any 8 consecutive lanes
+    // read 8 different 16-byte bank groups.
+    const uint32_t lofs = (uint32_t)(((lane >> 4) & 1) * 1024 + 64 * (lane & 15) +
+                                     16 * ((lane >> 5) ^ ((lane >> 1) & 3)));   // k half 0; half 1: ^ 32
     const int wn = wave / WMT, wm = wave % WMT;
-    const uint32_t ra = ring0 + wn * 8 * 1024 + lofs;
-    const uint32_t rb = ring0 + (kFa + wm * WB) * 1024 + lofs;
+    const uint32_t ra0 = ring0 + wn * 8 * 1024 + lofs, ra1 = ring0 + wn * 8 * 1024 + (lofs ^ 32);
+    const uint32_t rb0 = ring0 + (kFa + wm * WB) * 1024 + lofs, rb1 = ring0 + (kFa + wm * WB) * 1024 + (lofs ^ 32);
     const bool late_copy = NW == 8 && wn == 1;           // copies after the first k half
 
     v16i acc[4][JB];
@@ -245,7 +249,7 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
     wait_vmcnt<(NS - 1) * kOps>();                       // own copies of stage 0
     stage_barrier();
     TlFrags<WB> fr[2];
-    tl_issue<WB>(fr[0], ra, rb);
+    tl_issue<WB>(fr[0], ra0, ra1, rb0, rb1);
 
     // Iteration g: wait for stage g's operands (read in iteration g - 1) and
     // this wave's copies of stage g + 1; barrier (stage g + 1 published, stage
@@ -261,7 +265,7 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
             if (!late_copy) put(g + NS);                 // into the slot of stage g
             __atomic_signal_fence(__ATOMIC_SEQ_CST);     // this stage's copies stay in it
             const uint32_t so = (uint32_t)(((g + 1) % NS) * kStage);
-            tl_issue<WB>(nxt, ra + so, rb + so);
+            tl_issue<WB>(nxt, ra0 + so, ra1 + so, rb0 + so, rb1 + so);
         }
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
