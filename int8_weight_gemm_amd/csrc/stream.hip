@@ -47,7 +47,12 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StackStep S, int ntiles)
     const int nkb = S.K >> 6;
     const int spt = (nkb + KP - 1) / KP;         // stages per tile
     const int total = my_tiles * spt;
-    const int koff = (lane >> 4) << 4;
+    // copies: four consecutive lanes per row (lane l: row l / 4, piece
+    // (l % 4) ^ ((l / 8) % 4)); the operand of lane l (row l % 16, piece l / 16)
+    // is then at `lofs` in its fragment (conflict-free)
+    const int crow = lane >> 2;
+    const int koff = ((lane & 3) ^ ((lane >> 3) & 3)) << 4;
+    const int lofs = (lane & 15) * 64 + (((lane >> 4) ^ ((lane >> 1) & 3)) << 4);
 
     // ---- issue side: the tile whose stages are being loaded
     int itile = -1;
@@ -61,12 +66,12 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StackStep S, int ntiles)
             itile = t;
             int local;
             const GemmProb P = stream_prob(S, (int)blockIdx.x + t * G, local);
-            const int n = min(local * 64 + wave * 16 + (lane & 15), P.N - 1);
+            const int n = min(local * 64 + wave * 16 + crow, P.N - 1);
             iw = P.W + (int64_t)n * P.K + koff;
 #pragma unroll
             for (int u = 0; u < kXPerWave; ++u) {
                 const int q = wave + 4 * u, tb = q / KP;
-                const int tok = tb * 16 + (lane & 15);
+                const int tok = tb * 16 + crow;
                 ix[u] = P.X + (int64_t)(tok < P.M ? tok : 0) * P.ldx + koff;
             }
             if (wave == 0) isc = P.ws + min(local * 64 + lane, P.N - 1);
@@ -119,10 +124,10 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StackStep S, int ntiles)
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
             if (i < npc) {
-                const v4i a = *reinterpret_cast<const v4i*>(base + (wave * KP + i) * 1024 + lane * 16);
+                const v4i a = *reinterpret_cast<const v4i*>(base + (wave * KP + i) * 1024 + lofs);
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
-                    const v4i b = *reinterpret_cast<const v4i*>(base + kWBytes + (tb * KP + i) * 1024 + lane * 16);
+                    const v4i b = *reinterpret_cast<const v4i*>(base + kWBytes + (tb * KP + i) * 1024 + lofs);
                     acc[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[tb], 0, 0, 0);
                 }
             }

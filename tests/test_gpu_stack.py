@@ -147,6 +147,7 @@ def test_stack7b_sampled_tokens_match_oracle():
     say("stack7b oracle on", len(toks), "tokens")
     ref = oracle.stack(st["weights"], st["scales"], st["x"][toks])
     np.testing.assert_array_equal(y[toks], ref)
-    say("stack7b chunk 1000 (ragged tail 48) and 64 (skinny path)")
+    say("stack7b chunk 1000 (ragged tail 48), 64 and 32 (skinny paths)")
     np.testing.assert_array_equal(host(run(stack, x, 1000)), y)
     np.testing.assert_array_equal(host(run(stack, x[:256].contiguous(), 64)), y[:256])
+    np.testing.assert_array_equal(host(run(stack, x[:80].contiguous(), 32)), y[:80])
