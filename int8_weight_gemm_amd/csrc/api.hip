@@ -238,10 +238,38 @@ pf_status run_skinny_xres(GemmSet& set, int64_t M, hipStream_t s)
 
 // Runs a set of products that share M (skinny for M <= 64, tiled above, with
 // tiles of `tile_tokens` tokens).
+// One unsplit skinny problem through the streamed step kernel (weights and
+// token pieces copied per stage, any K, any output alignment).
+pf_status run_skinny_stream(GemmSet& set, int64_t M, hipStream_t s)
+{
+    const GemmProb& g = set.p[0];
+    StackStep S;
+    std::memset(&S, 0, sizeof(S));
+    S.npairs = 1;
+    S.nproj = 1;
+    S.K = g.K;
+    S.rows[0] = g.N;
+    S.tile_off[1] = (g.N + kSkinnyRows - 1) / kSkinnyRows;
+    S.tiles_m = 1;
+    S.splits = 1;
+    S.kb_per_split = g.K / 64;
+    S.ldx = g.ldx;
+    S.ldy = g.ldy;
+    StepPair& p = S.pair[0];
+    p.W[0] = g.W;
+    p.ws[0] = g.ws;
+    p.X = g.X;
+    p.xs = g.xs;
+    p.Y = g.Y;
+    p.M = g.M;
+    return launched(launch_gemm_stream(S, token_blocks(M), s));
+}
+
 pf_status run_products(GemmSet& set, int64_t M, int tile_tokens, hipStream_t s)
 {
     if (M <= 64) {
         if (set.nprob == 1 && xres_fits(set.p[0])) return run_skinny_xres(set, M, s);
+        if (set.nprob == 1 && set.p[0].splits == 1) return run_skinny_stream(set, M, s);
         finish_set(set, 1);
         return launched(launch_gemm_skinny(set, token_blocks(M), s));
     }
@@ -884,6 +912,10 @@ pf_status pf_gemm_i8_chunk(const int8_t* W, const float* w_scale, int64_t N, int
         int tile_tokens = 0;
         if (M <= 64) {
             SkinnyPlan p = plan_skinny(N, K, (N + kSkinnyRows - 1) / kSkinnyRows);
+            // splits longer than the token-resident kernel takes: with enough
+            // tiles for half the compute units the streamed kernel runs the
+            // whole K per tile (no partials, no second launch)
+            if (p.kb_per_split > 16 && p.tiles_n >= kComputeUnits / 2) p = unsplit(N, K);
             // a product of at most a few MB is over before a second launch (the
             // split's reduction) would start: split only as far as the
             // token-resident kernel needs (16 k-blocks per split)

@@ -106,6 +106,31 @@ def test_skinny_tails(M, split):
     np.testing.assert_array_equal(host(y), oracle.linear(W, ws, q, s))
 
 
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("M", [7, 33])
+def test_skinny_unaligned_output(M, split):
+    """Up to 64 tokens with an output that is only 4-byte aligned: the streamed
+    kernel (unsplit) or the piecewise one (split), both with scalar stores."""
+    N, K = 300, 1536
+    W, ws, q, s = _proj(N, K, M, 800 + M)
+    wsp = pf.workspace(pf.gemm_i8_chunk_workspace(N, K, M)) if split else None
+    buf = torch.full((M * N + 1,), -1.0, dtype=torch.float32, device="cuda")
+    out = buf[1:].view(M, N)
+    pf.gemm_i8_chunk(dev(W), dev(ws), dev(q), dev(s), ws=wsp, out=out)
+    np.testing.assert_array_equal(host(out), oracle.linear(W, ws, q, s))
+    assert host(buf)[0] == -1.0
+
+
+def test_skinny_many_tiles_long_k():
+    """129 tiles of 64 rows (the last ragged) and 33 k-blocks: the whole K per
+    tile in the streamed kernel, no split."""
+    N, K, M = 8200, 2112, 37
+    W, ws, q, s = _proj(N, K, M, 61)
+    wsp = pf.workspace(pf.gemm_i8_chunk_workspace(N, K, M))
+    y = pf.gemm_i8_chunk(dev(W), dev(ws), dev(q), dev(s), ws=wsp)
+    np.testing.assert_array_equal(host(y), oracle.linear(W, ws, q, s))
+
+
 def test_split_workspace_reused_with_garbage():
     # the split partials are overwritten each call: any workspace contents work
     N, K, M = 1024, 4096, 32
