@@ -118,8 +118,8 @@ __device__ __forceinline__ void rebuild_row(const QuantPair& P, int t, int K)
 
 // A row of at most 1024 U values with the values held in registers (U
 // float4 pieces per thread, pieces i = threadIdx.x + 256 u): every load of the
-// row is issued before any is used (the split partials four splits at a
-// time), and the codes come from the registers, so the row is read once.
+// row is issued before any is used (the split partials four splits at a time
+// up to U = 4), and the codes come from the registers, so the row is read once.
 // Same arithmetic as rebuild_row followed by quantize_row.
 template <int U>
 __device__ __forceinline__ void quant_row_regs(const QuantPair& P, int t, int K)
@@ -135,16 +135,17 @@ __device__ __forceinline__ void quant_row_regs(const QuantPair& P, int t, int K)
         int4 a[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) a[u] = prow[idx[u]];
-        for (int sp0 = 1; sp0 < P.splits; sp0 += 4) {
-            int4 w[U][4];
+        constexpr int SB = U <= 4 ? 4 : 1;          // splits loaded together
+        for (int sp0 = 1; sp0 < P.splits; sp0 += SB) {
+            int4 w[U][SB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < SB; ++j) {
                 const int64_t off = (int64_t)min(sp0 + j, P.splits - 1) * sstride;
 #pragma unroll
                 for (int u = 0; u < U; ++u) w[u][j] = prow[idx[u] + off];
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < SB; ++j)
                 if (sp0 + j < P.splits)
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
@@ -203,6 +204,10 @@ __device__ __forceinline__ void quant_row_regs(const QuantPair& P, int t, int K)
     }
 }
 
+// Rows of up to 4096 values (kLong = false) or longer (kLong, with more
+// registers per thread; a separate kernel so the short rows keep their
+// occupancy).
+template <bool kLong>
 __global__ __launch_bounds__(256) void k_quantize_step(QuantStep S)
 {
     const int bid = blockIdx.x;
@@ -213,9 +218,15 @@ __global__ __launch_bounds__(256) void k_quantize_step(QuantStep S)
     const QuantPair& P = S.pair[pi];
     const int t = bid - P.row0;
     const int n4 = S.K >> 2;
-    if (n4 <= 256) return quant_row_regs<1>(P, t, S.K);
-    if (n4 <= 512) return quant_row_regs<2>(P, t, S.K);
-    if (n4 <= 1024) return quant_row_regs<4>(P, t, S.K);
+    if (kLong) {
+        if (n4 <= 2048) return quant_row_regs<8>(P, t, S.K);
+        if (n4 <= 3072) return quant_row_regs<12>(P, t, S.K);
+        if (n4 <= 4096) return quant_row_regs<16>(P, t, S.K);
+    } else {
+        if (n4 <= 256) return quant_row_regs<1>(P, t, S.K);
+        if (n4 <= 512) return quant_row_regs<2>(P, t, S.K);
+        if (n4 <= 1024) return quant_row_regs<4>(P, t, S.K);
+    }
     if (P.part) {
         rebuild_row(P, t, S.K);
         if (!P.q) return;
@@ -229,7 +240,8 @@ __global__ __launch_bounds__(256) void k_quantize_step(QuantStep S)
 hipError_t launch_quantize_step(const QuantStep& S, hipStream_t s)
 {
     if (S.total_rows <= 0) return hipSuccess;
-    PF_LAUNCH(k_quantize_step, dim3(S.total_rows), dim3(256), 0, s, S);
+    if (S.K > 4096) PF_LAUNCH(k_quantize_step<true>, dim3(S.total_rows), dim3(256), 0, s, S);
+    else PF_LAUNCH(k_quantize_step<false>, dim3(S.total_rows), dim3(256), 0, s, S);
     return hipGetLastError();
 }
 
