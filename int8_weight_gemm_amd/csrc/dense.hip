@@ -6,6 +6,8 @@
 // Here a workgroup owns a band of weight rows, streams them from HBM with
 // 128-bit loads straight into the MFMA operand registers, and takes the chunk's
 // quantised tokens from LDS, where they are staged once per workgroup.
+#include <cstring>
+
 #include "device.hpp"
 #include "kernels.hpp"
 #include "problems.hpp"
@@ -69,19 +71,22 @@ __device__ __forceinline__ void quantize_row(const float* __restrict__ x, int K,
     }
 }
 
-__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x, int64_t ldx, int K,
-                                                  int8_t* __restrict__ q, float* __restrict__ scale)
-{
-    const int t = blockIdx.x;
-    quantize_row(x + (int64_t)t * ldx, K, q + (int64_t)t * K, scale + t);
-}
-
+// M rows of x [M][ldx]: the quantisation-step kernel with one pair (rows held
+// in registers up to 16384 values, two passes over the row beyond).
 hipError_t launch_quantize(const float* x, int64_t ldx, int M, int K, int8_t* q, float* scale,
                            hipStream_t s)
 {
     if (M <= 0) return hipSuccess;
-    PF_LAUNCH(k_quantize, dim3(M), dim3(256), 0, s, x, ldx, K, q, scale);
-    return hipGetLastError();
+    QuantStep S;
+    std::memset(&S, 0, sizeof(S));
+    S.npairs = 1;
+    S.K = K;
+    S.total_rows = M;
+    S.pair[0].src = x;
+    S.pair[0].ld = ldx;
+    S.pair[0].q = q;
+    S.pair[0].s = scale;
+    return launch_quantize_step(S, s);
 }
 
 // The token rows of several chunks in one launch (one workgroup per row).

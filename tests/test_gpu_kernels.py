@@ -35,7 +35,10 @@ def test_init_reports_gfx950():
 
 # --- quantisation ----------------------------------------------------------------
 
-@pytest.mark.parametrize("M,K", [(1, 64), (11, 1024), (32, 4096), (7, 11008), (512, 2048)])
+# rows held in registers for every width up to 16384 values (1 to 16 pieces
+# per thread), two passes beyond
+@pytest.mark.parametrize("M,K", [(1, 64), (11, 1024), (32, 4096), (7, 11008), (512, 2048), (3, 1088),
+                                 (5, 6144), (4, 16384), (3, 20480)])
 def test_quantize_matches_oracle(M, K):
     x = prefill_inputs.activations(np.random.default_rng(M * 7 + K), (M, K))
     x[0, :5] = [0.0, -0.0, 2.5, -2.5, 1e-30]
