@@ -422,13 +422,6 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmSet set)
     skinny_tile<TB, KP>(P, blockIdx.x - P.tile_begin);
 }
 
-template <int TB, int KP>
-__global__ __launch_bounds__(256) void k_gemm_skinny_step(StackStep S)
-{
-    int local;
-    const GemmProb P = step_prob(S, blockIdx.x, local);
-    skinny_tile<TB, KP>(P, local);
-}
 
 // Sum of the split partials and the epilogue; one thread per output.  Here
 // tile_begin counts blocks of 256 outputs.
@@ -484,16 +477,5 @@ hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t 
     if (e != hipSuccess) return e;
     return launch_split_reduce(set, s);
 }
-
-hipError_t launch_gemm_skinny_step(const StackStep& S, int token_blocks, hipStream_t s)
-{
-    const int blocks = S.npairs * S.tile_off[S.nproj];
-    if (blocks <= 0) return hipSuccess;
-    if (token_blocks < 1 || token_blocks > 4) return hipErrorInvalidValue;
-    const dim3 g(blocks), b(256);
-    PF_SKINNY_CASES(k_gemm_skinny_step, S)
-    return hipGetLastError();
-}
-
 
 }  // namespace pf

@@ -141,7 +141,6 @@ hipError_t launch_quantize(const float* x, int64_t ldx, int M, int K, int8_t* q,
                            hipStream_t s);
 hipError_t launch_quantize_step(const QuantStep& S, hipStream_t s);
 hipError_t launch_gemv(const GemmSet& set, hipStream_t s);
-hipError_t launch_gemm_skinny_step(const StackStep& S, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_tiled_step(const StackStep& S, int64_t M, hipStream_t s);
 hipError_t launch_gemm_stream(const StackStep& S, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_xres(const StackStep& S, int token_blocks, hipStream_t s);
