@@ -317,7 +317,10 @@ hipError_t launch_softmax_topk(const float* logits, int E, int T, int k, int* id
 // popcount over e's bitmap words), so each expert lists its tokens in
 // ascending order; its rank among t's selections is the number of t's ids
 // below e, which orders the combine table by ascending expert id.
-__global__ __launch_bounds__(1024) void k_group(const int* __restrict__ ids,
+// With kLds the ids are first copied into LDS (after the bitmap), so the
+// per-pair reads below, the rank loop's among them, do not go to memory.
+template <bool kLds>
+__global__ __launch_bounds__(1024) void k_group(const int* __restrict__ ids_g,
                                                 const float* __restrict__ w, int T, int k, int E,
                                                 int* __restrict__ off, int* __restrict__ pair_tok,
                                                 int* __restrict__ comb_row,
@@ -328,6 +331,24 @@ __global__ __launch_bounds__(1024) void k_group(const int* __restrict__ ids,
     __shared__ int scan[1024];
     const int words = (T + 31) >> 5;
     const int tid = threadIdx.x;
+    const int np = T * k;
+    int* ids_l = reinterpret_cast<int*>(sel + E * words);
+    if (kLds) {
+        for (int p0 = 0; p0 < np; p0 += 4 * 1024) {
+            int v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int p = p0 + u * 1024 + tid;
+                v[u] = p < np ? ids_g[p] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int p = p0 + u * 1024 + tid;
+                if (p < np) ids_l[p] = v[u];
+            }
+        }
+    }
+    const int* ids = kLds ? ids_l : ids_g;
     for (int i = tid; i < E * words; i += 1024) sel[i] = 0;
     for (int i = tid; i < 1024; i += 1024) cnt[i] = 0;
     __syncthreads();
@@ -366,8 +387,11 @@ hipError_t launch_group(const int* ids, const float* w, int T, int k, int E, int
                         int* pair_tok, int* comb_row, float* comb_w, hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
-    PF_LAUNCH(k_group, dim3(1), dim3(1024), group_lds_bytes(T, E), s, ids, w, T, k, E,
-                       off, pair_tok, comb_row, comb_w);
+    const size_t lds = group_lds_bytes(T, E), with_ids = lds + (size_t)T * k * 4;
+    if (with_ids <= 64 * 1024)
+        PF_LAUNCH(k_group<true>, dim3(1), dim3(1024), with_ids, s, ids, w, T, k, E, off, pair_tok, comb_row, comb_w);
+    else
+        PF_LAUNCH(k_group<false>, dim3(1), dim3(1024), lds, s, ids, w, T, k, E, off, pair_tok, comb_row, comb_w);
     return hipGetLastError();
 }
 

@@ -55,6 +55,12 @@ def test_streaming_expert_shapes_match_oracle(E, k, H, I, T):
     check(prefill_inputs.moe(E, k, H, I, T, seed=100 + E + T))
 
 
+def test_moe_many_pairs_grouping_from_memory():
+    # 16000 (token, expert) pairs: the ids do not fit in LDS beside the bitmap,
+    # so the grouping reads them from memory
+    check(prefill_inputs.moe(16, 8, 64, 64, 2000, seed=9))
+
+
 def test_moe_concentrated_routing():
     # A router with one dominant expert sends every token to the same experts:
     # groups larger than 32 tokens take the multi-group path.
