@@ -423,18 +423,56 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmSet set)
 }
 
 
-// Sum of the split partials and the epilogue; one thread per output.  Here
-// tile_begin counts blocks of 256 outputs.
+// Sum of the split partials and the epilogue.  A workgroup takes 1024 outputs
+// of the flattened M x N result (tile_begin counts such blocks), a thread four
+// consecutive ones.  When N, the row strides and the bases are multiples of
+// four elements (16 bytes), a thread's four outputs lie in one row and move as
+// 16-byte loads and stores, four splits' loads in flight at once; otherwise it
+// takes them one at a time.  The sums are integer sums, so the bits do not
+// depend on their order.
+constexpr int kReduceBlock = 1024;
+
 __global__ __launch_bounds__(256) void k_split_reduce(GemmSet set)
 {
     const GemmProb P = find_prob(set, blockIdx.x);
-    const int64_t idx = (int64_t)(blockIdx.x - P.tile_begin) * 256 + threadIdx.x;
-    if (idx >= (int64_t)P.M * P.N) return;
-    const int t = (int)(idx / P.N), n = (int)(idx - (int64_t)t * P.N);
-    const int* a = P.acc + (int64_t)t * P.acc_ld + n;
-    int v = 0;
-    for (int sp = 0; sp < P.splits; ++sp) v += a[(int64_t)sp * P.acc_split];
-    store_out(P, t, n, epilogue(v, P.ws[n], P.xs[t]));
+    const int64_t total = (int64_t)P.M * P.N;
+    const int64_t i0 = ((int64_t)(blockIdx.x - P.tile_begin) * 256 + threadIdx.x) * 4;
+    if (i0 >= total) return;
+    const bool vec = (P.N & 3) == 0 && (P.acc_ld & 3) == 0 && (P.acc_split & 3) == 0 &&
+                     ((uintptr_t)P.acc & 15) == 0 && ((uintptr_t)P.Y & 15) == 0 && (P.ldy & 3) == 0 &&
+                     (!P.Y2 || (((uintptr_t)P.Y2 & 15) == 0 && (P.ldy2 & 3) == 0));
+    if (vec) {
+        const int t = (int)(i0 / P.N), n = (int)(i0 - (int64_t)t * P.N);
+        const int* a = P.acc + (int64_t)t * P.acc_ld + n;
+        v4i v = v4i{0, 0, 0, 0};
+        int sp = 0;
+        for (; sp + 4 <= P.splits; sp += 4) {
+            v4i q[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) q[u] = *reinterpret_cast<const v4i*>(a + (int64_t)(sp + u) * P.acc_split);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v += q[u];
+        }
+        for (; sp < P.splits; ++sp) v += *reinterpret_cast<const v4i*>(a + (int64_t)sp * P.acc_split);
+        const float xs = P.xs[t];
+        float4 o;
+        o.x = epilogue(v[0], P.ws[n], xs);
+        o.y = epilogue(v[1], P.ws[n + 1], xs);
+        o.z = epilogue(v[2], P.ws[n + 2], xs);
+        o.w = epilogue(v[3], P.ws[n + 3], xs);
+        *reinterpret_cast<float4*>(P.Y + (int64_t)t * P.ldy + n) = o;
+        if (P.Y2) *reinterpret_cast<float4*>(P.Y2 + (int64_t)t * P.ldy2 + n) = o;
+        return;
+    }
+    for (int r = 0; r < 4; ++r) {
+        const int64_t idx = i0 + r;
+        if (idx >= total) break;
+        const int t = (int)(idx / P.N), n = (int)(idx - (int64_t)t * P.N);
+        const int* a = P.acc + (int64_t)t * P.acc_ld + n;
+        int v = 0;
+        for (int sp = 0; sp < P.splits; ++sp) v += a[(int64_t)sp * P.acc_split];
+        store_out(P, t, n, epilogue(v, P.ws[n], P.xs[t]));
+    }
 }
 
 hipError_t launch_split_reduce(const GemmSet& set, hipStream_t s)
@@ -446,7 +484,7 @@ hipError_t launch_split_reduce(const GemmSet& set, hipStream_t s)
     int begin = 0;
     for (int i = 0; i < r.nprob; ++i) {
         r.p[i].tile_begin = begin;
-        if (r.p[i].splits > 1) begin += (int)(((int64_t)r.p[i].M * r.p[i].N + 255) / 256);
+        if (r.p[i].splits > 1) begin += (int)(((int64_t)r.p[i].M * r.p[i].N + kReduceBlock - 1) / kReduceBlock);
     }
     if (begin == 0) return hipSuccess;
     r.total_tiles = begin;
