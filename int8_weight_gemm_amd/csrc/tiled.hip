@@ -2,13 +2,10 @@
 //
 // "Batched Prefill" (cellm), §The arithmetic: with hundreds of tokens per chunk
 // every weight byte feeds hundreds of multiply-adds, so the product is bound by
-// the matrix cores, not by HBM.  The kernel is laid out for v_mfma_i32_32x32x32_i8,
-// which keeps the matrix core of a SIMD busy from a single wave with a few
-// independent accumulators (the 16x16x64 form needs many more in flight):
-//  * a workgroup of four waves (one per SIMD, 512 registers each) owns 256
-//    weight rows x 64 WJ tokens (WJ = 4 or 2); wave (wn, wm) of the 2 x 2 grid
-//    owns 128 rows x 32 WJ tokens: 4 x WJ accumulator blocks of 32 x 32 in
-//    AGPRs;
+// the matrix cores, not by HBM.  The kernel is laid out for v_mfma_i32_32x32x32_i8:
+//  * a workgroup of eight waves (two per SIMD) owns 256 weight rows x 64 WJ
+//    tokens (WJ = 4 or 2); wave (wn, wm) of the 2 x 4 grid owns 128 rows x
+//    16 WJ tokens: 4 x WJ / 2 accumulator blocks of 32 x 32;
 //  * a stage is one k-block (64 bytes of K) of the tile's weight rows and
 //    tokens in LDS as 1 KB fragments of 16 rows x 64 bytes.  A copy gives four
 //    consecutive lanes one row's 64 contiguous bytes (lane l: row l / 4), the
@@ -19,11 +16,9 @@
 //    four stages, one barrier per stage, and the reads of stage g + 1 are in
 //    flight while the MFMAs of stage g run;
 //  * every fragment, weights and tokens, is copied by global_load_lds_dwordx4,
-//    three stages ahead.  (Weights through registers and ds_write_b128 issue
-//    about twice as slowly per fragment.)  The copies of a stage take the
-//    compute unit's address unit about 0.75 of the stage's MFMA time, and a
-//    wave that issues them cannot issue MFMAs meanwhile: that, not latency,
-//    is what holds this kernel below the matrix-core rate;
+//    three stages ahead.  These copies, 32 KB per stage and compute unit, are
+//    what holds the kernel: alone (no operand reads, no MFMAs) they take about
+//    80% of its time, while the operand reads and MFMAs alone take about 73%;
 //  * workgroups on one XCD (blockIdx % 8) take consecutive tiles, and the token
 //    tiles of one band of weight rows are consecutive, so the band is fetched
 //    from HBM once into that XCD's L2 and shared.
