@@ -285,70 +285,83 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
     wait_vmcnt<0>();                                     // no copy outlives the workgroup's LDS
 
     // Lane l, register 4 q + r of a 32 x 32 block: token l % 32, row
-    // 8 q + 4 (l / 32) + r.  Split: this split's int32 partials; unsplit:
-    // the epilogue with the tile's scales staged once through LDS.
+    // 8 q + 4 (l / 32) + r.  Split: this split's int32 partials; unsplit: the
+    // epilogue with the tile's scales staged once in LDS.  The tile leaves
+    // through the ring in two passes, rows 128 h .. + 127 in pass h: the waves
+    // of that row half write their values as [token][128 rows], the 16-byte
+    // piece of rows 4 g .. 4 g + 3 of token u at 512 u + 16 (g ^ (u % 32)), then
+    // every thread stores whole 512-byte token rows, 32 lanes per token.  (Each
+    // lane storing its own 16-byte pieces, 64 tokens per instruction, cost
+    // ~20% of the 7B prompt's time.)
     const bool split = P.splits > 1;
     int* const part = split ? P.acc + (int64_t)kidx * P.acc_split : nullptr;
-    float* const sws = reinterpret_cast<float*>(ring);
-    float* const sxs = sws + 256;
+    __shared__ float sws[256], sxs[256];
     if (!split) {
-        stage_barrier();                                 // every wave is done with the ring
         const int t = (int)threadIdx.x;
         if (t < 256) sws[t] = P.ws[min(n0 + t, P.N - 1)];
         if (t < 64 * WJ) sxs[t] = P.xs[min(t0 + t, P.M - 1)];
-        __syncthreads();
     }
-    const bool pv4 = split && ((P.acc_ld & 3) == 0) && ((P.acc_split & 3) == 0);
-    const bool vec = !split && (((uintptr_t)P.Y & 15) == 0) && ((P.ldy & 3) == 0) &&
-                     (!P.Y2 || ((((uintptr_t)P.Y2 & 15) == 0) && ((P.ldy2 & 3) == 0)));
+    __syncthreads();                                     // every wave is done with the ring
+    const bool vec = split ? ((P.acc_ld & 3) == 0 && (P.acc_split & 3) == 0 && ((uintptr_t)P.acc & 15) == 0)
+                           : (((uintptr_t)P.Y & 15) == 0 && (P.ldy & 3) == 0 &&
+                              (!P.Y2 || (((uintptr_t)P.Y2 & 15) == 0 && (P.ldy2 & 3) == 0)));
+    constexpr int kPieces = 64 * WJ * 32;                // 16-byte pieces per pass
+    static_assert(64 * WJ * 512 <= NS * kStage, "a pass fits in the ring");
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int h = 0; h < 2; ++h) {
+        if (wn == h) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int nl = wn * 128 + 32 * i + 8 * q + ((lane >> 5) << 2);   // row in the tile
-            const int n = n0 + nl;
-            if (n >= P.N) continue;
-            float4 w4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (!split) w4 = *reinterpret_cast<const float4*>(sws + nl);
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < JB; ++j) {
-                const int tl = wm * 32 * JB + 32 * j + lrow;                 // token in the tile
-                const int t = t0 + tl;
-                if (t >= P.M) continue;
-                const v4i a = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                if (split) {
-                    int* p = part + (int64_t)t * P.acc_ld + n;
-                    if (pv4 && n + 3 < P.N) {
-                        *reinterpret_cast<v4i*>(p) = a;
-                    } else {
+                for (int q = 0; q < 4; ++q)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (n + r < P.N) p[r] = a[r];
+                    for (int j = 0; j < JB; ++j) {
+                        const int g4 = 8 * i + 2 * q + (lane >> 5);          // rows 4 g4 .. + 3 of the half
+                        const int tl = wm * 32 * JB + 32 * j + lrow;         // token in the tile
+                        v4i val = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                        if (!split) {
+                            const float4 w4 = *reinterpret_cast<const float4*>(sws + 128 * h + 4 * g4);
+                            const float xs = sxs[tl];
+                            val = v4i{__float_as_int(epilogue(val[0], w4.x, xs)), __float_as_int(epilogue(val[1], w4.y, xs)),
+                                      __float_as_int(epilogue(val[2], w4.z, xs)), __float_as_int(epilogue(val[3], w4.w, xs))};
+                        }
+                        *reinterpret_cast<v4i*>(ring + tl * 512 + 16 * (g4 ^ (tl & 31))) = val;
                     }
-                    continue;
-                }
-                const float xs = sxs[tl];
-                float4 v;
-                v.x = epilogue(a[0], w4.x, xs);
-                v.y = epilogue(a[1], w4.y, xs);
-                v.z = epilogue(a[2], w4.z, xs);
-                v.w = epilogue(a[3], w4.w, xs);
-                float* y = P.Y + (int64_t)t * P.ldy + n;
-                float* y2 = P.Y2 ? P.Y2 + (int64_t)t * P.ldy2 + n : nullptr;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kPieces / (64 * NW); ++u) {
+            const int idx = (int)threadIdx.x + 64 * NW * u;
+            const int tl = idx >> 5, g4 = idx & 31;
+            const int t = t0 + tl, n = n0 + 128 * h + 4 * g4;
+            if (t >= P.M || n >= P.N) continue;
+            const v4i val = *reinterpret_cast<const v4i*>(ring + tl * 512 + 16 * (g4 ^ (tl & 31)));
+            if (split) {
+                int* p = part + (int64_t)t * P.acc_ld + n;
                 if (vec && n + 3 < P.N) {
-                    *reinterpret_cast<float4*>(y) = v;
-                    if (y2) *reinterpret_cast<float4*>(y2) = v;
+                    *reinterpret_cast<v4i*>(p) = val;
                 } else {
-                    const float e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (n + r < P.N) {
-                            y[r] = e[r];
-                            if (y2) y2[r] = e[r];
-                        }
+                        if (n + r < P.N) p[r] = val[r];
                 }
+                continue;
+            }
+            float* y = P.Y + (int64_t)t * P.ldy + n;
+            float* y2 = P.Y2 ? P.Y2 + (int64_t)t * P.ldy2 + n : nullptr;
+            if (vec && n + 3 < P.N) {
+                *reinterpret_cast<v4i*>(y) = val;
+                if (y2) *reinterpret_cast<v4i*>(y2) = val;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < P.N) {
+                        y[r] = __int_as_float(val[r]);
+                        if (y2) y2[r] = __int_as_float(val[r]);
+                    }
             }
         }
+        if (h == 0) __syncthreads();                     // pass 1 overwrites the ring
     }
 }
 
