@@ -15,77 +15,99 @@ namespace pf {
 // Router logits: l[t][e] = sum over k ascending of fl(Wr[e][k] * x[t][k]), each
 // product and each partial sum rounded on its own (no fused multiply-add: the
 // library is compiled with -ffp-contract=off).  32 tokens x 32 experts per
-// workgroup, 4 independent chains per thread; 64-wide k pieces staged in LDS,
-// double-buffered: the next piece is loaded into registers (two 16-byte loads
-// per operand per thread) while the current one is consumed.
+// workgroup; a thread owns TI tokens x EJ experts, each an independent chain;
+// 64-wide k pieces staged in LDS, double-buffered: the next piece is loaded
+// into registers while the current one is consumed.
 constexpr int kRtTile = 32;
 constexpr int kRtK = 64;
+constexpr int kRtTI = 1, kRtEJ = 2;                    // chains per thread: tokens x experts
 
-__global__ __launch_bounds__(256) void k_router(const float* __restrict__ Wr,
-                                                const float* __restrict__ x, int E, int H, int T,
-                                                float* __restrict__ logits)
+template <int TI, int EJ>
+__global__ __launch_bounds__(1024 / (TI * EJ)) void k_router(const float* __restrict__ Wr,
+                                                             const float* __restrict__ x, int E, int H, int T,
+                                                             float* __restrict__ logits)
 {
+    constexpr int NT = 1024 / (TI * EJ);                // threads
+    constexpr int CE = kRtTile / EJ, CT = kRtTile / TI;  // thread grid: CE experts x CT tokens
+    constexpr int NP = kRtTile * kRtK / 4;              // float4 pieces per operand and piece
+    constexpr int NF = (NP + NT - 1) / NT;              // of them per thread
+    static_assert(NP % NT == 0 || NT % NP == 0, "staging split");
+    const bool stager = (int)threadIdx.x < NP;          // false only with more threads than pieces
     // rows padded to 68 floats: 16-byte aligned, and the 16 rows a quarter-wave
     // reads at one k sit in distinct banks
     __shared__ __attribute__((aligned(16))) float sx[2][kRtTile][kRtK + 4];
     __shared__ __attribute__((aligned(16))) float sw[2][kRtTile][kRtK + 4];
     const int e0 = blockIdx.x * kRtTile, t0 = blockIdx.y * kRtTile;
-    const int ti = threadIdx.x >> 4, ei = threadIdx.x & 15;
-    // staging: float4 f = threadIdx.x + 256 u of a [32][64] piece -> row f / 16,
-    // column 4 (f % 16); this thread's two rows and column
-    const int r0 = threadIdx.x >> 4, r1 = r0 + 16, c4 = (threadIdx.x & 15) << 2;
-    const float* xr0 = x + (int64_t)min(t0 + r0, T - 1) * H + c4;
-    const float* xr1 = x + (int64_t)min(t0 + r1, T - 1) * H + c4;
-    const float* wr0 = Wr + (int64_t)min(e0 + r0, E - 1) * H + c4;
-    const float* wr1 = Wr + (int64_t)min(e0 + r1, E - 1) * H + c4;
-    float4 px0 = *reinterpret_cast<const float4*>(xr0), px1 = *reinterpret_cast<const float4*>(xr1);
-    float4 pw0 = *reinterpret_cast<const float4*>(wr0), pw1 = *reinterpret_cast<const float4*>(wr1);
-    *reinterpret_cast<float4*>(&sx[0][r0][c4]) = px0;
-    *reinterpret_cast<float4*>(&sx[0][r1][c4]) = px1;
-    *reinterpret_cast<float4*>(&sw[0][r0][c4]) = pw0;
-    *reinterpret_cast<float4*>(&sw[0][r1][c4]) = pw1;
-    float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+    const int ei = threadIdx.x % CE, ti = threadIdx.x / CE;
+    // staging: float4 f = threadIdx.x + NT u of a [32][64] piece -> row f / 16,
+    // column 4 (f % 16); rows past the end repeat the last one
+    int rr[NF], cc[NF];
+    const float* xr[NF];
+    const float* wr[NF];
+    float4 px[NF], pw[NF];
+#pragma unroll
+    for (int u = 0; u < NF; ++u) {
+        const int f = ((int)threadIdx.x + NT * u) % NP;
+        rr[u] = f >> 4;
+        cc[u] = (f & 15) << 2;
+        xr[u] = x + (int64_t)min(t0 + rr[u], T - 1) * H + cc[u];
+        wr[u] = Wr + (int64_t)min(e0 + rr[u], E - 1) * H + cc[u];
+        px[u] = *reinterpret_cast<const float4*>(xr[u]);
+        pw[u] = *reinterpret_cast<const float4*>(wr[u]);
+    }
+    if (stager) {
+#pragma unroll
+        for (int u = 0; u < NF; ++u) {
+            *reinterpret_cast<float4*>(&sx[0][rr[u]][cc[u]]) = px[u];
+            *reinterpret_cast<float4*>(&sw[0][rr[u]][cc[u]]) = pw[u];
+        }
+    }
+    float acc[TI][EJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < EJ; ++j) acc[i][j] = 0.0f;
     const int npieces = H / kRtK;
     __syncthreads();
     for (int pc = 0; pc < npieces; ++pc) {
         const int b = pc & 1;
         const bool more = pc + 1 < npieces;
-        if (more) {
+        if (more && stager) {
             const int k1 = (pc + 1) * kRtK;
-            px0 = *reinterpret_cast<const float4*>(xr0 + k1);
-            px1 = *reinterpret_cast<const float4*>(xr1 + k1);
-            pw0 = *reinterpret_cast<const float4*>(wr0 + k1);
-            pw1 = *reinterpret_cast<const float4*>(wr1 + k1);
+#pragma unroll
+            for (int u = 0; u < NF; ++u) {
+                px[u] = *reinterpret_cast<const float4*>(xr[u] + k1);
+                pw[u] = *reinterpret_cast<const float4*>(wr[u] + k1);
+            }
         }
 #pragma unroll 4
         for (int kk = 0; kk < kRtK; kk += 4) {
-            const float4 w0 = *reinterpret_cast<const float4*>(&sw[b][ei][kk]);
-            const float4 w1 = *reinterpret_cast<const float4*>(&sw[b][ei + 16][kk]);
-            const float4 x0 = *reinterpret_cast<const float4*>(&sx[b][ti][kk]);
-            const float4 x1 = *reinterpret_cast<const float4*>(&sx[b][ti + 16][kk]);
-            const float wa[4] = {w0.x, w0.y, w0.z, w0.w}, wb[4] = {w1.x, w1.y, w1.z, w1.w};
-            const float xa[4] = {x0.x, x0.y, x0.z, x0.w}, xb[4] = {x1.x, x1.y, x1.z, x1.w};
+            float4 wv[EJ], xv[TI];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {                // k ascending within each chain
-                acc[0][0] = acc[0][0] + wa[c] * xa[c];
-                acc[0][1] = acc[0][1] + wb[c] * xa[c];
-                acc[1][0] = acc[1][0] + wa[c] * xb[c];
-                acc[1][1] = acc[1][1] + wb[c] * xb[c];
-            }
+            for (int j = 0; j < EJ; ++j) wv[j] = *reinterpret_cast<const float4*>(&sw[b][ei + CE * j][kk]);
+#pragma unroll
+            for (int i = 0; i < TI; ++i) xv[i] = *reinterpret_cast<const float4*>(&sx[b][ti + CT * i][kk]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)                  // k ascending within each chain
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+#pragma unroll
+                    for (int j = 0; j < EJ; ++j) acc[i][j] = acc[i][j] + wv[j][c] * xv[i][c];
         }
-        if (more) {
-            *reinterpret_cast<float4*>(&sx[b ^ 1][r0][c4]) = px0;
-            *reinterpret_cast<float4*>(&sx[b ^ 1][r1][c4]) = px1;
-            *reinterpret_cast<float4*>(&sw[b ^ 1][r0][c4]) = pw0;
-            *reinterpret_cast<float4*>(&sw[b ^ 1][r1][c4]) = pw1;
+        if (more && stager) {
+#pragma unroll
+            for (int u = 0; u < NF; ++u) {
+                *reinterpret_cast<float4*>(&sx[b ^ 1][rr[u]][cc[u]]) = px[u];
+                *reinterpret_cast<float4*>(&sw[b ^ 1][rr[u]][cc[u]]) = pw[u];
+            }
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int t = t0 + ti + 16 * i, e = e0 + ei + 16 * j;
+        for (int j = 0; j < EJ; ++j) {
+            const int t = t0 + ti + CT * i, e = e0 + ei + CE * j;
             if (t < T && e < E) logits[(int64_t)t * E + e] = acc[i][j];
         }
 }
@@ -95,7 +117,7 @@ hipError_t launch_router(const float* Wr, const float* x, int E, int H, int T, f
 {
     if (T <= 0) return hipSuccess;
     dim3 g((E + kRtTile - 1) / kRtTile, (T + kRtTile - 1) / kRtTile);
-    PF_LAUNCH(k_router, g, dim3(256), 0, s, Wr, x, E, H, T, logits);
+    PF_LAUNCH((k_router<kRtTI, kRtEJ>), g, dim3(1024 / (kRtTI * kRtEJ)), 0, s, Wr, x, E, H, T, logits);
     return hipGetLastError();
 }
 
