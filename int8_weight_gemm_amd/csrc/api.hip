@@ -881,10 +881,32 @@ pf_status pf_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int
     }
 }
 
+// 65 to 128 tokens: products of at most this many weight bytes go through the
+// token-resident kernel (eight 16-token blocks, K split into slices of at most
+// 8 k-blocks) instead of the tiled one, whose 256-row tiles are then too few.
+constexpr int64_t kXres128MaxBytes = 16 << 20;
+
+bool xres128(int64_t N, int64_t K, int64_t M)
+{
+    return M > 64 && M <= 128 && N * K <= kXres128MaxBytes;
+}
+
+SkinnyPlan plan_xres128(int64_t N, int64_t K)
+{
+    SkinnyPlan p = unsplit(N, K);
+    const int nkb = (int)(K / 64);
+    p.kb_per_split = std::min(nkb, xres_max_kb(8));
+    p.splits = (nkb + p.kb_per_split - 1) / p.kb_per_split;
+    return p;
+}
+
 size_t pf_gemm_i8_chunk_workspace(int64_t N, int64_t K, int64_t M)
 {
     if (N <= 0 || N > INT32_MAX || !valid_k(K) || M <= 0 || M > INT32_MAX) return 0;
-    if (M > 64) return split_bytes(N, M, plan_tiled(N, K, M));
+    if (M > 64) {
+        const size_t tiled = split_bytes(N, M, plan_tiled(N, K, M));
+        return xres128(N, K, M) ? std::max(tiled, split_bytes(N, M, plan_xres128(N, K))) : tiled;
+    }
     const SkinnyPlan p = plan_skinny(N, K, (N + kSkinnyRows - 1) / kSkinnyRows);
     return split_bytes(N, M, p);
 }
@@ -929,6 +951,14 @@ pf_status pf_gemm_i8_chunk(const int8_t* W, const float* w_scale, int64_t N, int
             if (workspace && overlap(workspace, ws_bytes, y, yb)) return PF_EINVAL;
             char* scratch = static_cast<char*>(workspace);
             make_skinny(set.p[0], W, w_scale, N, K, xq, K, a_scale, M, y, N, p, scratch, M);
+        } else if (xres128(N, K, M) && xres_fits_shape(N, y) &&
+                   (plan_xres128(N, K).splits == 1 ||
+                    (workspace && ws_bytes >= split_bytes(N, M, plan_xres128(N, K))))) {
+            const SkinnyPlan p = plan_xres128(N, K);
+            if (workspace && overlap(workspace, ws_bytes, y, yb)) return PF_EINVAL;
+            char* scratch = static_cast<char*>(workspace);
+            make_skinny(set.p[0], W, w_scale, N, K, xq, K, a_scale, M, y, N, p, scratch, M);
+            return run_skinny_xres(set, M, (hipStream_t)stream);
         } else {
             SkinnyPlan p = plan_tiled(N, K, M);
             if (!workspace || ws_bytes < split_bytes(N, M, p)) p = plan_tiled(N, K, M, 1);

@@ -143,6 +143,9 @@ hipError_t launch_quantize_step(const QuantStep& S, hipStream_t s);
 hipError_t launch_gemv(const GemmSet& set, hipStream_t s);
 hipError_t launch_gemm_tiled_step(const StackStep& S, int64_t M, hipStream_t s);
 hipError_t launch_gemm_stream(const StackStep& S, int token_blocks, hipStream_t s);
+// K-blocks per split the token-resident product takes: 16 up to 64 tokens, 8 for
+// 65 to 128 tokens (run as eight 16-token blocks).
+constexpr int xres_max_kb(int token_blocks) { return token_blocks <= 4 ? 16 : 8; }
 hipError_t launch_gemm_xres(const StackStep& S, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_skinny(const GemmSet& set, int token_blocks, hipStream_t s);
 hipError_t launch_gemm_tiled(const GemmSet& set, int tile_tokens, hipStream_t s);

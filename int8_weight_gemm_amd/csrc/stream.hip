@@ -385,17 +385,56 @@ __device__ __forceinline__ XresItem xres_item(const StackStep& S, int item)
     return it;
 }
 
+// 128 tokens (eight blocks of 16) with token slices of 8 k-blocks: token block tb
+// at xa + (8 tb + i) KB.  Two assembly blocks of two k-blocks each, each ending
+// with its own wait, so no operand is used before it has landed.
+template <>
+__device__ __forceinline__ void lds_stage<8, 4>(StageFrags<8, 4>& f, uint32_t wa, uint32_t xa)
+{
+#define PF_XR8_HALF(I0, I1, A, XB)                                                       \
+    asm volatile(                                                                        \
+        "ds_read_b128 %0, %18 offset:" #A "\n"                                           \
+        "ds_read_b128 %1, %19 offset:" #XB "\n"                                          \
+        "ds_read_b128 %2, %19 offset:8192+" #XB "\n"                                     \
+        "ds_read_b128 %3, %19 offset:16384+" #XB "\n"                                    \
+        "ds_read_b128 %4, %19 offset:24576+" #XB "\n"                                    \
+        "ds_read_b128 %5, %19 offset:32768+" #XB "\n"                                    \
+        "ds_read_b128 %6, %19 offset:40960+" #XB "\n"                                    \
+        "ds_read_b128 %7, %19 offset:49152+" #XB "\n"                                    \
+        "ds_read_b128 %8, %19 offset:57344+" #XB "\n"                                    \
+        "ds_read_b128 %9, %18 offset:1024+" #A "\n"                                      \
+        "ds_read_b128 %10, %19 offset:1024+" #XB "\n"                                    \
+        "ds_read_b128 %11, %19 offset:9216+" #XB "\n"                                    \
+        "ds_read_b128 %12, %19 offset:17408+" #XB "\n"                                   \
+        "ds_read_b128 %13, %19 offset:25600+" #XB "\n"                                   \
+        "ds_read_b128 %14, %19 offset:33792+" #XB "\n"                                   \
+        "ds_read_b128 %15, %19 offset:41984+" #XB "\n"                                   \
+        "ds_read_b128 %16, %19 offset:50176+" #XB "\n"                                   \
+        "ds_read_b128 %17, %19 offset:58368+" #XB "\n"                                   \
+        "s_waitcnt lgkmcnt(0)"                                                           \
+        : "=&v"(f.a[I0]), "=&v"(f.b[0][I0]), "=&v"(f.b[1][I0]), "=&v"(f.b[2][I0]),       \
+          "=&v"(f.b[3][I0]), "=&v"(f.b[4][I0]), "=&v"(f.b[5][I0]), "=&v"(f.b[6][I0]),    \
+          "=&v"(f.b[7][I0]), "=&v"(f.a[I1]), "=&v"(f.b[0][I1]), "=&v"(f.b[1][I1]),       \
+          "=&v"(f.b[2][I1]), "=&v"(f.b[3][I1]), "=&v"(f.b[4][I1]), "=&v"(f.b[5][I1]),    \
+          "=&v"(f.b[6][I1]), "=&v"(f.b[7][I1])                                           \
+        : "v"(wa), "v"(xa))
+    PF_XR8_HALF(0, 1, 0, 0);
+    PF_XR8_HALF(2, 3, 2048, 2048);
+#undef PF_XR8_HALF
+}
+
 template <int TB, int KP, int NS>
 __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int wg_per_group, int per_wg)
 {
-    constexpr int kKsMax = 16;                          // k-blocks per split, at most
+    constexpr int kKsMax = TB <= 4 ? 16 : 8;            // k-blocks per split, at most
     constexpr int kXBytes = TB * kKsMax * 1024;         // resident token slice
     constexpr int kXPerWave = TB * kKsMax / 4;          // token DMAs per wave per slice
     constexpr int kSlot = KP * 1024 + 256;              // KP k-blocks of 16 rows + 64 scales
     constexpr int kLw = KP + 1;                         // DMAs per wave per stage
     static_assert(kLw * (NS - 1) <= 63, "vmcnt range");
     static_assert(KP == 2 || KP == 4, "lds_stage reads 2 or 4 k-blocks");
-    __shared__ __attribute__((aligned(16))) int8_t xl[kXBytes + 256];
+    constexpr int kXsBytes = TB <= 4 ? 256 : 512;       // token scales: 64 or 128
+    __shared__ __attribute__((aligned(16))) int8_t xl[kXBytes + kXsBytes];
     __shared__ __attribute__((aligned(16))) int8_t ring[4][NS * kSlot];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -437,6 +476,7 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int wg_per_group
                   xl + q * 1024);
         }
         if (wave == 0) dma4(pp.xs + min(lane, pp.M - 1), xl + kXBytes);
+        if (TB > 4 && wave == 1) dma4(pp.xs + min(64 + lane, pp.M - 1), xl + kXBytes + 256);
     };
 
     // ---- issue side: this wave's weight rows of the item being loaded
@@ -561,14 +601,16 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int wg_per_group
 // five 2-k-block stages, 79 KB at TB = 2) fits twice on a compute unit: the
 // grid targets two workgroups per CU, so while one of them waits for its first
 // data the other streams, and launches of other streams find room.  Larger
-// token slices take 4-k-block stages at one workgroup per CU.  Each workgroup
+// token slices take 4-k-block stages at one workgroup per CU; 65 to 128 tokens
+// run as eight blocks with slices of at most 8 k-blocks (64 KB).  Each workgroup
 // takes a run of tiles inside one (pair, split) slice.
 hipError_t launch_gemm_xres(const StackStep& S, int token_blocks, hipStream_t s)
 {
     const int groups = S.npairs * S.splits;              // (pair, split) token slices
     const int per_group = S.tile_off[S.nproj];           // tiles per slice
     if (groups <= 0 || per_group <= 0) return hipSuccess;
-    if (S.kb_per_split > 16 || (S.splits > 1 && !S.partials)) return hipErrorInvalidValue;
+    if (token_blocks > 4 && token_blocks <= 8) token_blocks = 8;   // 65..128 tokens: eight blocks
+    if (S.kb_per_split > xres_max_kb(token_blocks) || (S.splits > 1 && !S.partials)) return hipErrorInvalidValue;
     const int target = token_blocks <= 2 ? 2 * kComputeUnits : kComputeUnits;
     int wpg = target / groups;
     if (wpg < 1) wpg = 1;
@@ -580,6 +622,7 @@ hipError_t launch_gemm_xres(const StackStep& S, int token_blocks, hipStream_t s)
         case 2: PF_LAUNCH((k_gemm_xres<2, 2, 5>), g, b, 0, s, S, wpg, per_wg); break;
         case 3: PF_LAUNCH((k_gemm_xres<3, 4, 4>), g, b, 0, s, S, wpg, per_wg); break;
         case 4: PF_LAUNCH((k_gemm_xres<4, 4, 4>), g, b, 0, s, S, wpg, per_wg); break;
+        case 8: PF_LAUNCH((k_gemm_xres<8, 4, 4>), g, b, 0, s, S, wpg, per_wg); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -158,8 +158,9 @@ def test_tiled_matches_oracle(M):
 @pytest.mark.parametrize("K", [64, 192, 256, 320, 1088])
 @pytest.mark.parametrize("M", [65, 256])
 def test_tiled_k_blocks_around_ring_depth(M, K):
-    """k-block counts below, at and just above the stage ring's depth, and odd."""
-    N = 520                              # two full 256-row tiles and 8 rows
+    """k-block counts below, at and just above the stage ring's depth, and odd.
+    522 rows (not a multiple of four) keep 65 tokens on the tiled kernel."""
+    N = 522                              # two full 256-row tiles and 10 rows
     W, ws, q, s = _proj(N, K, M, 900 + M + K)
     y = pf.gemm_i8_chunk(dev(W), dev(ws), dev(q), dev(s))
     np.testing.assert_array_equal(host(y), oracle.linear(W, ws, q, s))
@@ -188,6 +189,27 @@ def test_tiled_split_k_with_garbage_workspace(N, K, M):
     args = (dev(W), dev(ws), dev(q), dev(s))
     ref = oracle.linear(W, ws, q, s)
     for _ in range(3):
+        np.testing.assert_array_equal(host(pf.gemm_i8_chunk(*args, ws=wsp)), ref)
+
+
+@pytest.mark.parametrize("K", [512, 1088, 4096])
+@pytest.mark.parametrize("M", [65, 80, 113, 128])
+def test_xres128_matches_oracle(M, K):
+    """65 to 128 tokens on a small product (rows a multiple of four, aligned
+    output): the token-resident kernel with eight 16-token blocks, tokens past M
+    repeating row 0 and never stored.  K in one slice of at most 8 k-blocks
+    (512), or split into slices with a ragged last one (1088: 8 + 8 + 1) or into
+    eight (4096), the partials summed by the reduction.  Repeated calls on a
+    workspace that starts as garbage."""
+    N = 392                              # six 64-row tiles and 8 rows
+    W, ws, q, s = _proj(N, K, M, 1700 + M + K)
+    nb = pf.gemm_i8_chunk_workspace(N, K, M)
+    if K > 512:
+        assert nb >= 4 * M * N * ((K // 64 + 7) // 8)
+    wsp = torch.randint(0, 255, (max(nb, 16),), dtype=torch.uint8, device="cuda")
+    args = (dev(W), dev(ws), dev(q), dev(s))
+    ref = oracle.linear(W, ws, q, s)
+    for _ in range(2):
         np.testing.assert_array_equal(host(pf.gemm_i8_chunk(*args, ws=wsp)), ref)
 
 
