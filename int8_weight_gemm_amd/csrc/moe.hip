@@ -351,8 +351,9 @@ __global__ __launch_bounds__(1024) void k_group(const int* __restrict__ ids_g,
     extern __shared__ unsigned sel[];
     __shared__ int cnt[1024];
     __shared__ int scan[1024];
+    __shared__ int wsum[16];
     const int words = (T + 31) >> 5;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int np = T * k;
     int* ids_l = reinterpret_cast<int*>(sel + E * words);
     if (kLds) {
@@ -380,15 +381,19 @@ __global__ __launch_bounds__(1024) void k_group(const int* __restrict__ ids_g,
         atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
-    // inclusive scan of cnt[0..1024) (Hillis-Steele)
-    scan[tid] = cnt[tid];
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-        const int v = tid >= d ? scan[tid - d] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
+    // inclusive scan of cnt[0..1024): within each wave by lane shuffles, then
+    // the 16 wave totals
+    int v = cnt[tid];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(v, d);
+        if (lane >= d) v += o;
     }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    for (int i = 0; i < wave; ++i) v += wsum[i];
+    scan[tid] = v;
+    __syncthreads();
     if (tid < E) off[tid + 1] = scan[tid];
     if (tid == 0) off[0] = 0;
     for (int p = tid; p < T * k; p += 1024) {
