@@ -691,7 +691,11 @@ hipError_t launch_expert(const ExpertArgs& a, hipStream_t s)
 
 // ---------------------------------------------------------------------------
 // Weighted combine: out[t][j] = +0, then over the token's experts in ascending
-// id out = fl(out + fl(w * y)).
+// id out = fl(out + fl(w * y)).  The rows of eight experts at a time are loaded
+// before any of them is added, so their loads are in flight together; the adds
+// keep the ascending order.
+constexpr int kCbBatch = 8;
+
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ypair,
                                                  const int* __restrict__ comb_row,
                                                  const float* __restrict__ comb_w, int k, int H,
@@ -699,16 +703,30 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ypair
 {
     const int t = blockIdx.x;
     float* o_row = out + (int64_t)t * H;
-    if (((uintptr_t)o_row & 15) == 0) {                 // four outputs per lane, 16-byte accesses
+    const int* rows = comb_row + (int64_t)t * k;
+    const float* wts = comb_w + (int64_t)t * k;
+    if (((uintptr_t)o_row & 15) == 0 && (H & 3) == 0) {   // four outputs per lane, 16-byte accesses
         for (int j = threadIdx.x * 4; j < H; j += 1024) {
             float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            for (int r = 0; r < k; ++r) {
-                const float wr = comb_w[t * k + r];
-                const float4 y = *reinterpret_cast<const float4*>(ypair + (int64_t)comb_row[t * k + r] * H + j);
-                o.x = o.x + wr * y.x;
-                o.y = o.y + wr * y.y;
-                o.z = o.z + wr * y.z;
-                o.w = o.w + wr * y.w;
+            for (int r0 = 0; r0 < k; r0 += kCbBatch) {
+                float4 y[kCbBatch];
+                float wr[kCbBatch];
+#pragma unroll
+                for (int u = 0; u < kCbBatch; ++u) {
+                    if (r0 + u < k) {
+                        wr[u] = wts[r0 + u];
+                        y[u] = *reinterpret_cast<const float4*>(ypair + (int64_t)rows[r0 + u] * H + j);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kCbBatch; ++u) {
+                    if (r0 + u < k) {
+                        o.x = o.x + wr[u] * y[u].x;
+                        o.y = o.y + wr[u] * y[u].y;
+                        o.z = o.z + wr[u] * y[u].z;
+                        o.w = o.w + wr[u] * y[u].w;
+                    }
+                }
             }
             *reinterpret_cast<float4*>(o_row + j) = o;
         }
@@ -717,7 +735,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ypair
     for (int j = threadIdx.x; j < H; j += 256) {
         float o = 0.0f;
         for (int r = 0; r < k; ++r) {
-            const float c = comb_w[t * k + r] * ypair[(int64_t)comb_row[t * k + r] * H + j];
+            const float c = wts[r] * ypair[(int64_t)rows[r] * H + j];
             o = o + c;
         }
         o_row[j] = o;
