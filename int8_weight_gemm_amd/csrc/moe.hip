@@ -302,22 +302,17 @@ __global__ __launch_bounds__(1024) void k_softmax_topk(const float* __restrict__
         if (lane == 0) cand[wave * kw + j] = best;
     }
     __syncthreads();
-    if (wave != 0) return;
-    const int nc = nw * kw;                              // <= 512: up to 8 per lane
-    unsigned long long c[kSmMaxE / 64 * kSmMaxK / 64];
-#pragma unroll
-    for (int i = 0; i < kSmMaxE / 64 * kSmMaxK / 64; ++i) c[i] = lane + 64 * i < nc ? cand[lane + 64 * i] : 0ull;
-    for (int j = 0; j < k; ++j) {
-        unsigned long long mine = 0ull;
-#pragma unroll
-        for (int i = 0; i < kSmMaxE / 64 * kSmMaxK / 64; ++i) mine = c[i] > mine ? c[i] : mine;
-        const unsigned long long best = wave_max_u64(mine);
-#pragma unroll
-        for (int i = 0; i < kSmMaxE / 64 * kSmMaxK / 64; ++i)
-            if (c[i] == best) c[i] = 0ull;
-        if (lane == 0) {
-            ids[(int64_t)t * k + j] = (int)(0xffffffffu - (unsigned)(best & 0xffffffffu));
-            w[(int64_t)t * k + j] = __uint_as_float((unsigned)(best >> 32));
+    // the k best of the nw * kw candidates: candidate i's place is the number of
+    // candidates above it (the keys are distinct), so every candidate finds its
+    // place at once and the first k write their (id, weight)
+    const int nc = nw * kw;
+    if (e < nc) {
+        const unsigned long long mine = cand[e];
+        int place = 0;
+        for (int j = 0; j < nc; ++j) place += cand[j] > mine;
+        if (place < k) {
+            ids[(int64_t)t * k + place] = (int)(0xffffffffu - (unsigned)(mine & 0xffffffffu));
+            w[(int64_t)t * k + place] = __uint_as_float((unsigned)(mine >> 32));
         }
     }
 }
