@@ -37,6 +37,13 @@
  *     (same stream); calls that overlap on one workspace race.
  *   - Input activations must be finite; results for NaN or Inf inputs are
  *     unspecified.
+ *   - State kept across calls: a per-device architecture check and, for
+ *     pf_prefill_stack, two library-owned streams per device (default
+ *     priority) with their fork/join events, created on first use and kept
+ *     until the process ends.  A mutex per device serialises the stack calls
+ *     that use them, so concurrent stack calls from several host threads on
+ *     one device run one after the other; every other entry point is
+ *     reentrant.
  *   - K of every product must be a positive multiple of 64 and at most 131072,
  *     which keeps every int32 accumulator exact (131072 * 127 * 127 < 2^31).
  *
@@ -56,6 +63,9 @@
 extern "C" {
 #endif
 
+/* The entry points below are the library's only exported symbols. */
+#define PF_API __attribute__((visibility("default")))
+
 typedef int pf_status;
 #define PF_OK          0
 #define PF_EINVAL     -1  /* bad argument: null, size, alignment, overlap       */
@@ -65,40 +75,40 @@ typedef int pf_status;
 #define PF_EINTERNAL  -5  /* unexpected internal error                           */
 
 /* Human-readable name of a status code (static string). */
-const char* pf_status_string(pf_status status);
+PF_API const char* pf_status_string(pf_status status);
 
 /* Checks that a gfx950 device is current.  Every entry point calls it on first
  * use; calling it first only moves the cost.  PF_ENODEV without a device. */
-pf_status pf_init(void);
+PF_API pf_status pf_init(void);
 
 /* Zero-fills `bytes` of device memory on `stream` (a fill kernel, no memset
  * node); a convenience for callers that want a defined workspace. */
-pf_status pf_workspace_clear(void* workspace, size_t bytes, void* stream);
+PF_API pf_status pf_workspace_clear(void* workspace, size_t bytes, void* stream);
 
 /* Per-token symmetric int8 quantisation of a chunk, done once per chunk
  * ("Batched Prefill", §The Solution: activations are quantised once per batch,
  * not once per weight row).
  * x [M][ldx] f32 (first K of each row used) -> xq [M][K] int8, a_scale [M] f32.
  * M = 0 is a no-op.  ldx >= K, ldx % 4 == 0. */
-pf_status pf_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx,
+PF_API pf_status pf_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx,
                           int8_t* xq, float* a_scale, void* stream);
 
 /* Workspace bytes pf_gemm_i8_chunk may use to split K across workgroups
  * (0 is always accepted; a larger workspace only adds parallelism). */
-size_t pf_gemm_i8_chunk_workspace(int64_t N, int64_t K, int64_t M);
+PF_API size_t pf_gemm_i8_chunk_workspace(int64_t N, int64_t K, int64_t M);
 
 /* One projection over a chunk of M tokens ("Batched Prefill", §The Solution:
  * each weight row is loaded once and dotted against every token column).
  * W [N][K] int8, w_scale [N] f32, xq [M][K] int8, a_scale [M] f32 -> y [M][N]
  * f32 (token-major).  Chooses an MFMA kernel by M (skinny M <= 64, tiled above).
  * workspace may be NULL with ws_bytes 0. */
-pf_status pf_gemm_i8_chunk(const int8_t* W, const float* w_scale, int64_t N, int64_t K,
+PF_API pf_status pf_gemm_i8_chunk(const int8_t* W, const float* w_scale, int64_t N, int64_t K,
                            const int8_t* xq, const float* a_scale, int64_t M, float* y,
                            void* workspace, size_t ws_bytes, void* stream);
 
 /* The per-token baseline ("Batched Prefill", §The Problem: one GEMV per token,
  * every weight re-read per token): y [N] = product of W with one token xq [K]. */
-pf_status pf_gemv_i8(const int8_t* W, const float* w_scale, int64_t N, int64_t K,
+PF_API pf_status pf_gemv_i8(const int8_t* W, const float* w_scale, int64_t N, int64_t K,
                      const int8_t* xq, const float* a_scale, float* y, void* stream);
 
 /* Projection set of one layer, in this order: q, k, v, o, gate, up, down.
@@ -115,15 +125,29 @@ typedef struct {
     int64_t hidden;          /* H */
     int64_t ffn;             /* F */
     const pf_layer* layers;  /* host array of n_layers */
+    /* Optional (NULL: none): a second host array of n_layers describing a second
+     * copy of the same weights at other addresses.  Chunk c reads its weights
+     * from it when c is odd (the per-token mode ignores it); with equal contents
+     * the results are unchanged.  Alternating two copies keeps one chunk's
+     * weights from being served to the next by a last-level cache that can hold
+     * one copy, so a caller can measure the rate of the weight stream from
+     * DRAM alone. */
+    const pf_layer* layers_alt;
 } pf_stack;
 
 /* Statistics of one pf_prefill_stack call.  time_kernels is the only input:
  * set it to 1 to give every launch a pair of HIP events stamped when the kernel
  * itself starts and ends (hipExtLaunchKernelGGL) and get per-class device
- * times; kernels of the two chunk groups may overlap in time.  Algorithmic
- * bytes count each kernel's inputs read once and outputs written once: for a
- * product, weights + weight scales + quantised tokens + token scales + f32
- * outputs; for a quantisation, f32 inputs + int8 codes + scales. */
+ * times; kernels of the three chunk groups (one stream each) overlap in time,
+ * so the summed launch durations (product_ms, quant_ms) can exceed the call's
+ * elapsed time, while the busy times (the union of a class's launch intervals)
+ * cannot.  Algorithmic bytes count what the method must move, once: for the
+ * products of a (chunk, layer) pair the weights and their scales, one read of
+ * the quantised tokens and their scales per phase (the six products that share
+ * them read them once) and every f32 output written once; for a quantisation
+ * the f32 inputs, the int8 codes and the scales.  Traffic that the schedule
+ * adds (the down product's split-K int32 partials, written and read back) is
+ * reported apart as overhead_bytes. */
 typedef struct {
     int time_kernels;          /* in: 1 = time every launch                       */
     int per_token_mode;        /* out: 1 if the per-token GEMV path ran           */
@@ -138,10 +162,13 @@ typedef struct {
     double quant_alg_bytes;
     double product_ms;         /* summed device time of the products (time_kernels) */
     double quant_ms;           /* summed device time of the quantisations (time_kernels) */
+    double product_busy_ms;    /* time at least one product ran (time_kernels)    */
+    double quant_busy_ms;      /* time at least one quantisation ran (time_kernels) */
+    double overhead_bytes;     /* split-K partials written and read back          */
 } pf_stack_stats;
 
 /* Workspace bytes for pf_prefill_stack with this stack and chunk size. */
-size_t pf_prefill_stack_workspace(const pf_stack* stack, int64_t chunk);
+PF_API size_t pf_prefill_stack_workspace(const pf_stack* stack, int64_t chunk);
 
 /* Sweeps a prompt of P tokens through every layer's projection set, one chunk
  * of `chunk` tokens at a time, the last chunk ragged ("Single-pass prefill",
@@ -156,7 +183,7 @@ size_t pf_prefill_stack_workspace(const pf_stack* stack, int64_t chunk);
  * instead (the per-token baseline); the bytes of y and proj are identical
  * ("Batched Prefill", §Correctness).  stats, when not NULL, is filled in and the
  * call then synchronises the stream (see pf_stack_stats). */
-pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int64_t chunk,
+PF_API pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int64_t chunk,
                            float* y, float* proj, void* workspace, size_t ws_bytes,
                            pf_stack_stats* stats, void* stream);
 
@@ -178,7 +205,7 @@ typedef struct {
 } pf_moe;
 
 /* Workspace bytes for pf_moe_chunk with T tokens. */
-size_t pf_moe_chunk_workspace(const pf_moe* moe, int64_t T);
+PF_API size_t pf_moe_chunk_workspace(const pf_moe* moe, int64_t T);
 
 /* Expert prefill of one chunk of T tokens x [T][H] f32, all on the device:
  *   logits[t][e] = sum over k ascending of fl(W_router[e][k] * x[t][k]) (f32,
@@ -194,13 +221,13 @@ size_t pf_moe_chunk_workspace(const pf_moe* moe, int64_t T);
  *     out[t][j] = fl(out[t][j] + fl(weights_e * y_e[j])).
  * ids [T][top_k] int32, weights [T][top_k] f32, out [T][H] f32.
  * Limits: T * top_k <= 65536, E <= 1024, top_k <= 32, E * ceil(T / 32) <= 12288. */
-pf_status pf_moe_chunk(const pf_moe* moe, const float* x, int64_t T, int32_t* ids,
+PF_API pf_status pf_moe_chunk(const pf_moe* moe, const float* x, int64_t T, int32_t* ids,
                        float* weights, float* out, void* workspace, size_t ws_bytes,
                        void* stream);
 
 /* The correctly rounded binary32 exp used by the softmax above, applied
  * elementwise to x [n] -> y [n] (exposed so that it can be checked). */
-pf_status pf_expf_cr(const float* x, int64_t n, float* y, void* stream);
+PF_API pf_status pf_expf_cr(const float* x, int64_t n, float* y, void* stream);
 
 #ifdef __cplusplus
 }

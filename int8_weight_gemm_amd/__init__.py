@@ -40,7 +40,7 @@ class _Layer(ctypes.Structure):
 
 class _Stack(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int64), ("hidden", ctypes.c_int64), ("ffn", ctypes.c_int64),
-                ("layers", ctypes.POINTER(_Layer))]
+                ("layers", ctypes.POINTER(_Layer)), ("layers_alt", ctypes.POINTER(_Layer))]
 
 
 class StackStats(ctypes.Structure):
@@ -50,7 +50,8 @@ class StackStats(ctypes.Structure):
                 ("elapsed_ms", ctypes.c_double), ("product_launches", ctypes.c_int64),
                 ("quant_launches", ctypes.c_int64), ("product_alg_bytes", ctypes.c_double),
                 ("quant_alg_bytes", ctypes.c_double), ("product_ms", ctypes.c_double),
-                ("quant_ms", ctypes.c_double)]
+                ("quant_ms", ctypes.c_double), ("product_busy_ms", ctypes.c_double),
+                ("quant_busy_ms", ctypes.c_double), ("overhead_bytes", ctypes.c_double)]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -186,21 +187,30 @@ def expf_cr(x: torch.Tensor) -> torch.Tensor:
 
 class Stack:
     """A projection stack resident in HBM: weights[l] = 7 int8 tensors (q, k, v, o,
-    gate, up, down), scales[l] = 7 f32 tensors."""
+    gate, up, down), scales[l] = 7 f32 tensors.  ``alt``, optional, is a second
+    (weights, scales) copy of the same values that odd chunks read (pf_stack's
+    layers_alt)."""
 
-    def __init__(self, weights, scales):
+    def __init__(self, weights, scales, alt=None):
         self.L = len(weights)
         self.H = weights[0][0].shape[1]
         self.F = weights[0][4].shape[0]
-        self.weights, self.scales = weights, scales
-        self._layers = (_Layer * self.L)()
+        self.weights, self.scales, self.alt = weights, scales, alt
+        self._layers = self._table(weights, scales)
+        self._alt = self._table(*alt) if alt is not None else None
+        self._desc = _Stack(self.L, self.H, self.F, ctypes.cast(self._layers, ctypes.POINTER(_Layer)),
+                            ctypes.cast(self._alt, ctypes.POINTER(_Layer)) if self._alt is not None
+                            else None)
+
+    def _table(self, weights, scales):
+        tab = (_Layer * self.L)()
         for l in range(self.L):
             for j in range(NPROJ):
                 _dev(weights[l][j], torch.int8, f"W[{l}][{j}]")
                 _dev(scales[l][j], torch.float32, f"w_scale[{l}][{j}]")
-                self._layers[l].W[j] = weights[l][j].data_ptr()
-                self._layers[l].w_scale[j] = scales[l][j].data_ptr()
-        self._desc = _Stack(self.L, self.H, self.F, ctypes.cast(self._layers, ctypes.POINTER(_Layer)))
+                tab[l].W[j] = weights[l][j].data_ptr()
+                tab[l].w_scale[j] = scales[l][j].data_ptr()
+        return tab
 
     @property
     def weight_bytes(self) -> int:

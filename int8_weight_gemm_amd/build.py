@@ -21,6 +21,8 @@ HIPCC_FLAGS = [
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # host code exports only the C entry points (PF_API in libprefill.h)
+    "-Xarch_host", "-fvisibility=hidden",
 ]
 
 

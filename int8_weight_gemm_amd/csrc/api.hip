@@ -93,6 +93,27 @@ SkinnyPlan unsplit(int64_t N, int64_t K)
     return SkinnyPlan{(int)((N + kSkinnyRows - 1) / kSkinnyRows), 1, (int)(K / 64), 0};
 }
 
+// Plan of a standalone product of at most 64 tokens; xres_shape: the output
+// rows suit the token-resident kernel (16-byte aligned, N a multiple of 4).
+SkinnyPlan plan_chunk_small(int64_t N, int64_t K, bool xres_shape)
+{
+    SkinnyPlan p = plan_skinny(N, K, (N + kSkinnyRows - 1) / kSkinnyRows);
+    // splits longer than the token-resident kernel takes: with enough tiles
+    // for half the compute units the streamed kernel runs the whole K per
+    // tile (no partials, no second launch)
+    if (p.kb_per_split > 16 && p.tiles_n >= kComputeUnits / 2) p = unsplit(N, K);
+    // a product of at most a few MB is over before a second launch (the
+    // split's reduction) would start: split only as far as the token-resident
+    // kernel needs (16 k-blocks per split)
+    if (N * K <= (8 << 20) && xres_shape) {
+        const int nkb = (int)(K / 64);
+        const int sp = (nkb + 15) / 16;
+        p.kb_per_split = (nkb + sp - 1) / sp;
+        p.splits = (nkb + p.kb_per_split - 1) / p.kb_per_split;
+    }
+    return p;
+}
+
 size_t split_bytes(int64_t N, int64_t M, const SkinnyPlan& p)
 {
     if (p.splits <= 1) return 0;
@@ -335,12 +356,15 @@ pf_status validate_stack(const pf_stack* st)
     if (!st || !st->layers || st->n_layers <= 0 || st->hidden <= 0 || st->ffn <= 0)
         return PF_EINVAL;
     if (!valid_k(st->hidden) || !valid_k(st->ffn)) return PF_EINVAL;
-    for (int64_t l = 0; l < st->n_layers; ++l)
-        for (int j = 0; j < PF_NPROJ; ++j) {
-            const pf_layer& ly = st->layers[l];
-            if (!ly.W[j] || !ly.w_scale[j] || !aligned16(ly.W[j]) || !aligned4(ly.w_scale[j]))
-                return PF_EINVAL;
-        }
+    for (const pf_layer* tab : {st->layers, st->layers_alt}) {
+        if (!tab) continue;
+        for (int64_t l = 0; l < st->n_layers; ++l)
+            for (int j = 0; j < PF_NPROJ; ++j) {
+                const pf_layer& ly = tab[l];
+                if (!ly.W[j] || !ly.w_scale[j] || !aligned16(ly.W[j]) || !aligned4(ly.w_scale[j]))
+                    return PF_EINVAL;
+            }
+    }
     return PF_OK;
 }
 
@@ -398,6 +422,12 @@ pf_status validate_moe(const pf_moe* m)
 double product_bytes(int64_t N, int64_t K, int64_t M)
 {
     return (double)N * K + 4.0 * N + (double)M * K + 4.0 * M + 4.0 * M * N;
+}
+
+// The same without the token read, for products that share one token read.
+double weight_out_bytes(int64_t N, int64_t K, int64_t M)
+{
+    return (double)N * K + 4.0 * N + 4.0 * M * N;
 }
 
 // Library-owned streams per device, one per chunk group after the first, which
@@ -475,6 +505,7 @@ public:
         if (timed_) kinds_.push_back(k);
         return PF_OK;
     }
+    void overhead(double bytes) { overhead_ += bytes; }
     pf_status end()
     {
         if (!on_) return PF_OK;
@@ -483,10 +514,33 @@ public:
         float ms = 0.0f;
         if (hipEventElapsedTime(&ms, t0_, t1_) != hipSuccess) return fail();
         total_ms_ = ms;
+        // per launch its own duration, and its interval on the call's clock
+        // (launches of different chunk groups may overlap in time)
+        std::vector<std::pair<double, double>> iv[2];
         for (size_t i = 0; i < kinds_.size(); ++i) {
-            if (hipEventElapsedTime(&ms, events_[2 * i], events_[2 * i + 1]) != hipSuccess)
+            float a = 0.0f, b = 0.0f;
+            if (hipEventElapsedTime(&ms, events_[2 * i], events_[2 * i + 1]) != hipSuccess ||
+                hipEventElapsedTime(&a, t0_, events_[2 * i]) != hipSuccess ||
+                hipEventElapsedTime(&b, t0_, events_[2 * i + 1]) != hipSuccess)
                 return fail();
             ms_[kinds_[i]] += ms;
+            iv[kinds_[i]].emplace_back(a, b);
+        }
+        // busy time of a kernel class: the union of its launches' intervals
+        for (int k = 0; k < 2; ++k) {
+            std::sort(iv[k].begin(), iv[k].end());
+            double busy = 0.0, lo = 0.0, hi = -1.0;
+            for (const auto& p : iv[k]) {
+                if (p.first > hi) {
+                    if (hi > lo) busy += hi - lo;
+                    lo = p.first;
+                    hi = p.second;
+                } else {
+                    hi = std::max(hi, p.second);
+                }
+            }
+            if (hi > lo) busy += hi - lo;
+            busy_[k] = busy;
         }
         return PF_OK;
     }
@@ -501,6 +555,9 @@ public:
         st->product_alg_bytes = bytes_[kProduct];
         st->quant_ms = timed_ ? ms_[kQuant] : 0.0;
         st->product_ms = timed_ ? ms_[kProduct] : 0.0;
+        st->quant_busy_ms = timed_ ? busy_[kQuant] : 0.0;
+        st->product_busy_ms = timed_ ? busy_[kProduct] : 0.0;
+        st->overhead_bytes = overhead_;
     }
 
 private:
@@ -517,6 +574,8 @@ private:
     int64_t launches_[2] = {0, 0};
     double bytes_[2] = {0.0, 0.0};
     double ms_[2] = {0.0, 0.0};
+    double busy_[2] = {0.0, 0.0};
+    double overhead_ = 0.0;
     double total_ms_ = 0.0;
 };
 
@@ -541,6 +600,11 @@ struct StackRun {
     hipStream_t s;
     int ng = 1;            // chunk groups, each on its own stream (chunk c in group c % ng)
 
+    // the layer table chunk c reads (the second copy for odd chunks, if any)
+    const pf_layer& layer(int64_t c, int64_t l) const
+    {
+        return (st->layers_alt && (c & 1)) ? st->layers_alt[l] : st->layers[l];
+    }
     int64_t H() const { return st->hidden; }
     int64_t F() const { return st->ffn; }
     int64_t NT() const { return 5 * st->hidden + 2 * st->ffn; }
@@ -665,7 +729,7 @@ struct StackRun {
         D.rows[0] = (int)H();
         D.yoff[0] = (int)offs(6);
         D.tile_off[1] = (int)(skinny ? (H() + kSkinnyRows - 1) / kSkinnyRows : ((H() + kTiledRows - 1) / kTiledRows) * tm);
-        double qa_bytes = 0, qd_bytes = 0, a_bytes = 0, d_bytes = 0;
+        double qa_bytes = 0, qd_bytes = 0, a_bytes = 0, d_bytes = 0, part_bytes = 0;
         int rows_a = 0, rows_d = 0;
         auto rebuild = [&](QuantPair& q, int64_t c, int64_t l_prev, bool last) {
             // rows of (c, l_prev)'s down product, from its split partials
@@ -673,7 +737,7 @@ struct StackRun {
             q.part = reinterpret_cast<const int*>(sl + lay.part);
             q.part_stride = ch * H();
             q.splits = sd;
-            q.ws = st->layers[l_prev].w_scale[6];
+            q.ws = layer(c, l_prev).w_scale[6];
             q.as = reinterpret_cast<const float*>(sl + lay.sb);
             q.h = rows(c, l_prev) + offs(6);
             q.ldh = NT();
@@ -682,7 +746,7 @@ struct StackRun {
         for (size_t i = 0; i < cs.size(); ++i) {
             const int64_t c = cs[i], l = step - start(c / ng);
             const int64_t c0 = c * ch, M = std::min(ch, P - c0);
-            const pf_layer& ly = st->layers[l];
+            const pf_layer& ly = layer(c, l);
             char* sl = slot(c);
             int8_t* a = reinterpret_cast<int8_t*>(sl + lay.a);
             int8_t* b = reinterpret_cast<int8_t*>(sl + lay.b);
@@ -695,7 +759,7 @@ struct StackRun {
                 q0.ld = H();
             } else if (rebuild_d) {
                 rebuild(q0, c, l - 1, false);
-                qa_bytes += (double)M * H() * 4 * sd + (double)M * H() * 4;
+                part_bytes += (double)M * H() * 4 * sd;       // the partials' re-read
             } else {
                 q0.src = rows(c, l - 1) + offs(6);
                 q0.ld = NT();
@@ -712,10 +776,12 @@ struct StackRun {
             q1.row0 = rows_d;
             rows_d += (int)M;
             StepPair& pa = A.pair[A.npairs++];
+            // the six products share one read of the quantised tokens
+            a_bytes += (double)M * H() + 4.0 * M;
             for (int j = 0; j < 6; ++j) {
                 pa.W[j] = ly.W[j];
                 pa.ws[j] = ly.w_scale[j];
-                a_bytes += product_bytes(rowsA[j], H(), M);
+                a_bytes += weight_out_bytes(rowsA[j], H(), M);
             }
             pa.X = a;
             pa.xs = sa;
@@ -731,6 +797,7 @@ struct StackRun {
             pd.part = reinterpret_cast<int*>(sl + lay.part);
             pd.M = (int)M;
             d_bytes += product_bytes(H(), F(), M);
+            if (rebuild_d) part_bytes += (double)M * H() * 4 * sd;   // the partials' write
             qa_bytes += (double)M * H() * 5 + M * 4.0;
             qd_bytes += (double)M * F() * 5 + M * 4.0;
         }
@@ -741,7 +808,9 @@ struct StackRun {
             rebuild(qf, fin, L - 1, true);
             qf.row0 = rows_a;
             rows_a += (int)M;
-            qa_bytes += (double)M * H() * 4 * (sd + 2);
+            // completes the last down product's epilogue: its output bytes are
+            // the product's; the partials' re-read is overhead
+            part_bytes += (double)M * H() * 4 * sd;
             fin = -1;
         }
         qa.total_rows = rows_a;
@@ -749,7 +818,11 @@ struct StackRun {
         pf_status r = PF_OK;
         if (qa.npairs > 0)
             r = rec.run(Recorder::kQuant, qa_bytes, [&] { return launched(launch_quantize_step(qa, sg)); }, sg);
-        if (r || cs.empty()) return r;
+        if (r) return r;
+        if (cs.empty()) {
+            rec.overhead(part_bytes);
+            return PF_OK;
+        }
         r = rec.run(Recorder::kProduct, a_bytes, [&] {
             if (!skinny) return launched(launch_gemm_tiled_step(A, ch, sg));
             return launched(xres_a ? launch_gemm_xres(A, tb, sg) : launch_gemm_stream(A, tb, sg));
@@ -760,6 +833,7 @@ struct StackRun {
             return launched(skinny ? launch_gemm_xres(D, tb, sg) : launch_gemm_tiled_step(D, ch, sg));
         }, sg);
         if (r) return r;
+        rec.overhead(part_bytes);
         if (rebuild_d)
             for (int64_t c : cs)
                 if (step - start(c / ng) == L - 1) fin = c;
@@ -790,11 +864,11 @@ struct StackRun {
                 GemmSet set;
                 std::memset(&set, 0, sizeof(set));
                 set.nprob = 6;
-                double bytes = 0;
+                double bytes = (double)H() + 4.0;        // the token, read once
                 for (int j = 0; j < 6; ++j) {
                     make_skinny(set.p[j], ly.W[j], ly.w_scale[j], rowsA[j], H(), a, H(), sa, 1,
                                 out + offs(j), NT(), unsplit(rowsA[j], H()), none, 1);
-                    bytes += product_bytes(rowsA[j], H(), 1);
+                    bytes += weight_out_bytes(rowsA[j], H(), 1);
                 }
                 finish_set(set, 0);
                 r = rec.run(Recorder::kProduct, bytes, [&] { return launched(launch_gemv(set, s)); });
@@ -821,6 +895,25 @@ struct StackRun {
         return PF_OK;
     }
 };
+
+// 65 to 128 tokens: products of at most this many weight bytes go through the
+// token-resident kernel (eight 16-token blocks, K split into slices of at most
+// 8 k-blocks) instead of the tiled one, whose 256-row tiles are then too few.
+constexpr int64_t kXres128MaxBytes = 16 << 20;
+
+bool xres128(int64_t N, int64_t K, int64_t M)
+{
+    return M > 64 && M <= 128 && N * K <= kXres128MaxBytes;
+}
+
+SkinnyPlan plan_xres128(int64_t N, int64_t K)
+{
+    SkinnyPlan p = unsplit(N, K);
+    const int nkb = (int)(K / 64);
+    p.kb_per_split = std::min(nkb, xres_max_kb(8));
+    p.splits = (nkb + p.kb_per_split - 1) / p.kb_per_split;
+    return p;
+}
 
 }  // namespace
 
@@ -881,25 +974,6 @@ pf_status pf_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int
     }
 }
 
-// 65 to 128 tokens: products of at most this many weight bytes go through the
-// token-resident kernel (eight 16-token blocks, K split into slices of at most
-// 8 k-blocks) instead of the tiled one, whose 256-row tiles are then too few.
-constexpr int64_t kXres128MaxBytes = 16 << 20;
-
-bool xres128(int64_t N, int64_t K, int64_t M)
-{
-    return M > 64 && M <= 128 && N * K <= kXres128MaxBytes;
-}
-
-SkinnyPlan plan_xres128(int64_t N, int64_t K)
-{
-    SkinnyPlan p = unsplit(N, K);
-    const int nkb = (int)(K / 64);
-    p.kb_per_split = std::min(nkb, xres_max_kb(8));
-    p.splits = (nkb + p.kb_per_split - 1) / p.kb_per_split;
-    return p;
-}
-
 size_t pf_gemm_i8_chunk_workspace(int64_t N, int64_t K, int64_t M)
 {
     if (N <= 0 || N > INT32_MAX || !valid_k(K) || M <= 0 || M > INT32_MAX) return 0;
@@ -907,8 +981,9 @@ size_t pf_gemm_i8_chunk_workspace(int64_t N, int64_t K, int64_t M)
         const size_t tiled = split_bytes(N, M, plan_tiled(N, K, M));
         return xres128(N, K, M) ? std::max(tiled, split_bytes(N, M, plan_xres128(N, K))) : tiled;
     }
-    const SkinnyPlan p = plan_skinny(N, K, (N + kSkinnyRows - 1) / kSkinnyRows);
-    return split_bytes(N, M, p);
+    // the output's alignment picks the plan: room for either
+    return std::max(split_bytes(N, M, plan_chunk_small(N, K, true)),
+                    split_bytes(N, M, plan_chunk_small(N, K, false)));
 }
 
 pf_status pf_gemm_i8_chunk(const int8_t* W, const float* w_scale, int64_t N, int64_t K,
@@ -933,20 +1008,7 @@ pf_status pf_gemm_i8_chunk(const int8_t* W, const float* w_scale, int64_t N, int
         set.nprob = 1;
         int tile_tokens = 0;
         if (M <= 64) {
-            SkinnyPlan p = plan_skinny(N, K, (N + kSkinnyRows - 1) / kSkinnyRows);
-            // splits longer than the token-resident kernel takes: with enough
-            // tiles for half the compute units the streamed kernel runs the
-            // whole K per tile (no partials, no second launch)
-            if (p.kb_per_split > 16 && p.tiles_n >= kComputeUnits / 2) p = unsplit(N, K);
-            // a product of at most a few MB is over before a second launch (the
-            // split's reduction) would start: split only as far as the
-            // token-resident kernel needs (16 k-blocks per split)
-            if (N * K <= (8 << 20) && xres_fits_shape(N, y)) {
-                const int nkb = (int)(K / 64);
-                const int sp = (nkb + 15) / 16;
-                p.kb_per_split = (nkb + sp - 1) / sp;
-                p.splits = (nkb + p.kb_per_split - 1) / p.kb_per_split;
-            }
+            SkinnyPlan p = plan_chunk_small(N, K, xres_fits_shape(N, y));
             if (!workspace || ws_bytes < split_bytes(N, M, p)) p = unsplit(N, K);
             if (workspace && overlap(workspace, ws_bytes, y, yb)) return PF_EINVAL;
             char* scratch = static_cast<char*>(workspace);
@@ -1001,8 +1063,14 @@ pf_status pf_gemv_i8(const int8_t* W, const float* w_scale, int64_t N, int64_t K
 
 size_t pf_prefill_stack_workspace(const pf_stack* stack, int64_t chunk)
 {
-    if (!stack || stack->hidden <= 0 || stack->ffn <= 0 || chunk <= 0) return 0;
-    return stack_layout(stack->n_layers, stack->hidden, stack->ffn, chunk).total;
+    if (!stack || stack->n_layers <= 0 || stack->hidden <= 0 || stack->ffn <= 0 || chunk <= 0) return 0;
+    // A call runs chunks of min(chunk, P) tokens.  The layout grows with the
+    // chunk inside each of its two regimes (up to 64 tokens: more slots and
+    // split partials; above: fewer slots), so the largest of the two regime
+    // tops covers every prompt length.
+    const int64_t L = stack->n_layers, H = stack->hidden, F = stack->ffn;
+    return std::max(stack_layout(L, H, F, chunk).total,
+                    stack_layout(L, H, F, std::min<int64_t>(chunk, 64)).total);
 }
 
 pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int64_t chunk,

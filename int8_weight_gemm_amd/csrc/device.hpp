@@ -52,18 +52,4 @@ __device__ __forceinline__ int wave_sum(int v)
     return v;
 }
 
-// Agent-scope atomics and coherent loads for the split-K accumulators.
-__device__ __forceinline__ void atomic_add_agent(int* p, int v)
-{
-    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int load_agent(const int* p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_agent(int* p, int v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 }  // namespace pf

@@ -31,6 +31,27 @@ def test_library_exports_every_declared_symbol():
     assert not missing, missing
 
 
+def exported_c_functions():
+    """Defined, exported text symbols of libprefill.so with C linkage (names that
+    are not C++-mangled and not the toolchain's own)."""
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", pf.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    names = set()
+    for line in out.splitlines():
+        parts = line.split()
+        if len(parts) == 3 and parts[1] in "TtWw" and not parts[2].startswith("_"):
+            names.add(parts[2])
+    return sorted(names)
+
+
+def test_library_exports_exactly_the_header():
+    """The C-linkage functions the library exports are the header's entry points,
+    no more (internal helpers stay out of the ABI) and no fewer."""
+    assert exported_c_functions() == declared()
+
+
 def test_status_strings():
     assert pf.status_string(pf.PF_OK) == "PF_OK"
     assert "invalid" in pf.status_string(pf.PF_EINVAL)
@@ -108,3 +129,31 @@ def test_stack_validation():
     # chunk must be positive
     assert lib.pf_prefill_stack(ctypes.byref(st), P(0x300000), 4, 0, P(0x310000), None, P(0x400000), 1 << 20,
                                 None, None) == pf.PF_EINVAL
+
+
+@pytest.mark.parametrize("L,H,F,chunk,P", [(16, 1024, 4096, 128, 40), (32, 4096, 11008, 256, 64),
+                                           (3, 128, 320, 96, 75), (2, 1024, 4096, 32, 40)])
+def test_stack_workspace_query_covers_short_prompts(L, H, F, chunk, P):
+    """A prompt shorter than one chunk runs as a chunk of P tokens, whose layout
+    (more slots and split partials up to 64 tokens) can exceed the layout of the
+    requested chunk; the size query covers it, so the call gets past the
+    workspace check with exactly the queried size (and then stops at the device
+    check here, or runs on a GPU host)."""
+    if os.environ.get("PF_EXPECT_GPU"):
+        pytest.skip("running on a GPU host")
+    lib = pf.lib()
+    layers = (pf._Layer * L)()
+    for l in range(L):
+        for j in range(7):
+            layers[l].W[j] = 0x1000000 + (l * 7 + j) * 0x10000
+            layers[l].w_scale[j] = 0x8000000 + (l * 7 + j) * 0x10000
+    st = pf._Stack(L, H, F, ctypes.cast(layers, ctypes.POINTER(pf._Layer)))
+    need = lib.pf_prefill_stack_workspace(ctypes.byref(st), chunk)
+    assert need > 0
+    x, y, ws = P_(0x100000000), P_(0x200000000), P_(0x300000000)
+    assert lib.pf_prefill_stack(ctypes.byref(st), x, P, chunk, y, None, ws, need, None, None) == pf.PF_ENODEV
+    for p in range(1, chunk + 1):
+        assert lib.pf_prefill_stack(ctypes.byref(st), x, p, chunk, y, None, ws, need, None, None) == pf.PF_ENODEV
+
+
+P_ = ctypes.c_void_p

@@ -2,9 +2,9 @@
 
 Covers: a small stack compared in full (outputs and every projection), the
 350M-class stack (16 layers, hidden 1024, 747 tokens in 32-token chunks plus an
-11-token tail) on sampled tokens with chunk invariance and the per-token GEMV
+11-token tail) on every token with chunk invariance and the per-token GEMV
 mode, and the 7B-class stack (32 layers, hidden 4096, 2048 tokens in 512-token
-chunks) on sampled tokens.
+chunks) on every token.
 """
 import hashlib
 import os
@@ -106,14 +106,13 @@ def _digest(a):
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
 
 
-def test_stack350m_sampled_tokens_match_oracle(stack350m):
+def test_stack350m_all_tokens_match_oracle(stack350m):
+    """Every one of the 747 tokens (23 chunks of 32 and the 11-token tail)."""
     st, stack, x = stack350m
     say("stack350m chunk 32")
     y = host(run(stack, x, 32))
-    # first chunk, a middle chunk, the last full chunk and the 11-token tail
-    toks = np.r_[0:4, 31:33, 400:404, 704:708, 735:747]
-    ref = oracle.stack(st["weights"], st["scales"], st["x"][toks])
-    np.testing.assert_array_equal(y[toks], ref)
+    ref = oracle.stack(st["weights"], st["scales"], st["x"])
+    np.testing.assert_array_equal(y, ref)
     assert np.all(np.isfinite(y))
 
 
@@ -135,19 +134,47 @@ def test_stack350m_repeatable(stack350m):
         np.testing.assert_array_equal(host(stack.prefill(x, 32, ws)), y0)
 
 
-def test_stack7b_sampled_tokens_match_oracle():
+@pytest.fixture(scope="module")
+def stack7b():
     say("stack7b: generating 6.5 GB of weights")
     st = prefill_inputs.workload("stack7b")
     stack = to_stack(st)
     x = dev(st["x"])
     say("stack7b chunk 512")
     y = host(run(stack, x, 512))
+    return st, stack, x, y
+
+
+def test_stack7b_chunk_invariance(stack7b):
+    st, stack, x, y = stack7b
     assert np.all(np.isfinite(y))
-    toks = np.array([0, 511, 512, 1500, 2047])
-    say("stack7b oracle on", len(toks), "tokens")
-    ref = oracle.stack(st["weights"], st["scales"], st["x"][toks])
-    np.testing.assert_array_equal(y[toks], ref)
     say("stack7b chunk 1000 (ragged tail 48), 64 and 32 (skinny paths)")
     np.testing.assert_array_equal(host(run(stack, x, 1000)), y)
     np.testing.assert_array_equal(host(run(stack, x[:256].contiguous(), 64)), y[:256])
     np.testing.assert_array_equal(host(run(stack, x[:80].contiguous(), 32)), y[:80])
+
+
+# every token of the 2048-token prompt against the oracle, one 512-token chunk
+# per test (the oracle takes ~12 s per chunk on 16 host cores)
+@pytest.mark.parametrize("c", [0, 1, 2, 3])
+def test_stack7b_chunk_matches_oracle(stack7b, c):
+    st, stack, x, y = stack7b
+    say(f"stack7b oracle on tokens {512 * c} .. {512 * c + 511}")
+    ref = oracle.stack(st["weights"], st["scales"], st["x"][512 * c:512 * (c + 1)])
+    np.testing.assert_array_equal(y[512 * c:512 * (c + 1)], ref)
+
+
+@pytest.mark.parametrize("chunk", [16, 96])
+def test_second_weight_copy_same_bytes(chunk):
+    """Odd chunks reading a second copy of the weights (pf_stack layers_alt)
+    give the same bytes, including the projections."""
+    st = prefill_inputs.stack(L=3, H=256, F=1024, P=200, seed=27)
+    y_ref, proj_ref = oracle.stack(st["weights"], st["scales"], st["x"], return_proj=True)
+    wd = [[dev(w) for w in wl] for wl in st["weights"]]
+    sd = [[dev(s) for s in sl] for sl in st["scales"]]
+    alt = ([[w.clone() for w in wl] for wl in wd], [[s.clone() for s in sl] for sl in sd])
+    stack = pf.Stack(wd, sd, alt=alt)
+    proj = torch.empty((3, 200, 5 * 256 + 2 * 1024), dtype=torch.float32, device="cuda")
+    y = stack.prefill(dev(st["x"]), chunk, pf.workspace(stack.workspace_bytes(chunk)), proj=proj)
+    np.testing.assert_array_equal(host(y), y_ref)
+    np.testing.assert_array_equal(host(proj), proj_ref)
