@@ -77,8 +77,10 @@ typedef int pf_status;
 /* Human-readable name of a status code (static string). */
 PF_API const char* pf_status_string(pf_status status);
 
-/* Checks that a gfx950 device is current.  Every entry point calls it on first
- * use; calling it first only moves the cost.  PF_ENODEV without a device. */
+/* Checks that a gfx950 device is current and looks up the device address of
+ * pf_gemm_i8_chunk_noalloc's scratch array on it.  Every entry point checks
+ * the device on first use; calling this first only moves the cost.  PF_ENODEV
+ * without a device. */
 PF_API pf_status pf_init(void);
 
 /* Zero-fills `bytes` of device memory on `stream` (a fill kernel, no memset
@@ -105,6 +107,24 @@ PF_API size_t pf_gemm_i8_chunk_workspace(int64_t N, int64_t K, int64_t M);
 PF_API pf_status pf_gemm_i8_chunk(const int8_t* W, const float* w_scale, int64_t N, int64_t K,
                            const int8_t* xq, const float* a_scale, int64_t M, float* y,
                            void* workspace, size_t ws_bytes, void* stream);
+
+/* pf_gemm_i8_chunk for callers that cannot allocate or pass device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same product and bytes, with the split-K int32 partials in
+ * a library-owned device array of PF_NOALLOC_SCRATCH_BYTES (64 MiB) per device,
+ * held until the process ends, instead of a caller's workspace.  The array's
+ * device address is looked up once per device (pf_init, or the first call on
+ * that device); the call allocates nothing.  Every call on a device shares that
+ * device's array, so calls that overlap in time on one device (different
+ * streams, or host threads) race; the array keeps the last call's partials,
+ * which every call overwrites before reading (nothing needs clearing).  Returns
+ * PF_EWORKSPACE, before any device work, when the product's split plan needs
+ * more than the array holds (pf_gemm_i8_chunk_workspace reports the need);
+ * otherwise as pf_gemm_i8_chunk. */
+#define PF_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+PF_API pf_status pf_gemm_i8_chunk_noalloc(const int8_t* W, const float* w_scale, int64_t N,
+                                          int64_t K, const int8_t* xq, const float* a_scale,
+                                          int64_t M, float* y, void* stream);
 
 /* The per-token baseline ("Batched Prefill", §The Problem: one GEMV per token,
  * every weight re-read per token): y [N] = product of W with one token xq [K]. */

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(HERE, "libprefill.so")
 
 PF_OK, PF_EINVAL, PF_ENODEV, PF_ELAUNCH, PF_EWORKSPACE, PF_EINTERNAL = 0, -1, -2, -3, -4, -5
 NPROJ = 7
+NOALLOC_SCRATCH_BYTES = 64 << 20     # PF_NOALLOC_SCRATCH_BYTES
 PROJ_NAMES = ("q", "k", "v", "o", "gate", "up", "down")
 
 
@@ -73,6 +74,7 @@ _SIGS = {
     "pf_quantize_act": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "pf_gemm_i8_chunk_workspace": ([_I64, _I64, _I64], _SZ),
     "pf_gemm_i8_chunk": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _SZ, _P], ctypes.c_int),
+    "pf_gemm_i8_chunk_noalloc": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _P], ctypes.c_int),
     "pf_gemv_i8": ([_P, _P, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "pf_prefill_stack_workspace": ([ctypes.POINTER(_Stack), _I64], _SZ),
     "pf_prefill_stack": ([ctypes.POINTER(_Stack), _P, _I64, _I64, _P, _P, _P, _SZ,
@@ -164,6 +166,19 @@ def gemm_i8_chunk(W, w_scale, xq, a_scale, ws: torch.Tensor | None = None,
     _check("pf_gemm_i8_chunk", lib().pf_gemm_i8_chunk(
         _ptr(W), _ptr(w_scale), N, K, _ptr(xq), _ptr(a_scale), M, _ptr(y),
         _ptr(ws), ws.numel() if ws is not None else 0, _stream()))
+    return y
+
+
+def gemm_i8_chunk_noalloc(W, w_scale, xq, a_scale, out: torch.Tensor | None = None) -> torch.Tensor:
+    """gemm_i8_chunk with the split partials in the library's own device array
+    (no workspace; out must be given to avoid any allocation here)."""
+    _dev(W, torch.int8, "W"); _dev(w_scale, torch.float32, "w_scale")
+    _dev(xq, torch.int8, "xq"); _dev(a_scale, torch.float32, "a_scale")
+    N, K = W.shape
+    M = xq.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=W.device)
+    _check("pf_gemm_i8_chunk_noalloc", lib().pf_gemm_i8_chunk_noalloc(
+        _ptr(W), _ptr(w_scale), N, K, _ptr(xq), _ptr(a_scale), M, _ptr(y), _stream()))
     return y
 
 

@@ -915,6 +915,96 @@ SkinnyPlan plan_xres128(int64_t N, int64_t K)
     return p;
 }
 
+
+// Argument checks of a chunk product (M = 0 passes: a no-op).
+pf_status check_chunk_args(const int8_t* W, const float* w_scale, int64_t N, int64_t K,
+                           const int8_t* xq, const float* a_scale, int64_t M, const float* y)
+{
+    if (N <= 0 || N > INT32_MAX || !valid_k(K) || M < 0 || M > INT32_MAX) return PF_EINVAL;
+    if (M == 0) return PF_OK;
+    if (!W || !w_scale || !xq || !a_scale || !y) return PF_EINVAL;
+    if (!aligned16(W) || !aligned4(w_scale) || !aligned16(xq) || !aligned4(a_scale) || !aligned4(y))
+        return PF_EINVAL;
+    const size_t yb = (size_t)M * N * 4;
+    if (overlap(y, yb, W, (size_t)N * K) || overlap(y, yb, w_scale, (size_t)N * 4) ||
+        overlap(y, yb, xq, (size_t)M * K) || overlap(y, yb, a_scale, (size_t)M * 4))
+        return PF_EINVAL;
+    return PF_OK;
+}
+
+// Scratch bytes a chunk product's plan uses when room to split is given (0:
+// it runs unsplit).
+size_t chunk_scratch_bytes(int64_t N, int64_t K, int64_t M, const float* y)
+{
+    if (M <= 64) return split_bytes(N, M, plan_chunk_small(N, K, xres_fits_shape(N, y)));
+    if (xres128(N, K, M) && xres_fits_shape(N, y)) return split_bytes(N, M, plan_xres128(N, K));
+    return split_bytes(N, M, plan_tiled(N, K, M));
+}
+
+// A validated chunk product (M > 0) on a gfx950 device: the plan by M, split
+// across workgroups when the workspace has room for the split's partials.
+pf_status run_chunk(const int8_t* W, const float* w_scale, int64_t N, int64_t K, const int8_t* xq,
+                    const float* a_scale, int64_t M, float* y, void* workspace, size_t ws_bytes,
+                    hipStream_t stream)
+{
+    GemmSet set;
+    std::memset(&set, 0, sizeof(set));
+    set.nprob = 1;
+    int tile_tokens = 0;
+    char* scratch = static_cast<char*>(workspace);
+    if (M <= 64) {
+        SkinnyPlan p = plan_chunk_small(N, K, xres_fits_shape(N, y));
+        if (!workspace || ws_bytes < split_bytes(N, M, p)) p = unsplit(N, K);
+        make_skinny(set.p[0], W, w_scale, N, K, xq, K, a_scale, M, y, N, p, scratch, M);
+    } else if (xres128(N, K, M) && xres_fits_shape(N, y) &&
+               (plan_xres128(N, K).splits == 1 ||
+                (workspace && ws_bytes >= split_bytes(N, M, plan_xres128(N, K))))) {
+        const SkinnyPlan p = plan_xres128(N, K);
+        make_skinny(set.p[0], W, w_scale, N, K, xq, K, a_scale, M, y, N, p, scratch, M);
+        return run_skinny_xres(set, M, stream);
+    } else {
+        SkinnyPlan p = plan_tiled(N, K, M);
+        if (!workspace || ws_bytes < split_bytes(N, M, p)) p = plan_tiled(N, K, M, 1);
+        make_tiled(set.p[0], W, w_scale, N, K, xq, K, a_scale, M, y, N, p, scratch);
+        tile_tokens = p.tokens;
+    }
+    return run_products(set, M, tile_tokens, stream);
+}
+
+
+// ---------------------------------------------------------------------------
+// Scratch of pf_gemm_i8_chunk_noalloc: the split partials live in this
+// file-scope device array instead of a caller's workspace.  Each device holds
+// its own copy at its own address, looked up once per device at set-up (the
+// array's name in host code is not a device address).
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+__device__ __attribute__((aligned(256))) char scratch[kNoallocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[64];
+
+// The device address of this device's scratch array (null if the lookup fails).
+void* scratch_ptr()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -936,7 +1026,8 @@ const char* pf_status_string(pf_status s)
 pf_status pf_init(void)
 {
     try {
-        return check_device();
+        if (pf_status st = check_device()) return st;
+        return scratch_ptr() ? PF_OK : PF_ELAUNCH;
     } catch (...) {
         return PF_EINTERNAL;
     }
@@ -991,45 +1082,31 @@ pf_status pf_gemm_i8_chunk(const int8_t* W, const float* w_scale, int64_t N, int
                            void* workspace, size_t ws_bytes, void* stream)
 {
     try {
-        if (N <= 0 || N > INT32_MAX || !valid_k(K) || M < 0 || M > INT32_MAX) return PF_EINVAL;
+        if (pf_status st = check_chunk_args(W, w_scale, N, K, xq, a_scale, M, y)) return st;
         if (M == 0) return PF_OK;
-        if (!W || !w_scale || !xq || !a_scale || !y) return PF_EINVAL;
-        if (!aligned16(W) || !aligned4(w_scale) || !aligned16(xq) || !aligned4(a_scale) ||
-            !aligned4(y))
-            return PF_EINVAL;
-        const size_t yb = (size_t)M * N * 4;
-        if (overlap(y, yb, W, (size_t)N * K) || overlap(y, yb, w_scale, (size_t)N * 4) ||
-            overlap(y, yb, xq, (size_t)M * K) || overlap(y, yb, a_scale, (size_t)M * 4))
-            return PF_EINVAL;
         if (workspace && !aligned16(workspace)) return PF_EINVAL;
+        if (workspace && overlap(workspace, ws_bytes, y, (size_t)M * N * 4)) return PF_EINVAL;
         if (pf_status st = check_device()) return st;
-        GemmSet set;
-        std::memset(&set, 0, sizeof(set));
-        set.nprob = 1;
-        int tile_tokens = 0;
-        if (M <= 64) {
-            SkinnyPlan p = plan_chunk_small(N, K, xres_fits_shape(N, y));
-            if (!workspace || ws_bytes < split_bytes(N, M, p)) p = unsplit(N, K);
-            if (workspace && overlap(workspace, ws_bytes, y, yb)) return PF_EINVAL;
-            char* scratch = static_cast<char*>(workspace);
-            make_skinny(set.p[0], W, w_scale, N, K, xq, K, a_scale, M, y, N, p, scratch, M);
-        } else if (xres128(N, K, M) && xres_fits_shape(N, y) &&
-                   (plan_xres128(N, K).splits == 1 ||
-                    (workspace && ws_bytes >= split_bytes(N, M, plan_xres128(N, K))))) {
-            const SkinnyPlan p = plan_xres128(N, K);
-            if (workspace && overlap(workspace, ws_bytes, y, yb)) return PF_EINVAL;
-            char* scratch = static_cast<char*>(workspace);
-            make_skinny(set.p[0], W, w_scale, N, K, xq, K, a_scale, M, y, N, p, scratch, M);
-            return run_skinny_xres(set, M, (hipStream_t)stream);
-        } else {
-            SkinnyPlan p = plan_tiled(N, K, M);
-            if (!workspace || ws_bytes < split_bytes(N, M, p)) p = plan_tiled(N, K, M, 1);
-            if (workspace && overlap(workspace, ws_bytes, y, yb)) return PF_EINVAL;
-            char* scratch = static_cast<char*>(workspace);
-            make_tiled(set.p[0], W, w_scale, N, K, xq, K, a_scale, M, y, N, p, scratch);
-            tile_tokens = p.tokens;
-        }
-        return run_products(set, M, tile_tokens, (hipStream_t)stream);
+        return run_chunk(W, w_scale, N, K, xq, a_scale, M, y, workspace, ws_bytes,
+                         (hipStream_t)stream);
+    } catch (...) {
+        return PF_EINTERNAL;
+    }
+}
+
+pf_status pf_gemm_i8_chunk_noalloc(const int8_t* W, const float* w_scale, int64_t N, int64_t K,
+                                   const int8_t* xq, const float* a_scale, int64_t M, float* y,
+                                   void* stream)
+{
+    try {
+        if (pf_status st = check_chunk_args(W, w_scale, N, K, xq, a_scale, M, y)) return st;
+        if (M == 0) return PF_OK;
+        if (chunk_scratch_bytes(N, K, M, y) > kNoallocScratchBytes) return PF_EWORKSPACE;
+        if (pf_status st = check_device()) return st;
+        void* ws = scratch_ptr();
+        if (!ws) return PF_ELAUNCH;
+        return run_chunk(W, w_scale, N, K, xq, a_scale, M, y, ws, kNoallocScratchBytes,
+                         (hipStream_t)stream);
     } catch (...) {
         return PF_EINTERNAL;
     }

@@ -157,3 +157,20 @@ def test_stack_workspace_query_covers_short_prompts(L, H, F, chunk, P):
 
 
 P_ = ctypes.c_void_p
+
+
+def test_noalloc_product_refuses_plans_beyond_its_array():
+    """pf_gemm_i8_chunk_noalloc refuses, before touching a device, a product
+    whose split plan needs more partials than its 64 MiB array holds (260 tiles
+    of 256 x 256 over K = 131072: a two-way split of 520 MiB), and accepts
+    the arguments of one that fits (then stops at the device check here)."""
+    if os.environ.get("PF_EXPECT_GPU"):
+        pytest.skip("running on a GPU host")
+    lib = pf.lib()
+    N, K, M = 3328, 131072, 5120
+    assert lib.pf_gemm_i8_chunk_workspace(N, K, M) > pf.NOALLOC_SCRATCH_BYTES
+    W, ws, q, s, y = (P_(a) for a in (0x1000000000, 0x2000000000, 0x3000000000, 0x4000000000,
+                                      0x5000000000))
+    assert lib.pf_gemm_i8_chunk_noalloc(W, ws, N, K, q, s, M, y, None) == pf.PF_EWORKSPACE
+    assert lib.pf_gemm_i8_chunk_noalloc(W, ws, 4096, 4096, q, s, 512, y, None) == pf.PF_ENODEV
+    assert lib.pf_gemm_i8_chunk_noalloc(W, ws, 4096, 100, q, s, 512, y, None) == pf.PF_EINVAL
