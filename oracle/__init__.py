@@ -54,12 +54,12 @@ def _load():
             "or_quantize": [P, I64, I64, P, P],
             "or_gemv": [P, P, I64, I64, P, F, P],
             "or_linear_per_token": [P, P, I64, I64, P, P, I64, P, INT],
-            "or_stack": [I64, I64, I64, P, P, P, I64, P, P, INT],
+            "or_stack": [I64, I64, I64, P, P, P, I64, P, P, INT, INT],
             "or_router": [P, I64, I64, P, P],
             "or_expf_cr_array": [P, I64, P, INT],
-            "or_softmax_topk": [P, I64, I64, P, P],
-            "or_expert": [I64, I64, P, P, P, P, P, P, I64, P, F, P],
-            "or_moe": [I64, I64, I64, I64, P, P, P, P, P, P, P, P, I64, P, P, P, INT],
+            "or_softmax_topk": [P, I64, I64, P, P, INT],
+            "or_expert": [I64, I64, P, P, P, P, P, P, I64, P, F, P, INT],
+            "or_moe": [I64, I64, I64, I64, P, P, P, P, P, P, P, P, I64, P, P, P, INT, INT, INT],
         }
         for name, args in sigs.items():
             fn = getattr(lib, name)
@@ -67,6 +67,8 @@ def _load():
             fn.restype = ctypes.c_int
         lib.or_expf_cr.argtypes = [F]
         lib.or_expf_cr.restype = F
+        lib.or_silu.argtypes = [F]
+        lib.or_silu.restype = F
         _lib = lib
     return _lib
 
@@ -125,12 +127,17 @@ def linear(W, w_scale, q, a_scale, threads: int | None = None) -> np.ndarray:
     return y
 
 
-def stack(weights, scales, x, return_proj: bool = False, threads: int | None = None):
+ACT_NONE, ACT_SWIGLU = 0, 1
+
+
+def stack(weights, scales, x, return_proj: bool = False, threads: int | None = None,
+          act: int = ACT_NONE):
     """The projection stack token by token.
 
     weights[l] is the list (q, k, v, o, gate, up, down) of int8 arrays of layer l,
     scales[l] the matching f32 per-row scales.  x [P, H] -> y [P, H]; with
-    ``return_proj`` also every projection output [L, P, 5H + 2F].
+    ``return_proj`` also every projection output [L, P, 5H + 2F].  act selects
+    the down projection's input: quantise(up), or quantise(silu(gate) * up).
     """
     L = len(weights)
     x = _c(np.atleast_2d(x), np.float32)
@@ -150,7 +157,7 @@ def stack(weights, scales, x, return_proj: bool = False, threads: int | None = N
     proj = np.empty((L, P, 5 * H + 2 * F), np.float32) if return_proj else None
     rc = _load().or_stack(L, H, F, ctypes.cast(wp, ctypes.c_void_p), ctypes.cast(sp, ctypes.c_void_p),
                           _ptr(x), P, _ptr(y), _ptr(proj) if proj is not None else None,
-                          threads or default_threads())
+                          threads or default_threads(), int(act))
     _check(rc, "or_stack")
     return (y, proj) if return_proj else y
 
@@ -177,27 +184,36 @@ def router(Wr, x) -> np.ndarray:
     return out
 
 
-def softmax_topk(logits, top_k: int):
-    """Per row of logits [T, E]: (ids int32 [T, k], weights f32 [T, k])."""
+def silu(g):
+    """silu(g) = g / (1 + expf_cr(-g)), each step rounded to binary32, elementwise."""
+    g = np.asarray(g, np.float32)
+    lib = _load()
+    return np.array([lib.or_silu(float(v)) for v in g.reshape(-1)], np.float32).reshape(g.shape)
+
+
+def softmax_topk(logits, top_k: int, renorm: bool = False):
+    """Per row of logits [T, E]: (ids int32 [T, k], weights f32 [T, k]); renorm:
+    weights renormalised over the chosen experts."""
     logits = _c(np.atleast_2d(logits), np.float32)
     T, E = logits.shape
     ids = np.empty((T, top_k), np.int32)
     w = np.empty((T, top_k), np.float32)
     lib = _load()
     for t in range(T):
-        _check(lib.or_softmax_topk(_ptr(logits[t]), E, top_k, _ptr(ids[t]), _ptr(w[t])),
-               "or_softmax_topk")
+        _check(lib.or_softmax_topk(_ptr(logits[t]), E, top_k, _ptr(ids[t]), _ptr(w[t]),
+                                   int(renorm)), "or_softmax_topk")
     return ids, w
 
 
 def expert(moe: dict, e: int, xq, xs) -> np.ndarray:
-    """Expert e applied to one quantised token (xq int8 [H], xs f32)."""
+    """Expert e applied to one quantised token (xq int8 [H], xs f32); the
+    activation is moe.get("activation", ACT_NONE)."""
     H, I = moe["hidden"], moe["inter"]
     y = np.empty(H, np.float32)
     xq = _c(xq, np.int8).reshape(H)
     rc = _load().or_expert(H, I, _ptr(moe["W_gate"]), _ptr(moe["W_up"]), _ptr(moe["W_down"]),
                            _ptr(moe["s_gate"]), _ptr(moe["s_up"]), _ptr(moe["s_down"]), e,
-                           _ptr(xq), float(np.float32(xs)), _ptr(y))
+                           _ptr(xq), float(np.float32(xs)), _ptr(y), int(moe.get("activation", 0)))
     _check(rc, "or_expert")
     return y
 
@@ -207,7 +223,8 @@ def moe(moe: dict, x, threads: int | None = None):
 
     ``moe`` holds n_experts, top_k, hidden, inter, W_router [E, H] f32,
     W_gate / W_up [E, I, H] int8, W_down [E, H, I] int8, s_gate / s_up [E, I] and
-    s_down [E, H] f32 (C-contiguous numpy arrays).
+    s_down [E, H] f32 (C-contiguous numpy arrays); optional "activation"
+    (ACT_NONE or ACT_SWIGLU) and "renormalize" (0 or 1) select the variants.
     """
     E, k, H, I = moe["n_experts"], moe["top_k"], moe["hidden"], moe["inter"]
     x = _c(np.atleast_2d(x), np.float32)
@@ -220,6 +237,7 @@ def moe(moe: dict, x, threads: int | None = None):
                                           ("s_gate", np.float32), ("s_up", np.float32),
                                           ("s_down", np.float32))]
     rc = _load().or_moe(E, k, H, I, *[_ptr(a) for a in arrs], _ptr(x), T, _ptr(ids), _ptr(w),
-                        _ptr(out), threads or default_threads())
+                        _ptr(out), threads or default_threads(), int(moe.get("activation", 0)),
+                        int(moe.get("renormalize", 0)))
     _check(rc, "or_moe")
     return ids, w, out

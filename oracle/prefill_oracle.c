@@ -100,8 +100,9 @@ int or_linear_per_token(const int8_t* W, const float* w_scale, int64_t N, int64_
  * reads quantise(up); the next layer's input is down, unchanged. */
 int or_stack(int64_t L, int64_t H, int64_t F, const int8_t* const* W,
              const float* const* w_scale, const float* x, int64_t P, float* y,
-             float* proj, int threads)
+             float* proj, int threads, int act)
 {
+    if (act != OR_ACT_NONE && act != OR_ACT_SWIGLU) return -1;
     if (!W || !w_scale || !x || !y || L <= 0 || H <= 0 || F <= 0 || P < 0) return -1;
     if (H > 131072 || F > 131072) return -1;
     for (int64_t i = 0; i < 7 * L; ++i)
@@ -118,8 +119,9 @@ int or_stack(int64_t L, int64_t H, int64_t F, const int8_t* const* W,
     {
         float* h = (float*)malloc(sizeof(float) * (size_t)H);
         float* outs = (float*)malloc(sizeof(float) * (size_t)total);
+        float* r = (float*)malloc(sizeof(float) * (size_t)F);
         int8_t* a = (int8_t*)malloc((size_t)(F > H ? F : H));
-        int failed = (!h || !outs || !a);
+        int failed = (!h || !outs || !r || !a);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t t = 0; t < P; ++t) {
             if (failed) continue;
@@ -130,8 +132,14 @@ int or_stack(int64_t L, int64_t H, int64_t F, const int8_t* const* W,
                 for (int j = 0; j < 6; ++j)
                     gemv_row_block(W[l * 7 + j], w_scale[l * 7 + j], nrow[j], H, a, sa,
                                    outs + off[j]);
+                /* the down projection's input: up, or silu(gate) * up */
+                const float* din = outs + off[5];
+                if (act == OR_ACT_SWIGLU) {
+                    for (int64_t i = 0; i < F; ++i) r[i] = or_silu(outs[off[4] + i]) * outs[off[5] + i];
+                    din = r;
+                }
                 float sb;
-                if (quantize_row(outs + off[5], F, a, &sb)) { failed = 1; break; }
+                if (quantize_row(din, F, a, &sb)) { failed = 1; break; }
                 gemv_row_block(W[l * 7 + 6], w_scale[l * 7 + 6], H, F, a, sb, outs + off[6]);
                 if (proj)
                     memcpy(proj + (l * P + t) * total, outs, sizeof(float) * (size_t)total);
@@ -145,6 +153,7 @@ int or_stack(int64_t L, int64_t H, int64_t F, const int8_t* const* W,
         }
         free(h);
         free(outs);
+        free(r);
         free(a);
     }
     return status;
@@ -183,6 +192,16 @@ int or_expf_cr_array(const float* x, int64_t n, float* y, int threads)
     return 0;
 }
 
+/* SiLU through the correctly rounded exp, each step rounded on its own:
+ * silu(g) = fl(g / fl(1 + expf_cr(-g))).  For g below about -88.7, exp(-g)
+ * overflows to +inf and the quotient is -0. */
+float or_silu(float g)
+{
+    float e = or_expf_cr(-g);
+    float d = 1.0f + e;
+    return g / d;
+}
+
 /* Router product for one token ("Red Lite dev24", What changed, item 1: the
  * router is one extra f32 GEMM).  The summation order the page leaves open is
  * fixed here: ascending k, each product and each sum rounded on its own. */
@@ -207,9 +226,10 @@ int or_router(const float* Wr, int64_t E, int64_t H, const float* x, float* logi
  * normaliser sums in ascending expert id, ties in p go to the lower id, and the
  * weights are the softmax probabilities of the chosen experts. */
 int or_softmax_topk(const float* logits, int64_t E, int64_t top_k,
-                    int32_t* ids, float* weights)
+                    int32_t* ids, float* weights, int renorm)
 {
     if (!logits || !ids || !weights || E <= 0 || top_k <= 0 || top_k > E) return -1;
+    if (renorm != 0 && renorm != 1) return -1;
     float* p = (float*)malloc(sizeof(float) * (size_t)E);
     unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
     if (!p || !taken) { free(p); free(taken); return -1; }
@@ -234,6 +254,13 @@ int or_softmax_topk(const float* logits, int64_t E, int64_t top_k,
         ids[j] = (int32_t)best;
         weights[j] = p[best];
     }
+    if (renorm) {
+        /* weights over the chosen experts only: T = the chosen p summed in
+         * rank order (descending p, ties to the lower id), w_j = p_j / T */
+        float T = 0.0f;
+        for (int64_t j = 0; j < top_k; ++j) T = T + weights[j];
+        for (int64_t j = 0; j < top_k; ++j) weights[j] = weights[j] / T;
+    }
     free(p);
     free(taken);
     return 0;
@@ -245,11 +272,14 @@ int or_softmax_topk(const float* logits, int64_t E, int64_t top_k,
 static int expert_apply(int64_t H, int64_t I, const int8_t* Wg, const int8_t* Wu,
                         const int8_t* Wd, const float* sg, const float* su, const float* sd,
                         int64_t e, const int8_t* xq, float xs, float* y,
-                        float* g, float* u, int8_t* hq)
+                        float* g, float* u, int8_t* hq, int act)
 {
     gemv_row_block(Wg + e * I * H, sg + e * I, I, H, xq, xs, g);
     gemv_row_block(Wu + e * I * H, su + e * I, I, H, xq, xs, u);
-    for (int64_t i = 0; i < I; ++i) g[i] = g[i] * u[i];
+    if (act == OR_ACT_SWIGLU)
+        for (int64_t i = 0; i < I; ++i) g[i] = or_silu(g[i]) * u[i];
+    else
+        for (int64_t i = 0; i < I; ++i) g[i] = g[i] * u[i];
     float hs;
     int rc = quantize_row(g, I, hq, &hs);
     if (rc) return rc;
@@ -259,15 +289,16 @@ static int expert_apply(int64_t H, int64_t I, const int8_t* Wg, const int8_t* Wu
 
 int or_expert(int64_t H, int64_t I, const int8_t* Wg, const int8_t* Wu,
               const int8_t* Wd, const float* sg, const float* su, const float* sd,
-              int64_t e, const int8_t* xq, float xs, float* y)
+              int64_t e, const int8_t* xq, float xs, float* y, int act)
 {
     if (!Wg || !Wu || !Wd || !sg || !su || !sd || !xq || !y || H <= 0 || I <= 0 || e < 0)
         return -1;
+    if (act != OR_ACT_NONE && act != OR_ACT_SWIGLU) return -1;
     float* g = (float*)malloc(sizeof(float) * (size_t)I);
     float* u = (float*)malloc(sizeof(float) * (size_t)I);
     int8_t* hq = (int8_t*)malloc((size_t)I);
     int rc = (!g || !u || !hq) ? -1
-                               : expert_apply(H, I, Wg, Wu, Wd, sg, su, sd, e, xq, xs, y, g, u, hq);
+                               : expert_apply(H, I, Wg, Wu, Wd, sg, su, sd, e, xq, xs, y, g, u, hq, act);
     free(g);
     free(u);
     free(hq);
@@ -278,10 +309,11 @@ int or_moe(int64_t E, int64_t top_k, int64_t H, int64_t I, const float* Wr,
            const int8_t* Wg, const int8_t* Wu, const int8_t* Wd,
            const float* sg, const float* su, const float* sd,
            const float* x, int64_t T, int32_t* ids, float* weights, float* out,
-           int threads)
+           int threads, int act, int renorm)
 {
     if (!Wr || !Wg || !Wu || !Wd || !sg || !su || !sd || !x || !ids || !weights || !out)
         return -1;
+    if ((act != OR_ACT_NONE && act != OR_ACT_SWIGLU) || (renorm != 0 && renorm != 1)) return -1;
     if (E <= 0 || top_k <= 0 || top_k > E || H <= 0 || I <= 0 || T < 0) return -1;
     if (H > 131072 || I > 131072) return -1;
     if (threads < 1) threads = 1;
@@ -303,7 +335,7 @@ int or_moe(int64_t E, int64_t top_k, int64_t H, int64_t I, const float* Wr,
             float xs;
             int rc = quantize_row(xt, H, xq, &xs);
             if (!rc) rc = or_router(Wr, E, H, xt, logits);
-            if (!rc) rc = or_softmax_topk(logits, E, top_k, ids + t * top_k, weights + t * top_k);
+            if (!rc) rc = or_softmax_topk(logits, E, top_k, ids + t * top_k, weights + t * top_k, renorm);
             if (rc) { failed = rc; continue; }
             /* combine in ascending expert id */
             memset(chosen, 0, (size_t)E);
@@ -315,7 +347,7 @@ int or_moe(int64_t E, int64_t top_k, int64_t H, int64_t I, const float* Wr,
                 float w = 0.0f;
                 for (int64_t j = 0; j < top_k; ++j)
                     if (ids[t * top_k + j] == e) w = weights[t * top_k + j];
-                rc = expert_apply(H, I, Wg, Wu, Wd, sg, su, sd, e, xq, xs, y, g, u, hq);
+                rc = expert_apply(H, I, Wg, Wu, Wd, sg, su, sd, e, xq, xs, y, g, u, hq, act);
                 if (rc) { failed = rc; break; }
                 for (int64_t n = 0; n < H; ++n) {
                     float c = w * y[n];

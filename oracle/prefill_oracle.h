@@ -31,6 +31,17 @@ extern "C" {
 
 /* Return codes: 0 ok, -1 bad argument, -2 non-finite input value. */
 
+/* The nonlinearity between the gate/up products and the down product.
+ * OR_ACT_NONE: the reading used when the pages name no activation (the stack's
+ * down reads quantise(up); an expert's down reads quantise(g * u)).
+ * OR_ACT_SWIGLU: the gated SiLU of the feed-forward blocks of the model
+ * families the pages run (the pages name gate, up and down projections but no
+ * formula): r_i = fl(silu(g_i) * u_i) with silu(g) = fl(g / fl(1 + expf_cr(-g))),
+ * the stack's down reading quantise(r) (gate then feeds it) and an expert's
+ * down reading quantise(r). */
+#define OR_ACT_NONE 0
+#define OR_ACT_SWIGLU 1
+
 /* Per-token symmetric quantisation, once per token row [cellm §The Solution:
  * activations quantised once per batch]: amax = max|x_k| (exact),
  * s = fl(amax / 127), q_k = clamp(roundf(fl(x_k / s)), -127, 127) with roundf
@@ -55,13 +66,14 @@ int or_linear_per_token(const int8_t* W, const float* w_scale, int64_t N, int64_
  * Per layer l, with h the layer input (h = x for l = 0):
  *   (a, sa) = quantise(h);  p_j = gemv(W[l][j], a, sa) for j = q,k,v,o,gate,up;
  *   (b, sb) = quantise(up); down = gemv(W[l][6], b, sb);  next h = down.
+ * With act = OR_ACT_SWIGLU, (b, sb) = quantise(silu(gate) * up) instead.
  * Weights: W[l*7 + j], w_scale[l*7 + j]; shapes q,k,v,o [H][H], gate,up [F][H],
  * down [H][F].  x [P][H] -> y [P][H].  proj, when not NULL, receives every
  * projection output: proj[((l*P + t) * (5H + 2F)) + off_j + n] with the seven
  * outputs concatenated in the order q,k,v,o,gate,up,down. */
 int or_stack(int64_t L, int64_t H, int64_t F, const int8_t* const* W,
              const float* const* w_scale, const float* x, int64_t P, float* y,
-             float* proj, int threads);
+             float* proj, int threads, int act);
 
 /* Correctly rounded binary32 exp (the exact exponential rounded to nearest,
  * ties to even).  Aborts if the long-double evaluation cannot decide the
@@ -70,6 +82,9 @@ int or_stack(int64_t L, int64_t H, int64_t F, const int8_t* const* W,
 float or_expf_cr(float x);
 int or_expf_cr_array(const float* x, int64_t n, float* y, int threads);
 
+/* silu(g) = fl(g / fl(1 + or_expf_cr(-g))), each operation rounded on its own. */
+float or_silu(float g);
+
 /* Router logits of one token, the f32 product of [red "What changed", item 1]:
  * l[e] = 0, then for k ascending l[e] = fl(l[e] + fl(Wr[e][k] * x[k])). */
 int or_router(const float* Wr, int64_t E, int64_t H, const float* x, float* logits);
@@ -77,26 +92,30 @@ int or_router(const float* Wr, int64_t E, int64_t H, const float* x, float* logi
 /* Softmax over E logits, then the top_k largest probabilities [red "What
  * changed", item 2]: m = max l; z_e = expf_cr(fl(l_e - m)); S = sum of z in
  * ascending e; p_e = fl(z_e / S).  ids ordered by descending p, ties to the
- * lower id; weights[j] = p[ids[j]] (not renormalised). */
+ * lower id; weights[j] = p[ids[j]] (not renormalised).  With renorm = 1 the
+ * weights are renormalised over the chosen experts: T = sum of weights[j] in
+ * rank order j = 0 .. top_k-1, then weights[j] = fl(weights[j] / T). */
 int or_softmax_topk(const float* logits, int64_t E, int64_t top_k,
-                    int32_t* ids, float* weights);
+                    int32_t* ids, float* weights, int renorm);
 
 /* One expert applied to one token: g = gemv(Wg_e, xq), u = gemv(Wu_e, xq),
- * r_i = fl(g_i * u_i), (hq, hs) = quantise(r), y = gemv(Wd_e, hq, hs).
+ * r_i = fl(g_i * u_i) (act OR_ACT_NONE) or fl(silu(g_i) * u_i) (OR_ACT_SWIGLU),
+ * (hq, hs) = quantise(r), y = gemv(Wd_e, hq, hs).
  * Wg, Wu [E][I][H]; Wd [E][H][I]; sg, su [E][I]; sd [E][H]. */
 int or_expert(int64_t H, int64_t I, const int8_t* Wg, const int8_t* Wu,
               const int8_t* Wd, const float* sg, const float* su, const float* sd,
-              int64_t e, const int8_t* xq, float xs, float* y);
+              int64_t e, const int8_t* xq, float xs, float* y, int act);
 
 /* Mixture-of-experts prefill of T tokens, token by token:
  * xq = quantise(x_t); logits = router(x_t); (ids, w) = softmax_topk(logits);
  * out_t = +0, then for each selected expert in ascending id
- * out_t[j] = fl(out_t[j] + fl(w_e * y_e[j])).  ids, weights [T][top_k]. */
+ * out_t[j] = fl(out_t[j] + fl(w_e * y_e[j])).  ids, weights [T][top_k].
+ * act and renorm select the variants of or_expert and or_softmax_topk. */
 int or_moe(int64_t E, int64_t top_k, int64_t H, int64_t I, const float* Wr,
            const int8_t* Wg, const int8_t* Wu, const int8_t* Wd,
            const float* sg, const float* su, const float* sd,
            const float* x, int64_t T, int32_t* ids, float* weights, float* out,
-           int threads);
+           int threads, int act, int renorm);
 
 #ifdef __cplusplus
 }

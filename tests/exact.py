@@ -90,17 +90,21 @@ def gemv(W, ws, q, a_scale) -> list[float]:
     return [epilogue(int(acc[n]), ws[n], a_scale) for n in range(W.shape[0])]
 
 
-def stack_token(weights, scales, x) -> tuple[list[float], list[list[float]]]:
+def stack_token(weights, scales, x, act: int = 0) -> tuple[list[float], list[list[float]]]:
     """One token through the stack, composed from the brute-force pieces.
 
     Returns the final activation and, per layer, the seven projection outputs
-    concatenated (q, k, v, o, gate, up, down)."""
+    concatenated (q, k, v, o, gate, up, down).  act 1: the down projection reads
+    quantise(silu(gate) * up)."""
     h = [float(v) for v in np.asarray(x, np.float32)]
     per_layer = []
     for wl, sl in zip(weights, scales):
         a, sa = quantize_row(np.array(h, np.float32))
         outs = [gemv(wl[j], sl[j], a, sa) for j in range(6)]
-        b, sb = quantize_row(np.array(outs[5], np.float32))
+        din = outs[5]
+        if act:
+            din = [f32_round(fr(silu(g)) * fr(u)) for g, u in zip(outs[4], outs[5])]
+        b, sb = quantize_row(np.array(din, np.float32))
         down = gemv(wl[6], sl[6], b, sb)
         per_layer.append(sum(outs, []) + down)
         h = down
@@ -129,8 +133,20 @@ def exp_cr(x: float) -> float:
     return f32_round(v)
 
 
-def softmax_topk(logits, k) -> tuple[list[int], list[float], list[float]]:
-    """Brute-force softmax + top-k: returns (ids, weights, all p)."""
+def silu(g) -> float:
+    """silu(g) = RN(g / RN(1 + exp_cr(-g))), each step rounded exactly."""
+    g = f32(g)
+    e = exp_cr(-g)
+    if math.isinf(e):
+        return -0.0 if g < 0 else 0.0            # g / inf, with g's sign
+    d = f32_round(1 + fr(e))
+    q = f32_round(fr(g) / fr(d))
+    return -0.0 if (q == 0 and g < 0) else q
+
+
+def softmax_topk(logits, k, renorm: bool = False) -> tuple[list[int], list[float], list[float]]:
+    """Brute-force softmax + top-k: returns (ids, weights, all p); renorm:
+    weights divided by their sum taken in rank order."""
     ls = [float(v) for v in np.asarray(logits, np.float32)]
     m = max(ls)
     z = [exp_cr(f32_round(fr(v) - fr(m))) for v in ls]
@@ -139,4 +155,10 @@ def softmax_topk(logits, k) -> tuple[list[int], list[float], list[float]]:
         S = f32_round(fr(S) + fr(v))
     p = [f32_round(fr(v) / fr(S)) for v in z]
     order = sorted(range(len(p)), key=lambda e: (-p[e], e))[:k]
-    return order, [p[e] for e in order], p
+    w = [p[e] for e in order]
+    if renorm:
+        T = 0.0
+        for v in w:
+            T = f32_round(fr(T) + fr(v))
+        w = [f32_round(fr(v) / fr(T)) for v in w]
+    return order, w, p

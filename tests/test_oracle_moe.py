@@ -89,15 +89,18 @@ def test_expf_matches_mpmath_sample():
 
 
 @pytest.mark.slow
-def test_expf_exhaustive_nonpositive():
-    """Every binary32 x in [-104, 0]: the oracle's exp equals RN(exp(x)).
+@pytest.mark.parametrize("lo_x,hi_x", [(-0.0, -104.0), (0.0, 89.0)])
+def test_expf_exhaustive(lo_x, hi_x):
+    """Every binary32 x in [-104, 0] (the softmax's arguments) and in [0, 89]
+    (the gated SiLU's exp(-g) for g < 0; exp overflows past 88.72): the
+    oracle's exp equals RN(exp(x)).
 
     float64 exp has error below one double ulp, so its binary32 rounding is the
     correct rounding except when exp(x) lies within ~2^-52 (relative) of a
     binary32 midpoint; those few inputs are recomputed with mpmath at 80 digits.
     """
-    top = int(np.array(-104.0, np.float32).view(np.uint32))
-    start = int(np.array(-0.0, np.float32).view(np.uint32))  # 0x80000000
+    top = int(np.array(hi_x, np.float32).view(np.uint32))
+    start = int(np.array(lo_x, np.float32).view(np.uint32))  # +-0: bits 0 or 0x80000000
     step = 1 << 24
     flagged = 0
     for lo in range(start, top + 1, step):
