@@ -153,7 +153,19 @@ typedef struct {
      * one copy, so a caller can measure the rate of the weight stream from
      * DRAM alone. */
     const pf_layer* layers_alt;
+    /* PF_ACT_NONE: down reads quantise(up).  PF_ACT_SWIGLU: down reads
+     * quantise(r), r = fl(silu(gate) * up) elementwise with silu(g) =
+     * fl(g / fl(1 + expf_cr(-g))) (expf_cr as pf_expf_cr), so gate feeds down
+     * too.  The pages name gate, up and down projections but no activation;
+     * the gated SiLU is the feed-forward of the model families they run.  With
+     * no normalisation between layers the gated product is of degree two in
+     * the layer input, so long chains of it grow or shrink without bound: it
+     * suits stacks of a few layers (the expert layer is one). */
+    int64_t activation;
 } pf_stack;
+
+#define PF_ACT_NONE 0
+#define PF_ACT_SWIGLU 1
 
 /* Statistics of one pf_prefill_stack call.  time_kernels is the only input:
  * set it to 1 to give every launch a pair of HIP events stamped when the kernel
@@ -222,6 +234,9 @@ typedef struct {
     const float* s_gate;
     const float* s_up;
     const float* s_down;
+    int64_t activation;  /* PF_ACT_NONE: r = fl(g * u); PF_ACT_SWIGLU: r = fl(silu(g) * u) */
+    int64_t renormalize; /* 0: weights = softmax p of the chosen experts; 1: divided by
+                            their sum T (taken in rank order), w = fl(p / T)        */
 } pf_moe;
 
 /* Workspace bytes for pf_moe_chunk with T tokens. */
@@ -233,10 +248,13 @@ PF_API size_t pf_moe_chunk_workspace(const pf_moe* moe, int64_t T);
  *   p = softmax(logits[t]) with correctly rounded expf, normaliser summed in
  *     ascending e; ids[t] = the top_k experts by descending p, ties to the lower
  *     id; weights[t][j] = p[ids[t][j]] (not renormalised);
+ *     (with renormalize, weights[t][j] = fl(p / T), T the chosen p summed in
+ *     rank order);
  *   tokens are grouped by expert (the union of selected experts, tokens in
  *     ascending order within an expert) and each expert runs as int8 products
- *     over its group: g = gate(xq), u = up(xq), r = fl(g * u), (hq, hs) =
- *     quantise(r) per (token, expert) row, y_e = down(hq);
+ *     over its group: g = gate(xq), u = up(xq), r = fl(g * u) (or
+ *     fl(silu(g) * u) with PF_ACT_SWIGLU), (hq, hs) = quantise(r) per
+ *     (token, expert) row, y_e = down(hq);
  *   out[t] = +0 then, over the selected experts in ascending id,
  *     out[t][j] = fl(out[t][j] + fl(weights_e * y_e[j])).
  * ids [T][top_k] int32, weights [T][top_k] f32, out [T][H] f32.

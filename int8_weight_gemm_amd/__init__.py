@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(HERE, "libprefill.so")
 PF_OK, PF_EINVAL, PF_ENODEV, PF_ELAUNCH, PF_EWORKSPACE, PF_EINTERNAL = 0, -1, -2, -3, -4, -5
 NPROJ = 7
 NOALLOC_SCRATCH_BYTES = 64 << 20     # PF_NOALLOC_SCRATCH_BYTES
+ACT_NONE, ACT_SWIGLU = 0, 1          # PF_ACT_NONE, PF_ACT_SWIGLU
 PROJ_NAMES = ("q", "k", "v", "o", "gate", "up", "down")
 
 
@@ -41,7 +42,8 @@ class _Layer(ctypes.Structure):
 
 class _Stack(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int64), ("hidden", ctypes.c_int64), ("ffn", ctypes.c_int64),
-                ("layers", ctypes.POINTER(_Layer)), ("layers_alt", ctypes.POINTER(_Layer))]
+                ("layers", ctypes.POINTER(_Layer)), ("layers_alt", ctypes.POINTER(_Layer)),
+                ("activation", ctypes.c_int64)]
 
 
 class StackStats(ctypes.Structure):
@@ -62,7 +64,8 @@ class _Moe(ctypes.Structure):
     _fields_ = [("n_experts", ctypes.c_int64), ("top_k", ctypes.c_int64), ("hidden", ctypes.c_int64),
                 ("inter", ctypes.c_int64), ("W_router", ctypes.c_void_p), ("W_gate", ctypes.c_void_p),
                 ("W_up", ctypes.c_void_p), ("W_down", ctypes.c_void_p), ("s_gate", ctypes.c_void_p),
-                ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+                ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+                ("activation", ctypes.c_int64), ("renormalize", ctypes.c_int64)]
 
 
 _lib = None
@@ -204,9 +207,9 @@ class Stack:
     """A projection stack resident in HBM: weights[l] = 7 int8 tensors (q, k, v, o,
     gate, up, down), scales[l] = 7 f32 tensors.  ``alt``, optional, is a second
     (weights, scales) copy of the same values that odd chunks read (pf_stack's
-    layers_alt)."""
+    layers_alt); activation: ACT_NONE or ACT_SWIGLU (pf_stack's activation)."""
 
-    def __init__(self, weights, scales, alt=None):
+    def __init__(self, weights, scales, alt=None, activation: int = ACT_NONE):
         self.L = len(weights)
         self.H = weights[0][0].shape[1]
         self.F = weights[0][4].shape[0]
@@ -215,7 +218,7 @@ class Stack:
         self._alt = self._table(*alt) if alt is not None else None
         self._desc = _Stack(self.L, self.H, self.F, ctypes.cast(self._layers, ctypes.POINTER(_Layer)),
                             ctypes.cast(self._alt, ctypes.POINTER(_Layer)) if self._alt is not None
-                            else None)
+                            else None, int(activation))
 
     def _table(self, weights, scales):
         tab = (_Layer * self.L)()
@@ -255,7 +258,8 @@ class Stack:
 class Moe:
     """Mixture-of-experts layer resident in HBM (tensors as in pf_moe)."""
 
-    def __init__(self, n_experts, top_k, W_router, W_gate, W_up, W_down, s_gate, s_up, s_down):
+    def __init__(self, n_experts, top_k, W_router, W_gate, W_up, W_down, s_gate, s_up, s_down,
+                 activation: int = ACT_NONE, renormalize: int = 0):
         E, I, H = W_gate.shape
         for n, t, dt in (("W_router", W_router, torch.float32), ("W_gate", W_gate, torch.int8),
                          ("W_up", W_up, torch.int8), ("W_down", W_down, torch.int8),
@@ -264,7 +268,8 @@ class Moe:
             _dev(t, dt, n)
         self.E, self.k, self.H, self.I = n_experts, top_k, H, I
         self.tensors = (W_router, W_gate, W_up, W_down, s_gate, s_up, s_down)
-        self._desc = _Moe(n_experts, top_k, H, I, *[t.data_ptr() for t in self.tensors])
+        self._desc = _Moe(n_experts, top_k, H, I, *[t.data_ptr() for t in self.tensors],
+                          int(activation), int(renormalize))
 
     @property
     def expert_weight_bytes(self) -> int:

@@ -355,6 +355,7 @@ pf_status validate_stack(const pf_stack* st)
 {
     if (!st || !st->layers || st->n_layers <= 0 || st->hidden <= 0 || st->ffn <= 0)
         return PF_EINVAL;
+    if (st->activation != PF_ACT_NONE && st->activation != PF_ACT_SWIGLU) return PF_EINVAL;
     if (!valid_k(st->hidden) || !valid_k(st->ffn)) return PF_EINVAL;
     for (const pf_layer* tab : {st->layers, st->layers_alt}) {
         if (!tab) continue;
@@ -407,6 +408,9 @@ pf_status validate_moe(const pf_moe* m)
         m->top_k > m->n_experts)
         return PF_EINVAL;
     if (!valid_k(m->hidden) || !valid_k(m->inter)) return PF_EINVAL;
+    if ((m->activation != PF_ACT_NONE && m->activation != PF_ACT_SWIGLU) ||
+        (m->renormalize != 0 && m->renormalize != 1))
+        return PF_EINVAL;
     const void* mats[] = {m->W_router, m->W_gate, m->W_up, m->W_down};
     for (const void* p : mats)
         if (!p || !aligned16(p)) return PF_EINVAL;
@@ -770,6 +774,7 @@ struct StackRun {
             rows_a += (int)M;
             QuantPair& q1 = qd.pair[qd.npairs++];
             q1.src = out + offs(5);
+            q1.gate = st->activation == PF_ACT_SWIGLU ? out + offs(4) : nullptr;
             q1.ld = NT();
             q1.q = b;
             q1.s = sb;
@@ -799,7 +804,8 @@ struct StackRun {
             d_bytes += product_bytes(H(), F(), M);
             if (rebuild_d) part_bytes += (double)M * H() * 4 * sd;   // the partials' write
             qa_bytes += (double)M * H() * 5 + M * 4.0;
-            qd_bytes += (double)M * F() * 5 + M * 4.0;
+            // up read (and gate with the gated SiLU), codes and scales written
+            qd_bytes += (double)M * F() * (st->activation == PF_ACT_SWIGLU ? 9 : 5) + M * 4.0;
         }
         if (fin >= 0) {
             // the chunk that left the last layer: rebuild its output, no quantisation
@@ -873,7 +879,11 @@ struct StackRun {
                 finish_set(set, 0);
                 r = rec.run(Recorder::kProduct, bytes, [&] { return launched(launch_gemv(set, s)); });
                 if (r) return r;
-                r = rec.run(Recorder::kQuant, (double)F() * 5 + 4, [&] {
+                const bool gated = st->activation == PF_ACT_SWIGLU;
+                r = rec.run(Recorder::kQuant, (double)F() * (gated ? 9 : 5) + 4, [&] {
+                    if (gated)
+                        return launched(launch_quantize_gated(out + offs(5), out + offs(4), NT(), 1,
+                                                              (int)F(), b, sb, s));
                     return launched(launch_quantize(out + offs(5), NT(), 1, (int)F(), b, sb, s));
                 });
                 if (r) return r;
@@ -1256,7 +1266,8 @@ pf_status pf_moe_chunk(const pf_moe* moe, const float* x, int64_t T, int32_t* id
 
         pf_status st = launched(launch_quantize(x, H, Ti, (int)H, xq, xs, s));
         if (!st) st = launched(launch_router(moe->W_router, x, Ei, (int)H, Ti, logits, s));
-        if (!st) st = launched(launch_softmax_topk(logits, Ei, Ti, ki, ids, weights, s));
+        if (!st) st = launched(launch_softmax_topk(logits, Ei, Ti, ki, (int)moe->renormalize, ids,
+                                                   weights, s));
         if (!st) st = launched(launch_group(ids, weights, Ti, ki, Ei, off, pair_tok, comb_row, comb_w, s));
         if (st) return st;
         ExpertArgs gu;
@@ -1265,6 +1276,7 @@ pf_status pf_moe_chunk(const pf_moe* moe, const float* x, int64_t T, int32_t* id
         gu.off = off; gu.gather = pair_tok; gu.X = xq; gu.xs = xs; gu.Y = r;
         gu.ldx = H; gu.ldy = I; gu.N = (int)I; gu.K = (int)H; gu.E = Ei;
         gu.tiles_n = (int)((I + 63) / 64);
+        gu.act = (int)moe->activation;
         st = launched(launch_expert(gu, s));
         if (!st) st = launched(launch_quantize(r, I, Ti * ki, (int)I, hq, hs, s));
         if (st) return st;

@@ -9,6 +9,7 @@
 #include <cstring>
 
 #include "device.hpp"
+#include "expf_cr.hpp"
 #include "kernels.hpp"
 #include "problems.hpp"
 
@@ -42,15 +43,25 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s)
 // Per-token quantisation: one workgroup per token row.  amax is an exact
 // maximum (order-free); the scale and every code follow the per-token
 // definition bit for bit.
+// r = fl(silu(g) * u) elementwise (the gated SiLU's row).
+__device__ __forceinline__ float4 gated(float4 g, float4 u)
+{
+    return float4{silu_cr(g.x) * u.x, silu_cr(g.y) * u.y, silu_cr(g.z) * u.z, silu_cr(g.w) * u.w};
+}
+
+// With gate != null the row quantised is gated(gate, x), evaluated again in the
+// second pass (the same bits).
 __device__ __forceinline__ void quantize_row(const float* __restrict__ x, int K,
-                                             int8_t* __restrict__ q, float* __restrict__ scale)
+                                             int8_t* __restrict__ q, float* __restrict__ scale,
+                                             const float* __restrict__ gate = nullptr)
 {
     const float4* row = reinterpret_cast<const float4*>(x);
+    const float4* grow = reinterpret_cast<const float4*>(gate);
     int* qrow = reinterpret_cast<int*>(q);
     const int n4 = K >> 2;
     float amax = 0.0f;
     for (int i = threadIdx.x; i < n4; i += 256) {
-        const float4 v = row[i];
+        const float4 v = gate ? gated(grow[i], row[i]) : row[i];
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
     amax = wave_max(amax);
@@ -63,7 +74,7 @@ __device__ __forceinline__ void quantize_row(const float* __restrict__ x, int K,
     for (int i = threadIdx.x; i < n4; i += 256) {
         int packed = 0;
         if (s != 0.0f) {
-            const float4 v = row[i];
+            const float4 v = gate ? gated(grow[i], row[i]) : row[i];
             packed = (quant_code(v.x, s) & 0xff) | ((quant_code(v.y, s) & 0xff) << 8) |
                      ((quant_code(v.z, s) & 0xff) << 16) | ((quant_code(v.w, s) & 0xff) << 24);
         }
@@ -232,6 +243,11 @@ __device__ __forceinline__ void quant_row_regs(const QuantPair& P, int t, int K)
         const float4* row = reinterpret_cast<const float4*>(P.src + (int64_t)t * P.ld);
 #pragma unroll
         for (int u = 0; u < U; ++u) v[u] = row[idx[u]];
+        if (P.gate) {
+            const float4* grow = reinterpret_cast<const float4*>(P.gate + (int64_t)t * P.ld);
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = gated(grow[idx[u]], v[u]);
+        }
     }
     float amax = 0.0f;
 #pragma unroll
@@ -288,7 +304,25 @@ __global__ __launch_bounds__(256) void k_quantize_step(QuantStep S)
         quantize_row(P.h + (int64_t)t * P.ldh, S.K, P.q + (int64_t)t * S.K, P.s + t);
         return;
     }
-    quantize_row(P.src + (int64_t)t * P.ld, S.K, P.q + (int64_t)t * S.K, P.s + t);
+    quantize_row(P.src + (int64_t)t * P.ld, S.K, P.q + (int64_t)t * S.K, P.s + t,
+                 P.gate ? P.gate + (int64_t)t * P.ld : nullptr);
+}
+
+hipError_t launch_quantize_gated(const float* up, const float* gate, int64_t ld, int M, int K,
+                                 int8_t* q, float* scale, hipStream_t s)
+{
+    if (M <= 0) return hipSuccess;
+    QuantStep S;
+    std::memset(&S, 0, sizeof(S));
+    S.npairs = 1;
+    S.K = K;
+    S.total_rows = M;
+    S.pair[0].src = up;
+    S.pair[0].gate = gate;
+    S.pair[0].ld = ld;
+    S.pair[0].q = q;
+    S.pair[0].s = scale;
+    return launch_quantize_step(S, s);
 }
 
 hipError_t launch_quantize_step(const QuantStep& S, hipStream_t s)

@@ -98,6 +98,8 @@ struct StackStep {
 constexpr int kMaxQuant = kMaxPairs + 1;
 struct QuantPair {
     const float* src;     // mode 0 rows
+    const float* gate;    // mode 0, optional: rows [M][ld] g; the row quantised is then
+                          // r = fl(silu(g) * src), silu through the correctly rounded exp
     int8_t* q;            // [M][K] codes, or null
     float* s;             // [M] scales
     int64_t ld;           // floats between source rows
@@ -133,6 +135,7 @@ struct ExpertArgs {
     int64_t ldx, ldy;
     int N, K, E;
     int tiles_n;
+    int act;              // gate/up pair: 0 -> g * u; 1 -> silu(g) * u
 };
 
 // Host launch wrappers (return a hipError_t of the launch).
@@ -140,6 +143,9 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_quantize(const float* x, int64_t ldx, int M, int K, int8_t* q, float* scale,
                            hipStream_t s);
 hipError_t launch_quantize_step(const QuantStep& S, hipStream_t s);
+// M rows r = fl(silu(gate) * up) (rows of both at stride ld) quantised per row.
+hipError_t launch_quantize_gated(const float* up, const float* gate, int64_t ld, int M, int K,
+                                 int8_t* q, float* scale, hipStream_t s);
 hipError_t launch_gemv(const GemmSet& set, hipStream_t s);
 hipError_t launch_gemm_tiled_step(const StackStep& S, int64_t M, hipStream_t s);
 hipError_t launch_gemm_stream(const StackStep& S, int token_blocks, hipStream_t s);
@@ -157,8 +163,8 @@ int tiled_tokens(int64_t M);
 
 hipError_t launch_router(const float* Wr, const float* x, int E, int H, int T, float* logits,
                          hipStream_t s);
-hipError_t launch_softmax_topk(const float* logits, int E, int T, int k, int* ids, float* w,
-                               hipStream_t s);
+hipError_t launch_softmax_topk(const float* logits, int E, int T, int k, int renorm, int* ids,
+                               float* w, hipStream_t s);
 hipError_t launch_group(const int* ids, const float* w, int T, int k, int E, int* off,
                         int* pair_tok, int* comb_row, float* comb_w, hipStream_t s);
 hipError_t launch_expert(const ExpertArgs& a, hipStream_t s);

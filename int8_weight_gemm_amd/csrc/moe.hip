@@ -7,6 +7,7 @@
 // No host round trip: the expert plan stays in device memory.
 #include "device.hpp"
 #include "kernels.hpp"
+#include "expf_cr.hpp"
 #include "lds_dma.hpp"
 
 namespace pf {
@@ -121,108 +122,6 @@ hipError_t launch_router(const float* Wr, const float* x, int E, int H, int T, f
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Correctly rounded binary32 exp.  exp(x) is evaluated in double-double
-// arithmetic (about 95 correct bits after the squarings below), far more than
-// the roughly 24 + 40 bits that any binary32 argument needs to decide its
-// rounding, and the double-double value is then rounded to binary32 exactly.
-//   x = k ln2 + r, |r| <= ln2/2 (k = rint(x / ln2); k ln2 in double-double);
-//   s = r / 2^10;  e^s - 1 by its Taylor series to s^10 (|s| < 3.4e-4);
-//   (1 + m)^(2^10) by ten squarings m <- 2m + m^2;  e^x = 2^k (1 + m).
-struct dd {
-    double hi, lo;
-};
-
-__device__ __forceinline__ dd two_sum(double a, double b)
-{
-    const double s = a + b;
-    const double bb = s - a;
-    const double e = (a - (s - bb)) + (b - bb);
-    return {s, e};
-}
-__device__ __forceinline__ dd fast_two_sum(double a, double b)
-{
-    const double s = a + b;
-    const double e = b - (s - a);
-    return {s, e};
-}
-__device__ __forceinline__ dd two_prod(double a, double b)
-{
-    const double p = a * b;
-    const double e = fma(a, b, -p);
-    return {p, e};
-}
-__device__ __forceinline__ dd dd_add(dd a, dd b)
-{
-    dd s = two_sum(a.hi, b.hi);
-    const dd t = two_sum(a.lo, b.lo);
-    s.lo = s.lo + t.hi;
-    s = fast_two_sum(s.hi, s.lo);
-    s.lo = s.lo + t.lo;
-    return fast_two_sum(s.hi, s.lo);
-}
-__device__ __forceinline__ dd dd_mul(dd a, dd b)
-{
-    dd p = two_prod(a.hi, b.hi);
-    const double c = a.hi * b.lo;
-    const double d = a.lo * b.hi;
-    p.lo = p.lo + (c + d);
-    return fast_two_sum(p.hi, p.lo);
-}
-__device__ __forceinline__ dd dd_mul_d(dd a, double b)
-{
-    dd p = two_prod(a.hi, b);
-    p.lo = p.lo + a.lo * b;
-    return fast_two_sum(p.hi, p.lo);
-}
-__device__ __forceinline__ dd dd_div_d(dd a, double b)
-{
-    const double q1 = a.hi / b;
-    const dd p = two_prod(q1, b);
-    const double r = ((a.hi - p.hi) - p.lo + a.lo) / b;
-    return fast_two_sum(q1, r);
-}
-
-// ln 2 split into double-double: the nearest double and the nearest double to
-// the remainder.
-__device__ constexpr double kLn2Hi = 0x1.62e42fefa39efp-1;
-__device__ constexpr double kLn2Lo = 0x1.abc9e3b39803fp-56;
-
-__device__ float expf_cr(float xf)
-{
-    if (xf != xf) return xf;
-    if (xf < -104.0f) return 0.0f;    // exp(x) < 2^-150: rounds to +0
-    if (xf > 89.0f) return __builtin_huge_valf();
-    if (xf == 0.0f) return 1.0f;
-    const double x = (double)xf;
-    const double k = rint(x * (1.0 / kLn2Hi));
-    const dd kl = dd_mul_d(dd{kLn2Hi, kLn2Lo}, k);
-    const dd r = dd_add(dd{x, 0.0}, dd{-kl.hi, -kl.lo});
-    const dd s{ldexp(r.hi, -10), ldexp(r.lo, -10)};
-    // m = e^s - 1 = s (1 + s/2 (1 + s/3 (1 + ... (1 + s/10))))
-    dd m{1.0, 0.0};
-    for (int n = 10; n >= 2; --n) m = dd_add(dd{1.0, 0.0}, dd_mul(dd_div_d(s, (double)n), m));
-    m = dd_mul(s, m);
-    for (int i = 0; i < 10; ++i) m = dd_add(dd_mul_d(m, 2.0), dd_mul(m, m));
-    dd y = dd_add(dd{1.0, 0.0}, m);
-    const int ki = (int)k;
-    y.hi = ldexp(y.hi, ki);
-    y.lo = ldexp(y.lo, ki);
-    // Round hi + lo to binary32.  f = RN(hi); the exact value lies on the far
-    // side of the midpoint between f and its neighbour only if hi is that
-    // midpoint and lo points away from f.
-    float f = (float)y.hi;
-    const double d = y.hi - (double)f;   // exact
-    if (d != 0.0) {
-        const float g = d > 0.0 ? nextafterf(f, __builtin_huge_valf()) : nextafterf(f, 0.0f);
-        const double half = ((double)g - (double)f) * 0.5;
-        if (d == half && ((d > 0.0 && y.lo > 0.0) || (d < 0.0 && y.lo < 0.0))) f = g;
-    } else if (y.lo != 0.0) {
-        // hi is a binary32 value: the exact value differs by |lo| << half a unit
-    }
-    return f;
-}
-
 __global__ __launch_bounds__(256) void k_expf(const float* __restrict__ x, int64_t n,
                                               float* __restrict__ y)
 {
@@ -261,7 +160,7 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 }
 
 __global__ __launch_bounds__(1024) void k_softmax_topk(const float* __restrict__ logits, int E, int T,
-                                                       int k, int* __restrict__ ids,
+                                                       int k, int renorm, int* __restrict__ ids,
                                                        float* __restrict__ w)
 {
     __shared__ __attribute__((aligned(16))) float zs[kSmMaxE];
@@ -306,23 +205,41 @@ __global__ __launch_bounds__(1024) void k_softmax_topk(const float* __restrict__
     // candidates above it (the keys are distinct), so every candidate finds its
     // place at once and the first k write their (id, weight)
     const int nc = nw * kw;
+    __shared__ float chosen[kSmMaxK];
+    int place = k;
+    unsigned long long mine = 0ull;
     if (e < nc) {
-        const unsigned long long mine = cand[e];
-        int place = 0;
+        mine = cand[e];
+        place = 0;
         for (int j = 0; j < nc; ++j) place += cand[j] > mine;
         if (place < k) {
             ids[(int64_t)t * k + place] = (int)(0xffffffffu - (unsigned)(mine & 0xffffffffu));
-            w[(int64_t)t * k + place] = __uint_as_float((unsigned)(mine >> 32));
+            chosen[place] = __uint_as_float((unsigned)(mine >> 32));
         }
     }
+    if (!renorm) {
+        if (place < k) w[(int64_t)t * k + place] = chosen[place];
+        return;
+    }
+    // renormalised over the chosen: T = the chosen p summed in rank order
+    // (one lane, sequentially), then w = p / T
+    __syncthreads();
+    __shared__ float sT;
+    if (e == 0) {
+        float Tk = 0.0f;
+        for (int j = 0; j < k; ++j) Tk = Tk + chosen[j];
+        sT = Tk;
+    }
+    __syncthreads();
+    if (place < k) w[(int64_t)t * k + place] = chosen[place] / sT;
 }
 
-hipError_t launch_softmax_topk(const float* logits, int E, int T, int k, int* ids, float* w,
-                               hipStream_t s)
+hipError_t launch_softmax_topk(const float* logits, int E, int T, int k, int renorm, int* ids,
+                               float* w, hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
     if (E > kSmMaxE || k > kSmMaxK) return hipErrorInvalidValue;
-    PF_LAUNCH(k_softmax_topk, dim3(T), dim3(64 * ((E + 63) / 64)), 0, s, logits, E, T, k, ids, w);
+    PF_LAUNCH(k_softmax_topk, dim3(T), dim3(64 * ((E + 63) / 64)), 0, s, logits, E, T, k, renorm, ids, w);
     return hipGetLastError();
 }
 
@@ -501,7 +418,7 @@ __global__ __launch_bounds__(256) void k_expert(ExpertArgs A)
                 const float g = epilogue(acc0[tb][q], A.s0[(int64_t)e * A.N + n], xs);
                 if (kPair) {
                     const float u = epilogue(acc1[tb][q], A.s1[(int64_t)e * A.N + n], xs);
-                    yrow[n] = g * u;
+                    yrow[n] = (A.act ? silu_cr(g) : g) * u;
                 } else {
                     yrow[n] = g;
                 }
@@ -636,7 +553,7 @@ __global__ __launch_bounds__(256) void k_expert_stream(ExpertArgs A)
                         const float g = epilogue(acc[0][tb][q], ws0[rb][q], xsv[tb]);
                         if (kPair) {
                             const float u = epilogue(acc[M - 1][tb][q], ws1[rb][q], xsv[tb]);
-                            vp[q] = g * u;
+                            vp[q] = (A.act ? silu_cr(g) : g) * u;
                         } else {
                             vp[q] = g;
                         }
