@@ -186,7 +186,7 @@ __device__ __forceinline__ void rebuild_row(const QuantPair& P, int t, int K)
 // row is issued before any is used (the split partials four splits at a time
 // up to U = 4), and the codes come from the registers, so the row is read once.
 // Same arithmetic as rebuild_row followed by quantize_row.
-template <int U>
+template <int U, bool kGated>
 __device__ __forceinline__ void quant_row_regs(const QuantPair& P, int t, int K)
 {
     const int n4 = K >> 2;
@@ -243,7 +243,7 @@ __device__ __forceinline__ void quant_row_regs(const QuantPair& P, int t, int K)
         const float4* row = reinterpret_cast<const float4*>(P.src + (int64_t)t * P.ld);
 #pragma unroll
         for (int u = 0; u < U; ++u) v[u] = row[idx[u]];
-        if (P.gate) {
+        if (kGated) {
             const float4* grow = reinterpret_cast<const float4*>(P.gate + (int64_t)t * P.ld);
 #pragma unroll
             for (int u = 0; u < U; ++u) v[u] = gated(grow[idx[u]], v[u]);
@@ -277,7 +277,7 @@ __device__ __forceinline__ void quant_row_regs(const QuantPair& P, int t, int K)
 // Rows of up to 4096 values (kLong = false) or longer (kLong, with more
 // registers per thread; a separate kernel so the short rows keep their
 // occupancy).
-template <bool kLong>
+template <bool kLong, bool kGated>
 __global__ __launch_bounds__(256) void k_quantize_step(QuantStep S)
 {
     const int bid = blockIdx.x;
@@ -289,13 +289,13 @@ __global__ __launch_bounds__(256) void k_quantize_step(QuantStep S)
     const int t = bid - P.row0;
     const int n4 = S.K >> 2;
     if (kLong) {
-        if (n4 <= 2048) return quant_row_regs<8>(P, t, S.K);
-        if (n4 <= 3072) return quant_row_regs<12>(P, t, S.K);
-        if (n4 <= 4096) return quant_row_regs<16>(P, t, S.K);
+        if (n4 <= 2048) return quant_row_regs<8, kGated>(P, t, S.K);
+        if (n4 <= 3072) return quant_row_regs<12, kGated>(P, t, S.K);
+        if (n4 <= 4096) return quant_row_regs<16, kGated>(P, t, S.K);
     } else {
-        if (n4 <= 256) return quant_row_regs<1>(P, t, S.K);
-        if (n4 <= 512) return quant_row_regs<2>(P, t, S.K);
-        if (n4 <= 1024) return quant_row_regs<4>(P, t, S.K);
+        if (n4 <= 256) return quant_row_regs<1, kGated>(P, t, S.K);
+        if (n4 <= 512) return quant_row_regs<2, kGated>(P, t, S.K);
+        if (n4 <= 1024) return quant_row_regs<4, kGated>(P, t, S.K);
     }
     if (P.part) {
         rebuild_row(P, t, S.K);
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256) void k_quantize_step(QuantStep S)
         return;
     }
     quantize_row(P.src + (int64_t)t * P.ld, S.K, P.q + (int64_t)t * S.K, P.s + t,
-                 P.gate ? P.gate + (int64_t)t * P.ld : nullptr);
+                 kGated ? P.gate + (int64_t)t * P.ld : nullptr);
 }
 
 hipError_t launch_quantize_gated(const float* up, const float* gate, int64_t ld, int M, int K,
@@ -328,8 +328,19 @@ hipError_t launch_quantize_gated(const float* up, const float* gate, int64_t ld,
 hipError_t launch_quantize_step(const QuantStep& S, hipStream_t s)
 {
     if (S.total_rows <= 0) return hipSuccess;
-    if (S.K > 4096) PF_LAUNCH(k_quantize_step<true>, dim3(S.total_rows), dim3(256), 0, s, S);
-    else PF_LAUNCH(k_quantize_step<false>, dim3(S.total_rows), dim3(256), 0, s, S);
+    // gated rows (every pair of a launch alike) in their own instantiations, so
+    // that the plain ones carry no call
+    const bool gated = S.pair[0].gate != nullptr;
+    for (int i = 1; i < S.npairs; ++i)
+        if ((S.pair[i].gate != nullptr) != gated) return hipErrorInvalidValue;
+    const dim3 g(S.total_rows), b(256);
+    if (gated) {
+        if (S.K > 4096) PF_LAUNCH((k_quantize_step<true, true>), g, b, 0, s, S);
+        else PF_LAUNCH((k_quantize_step<false, true>), g, b, 0, s, S);
+    } else {
+        if (S.K > 4096) PF_LAUNCH((k_quantize_step<true, false>), g, b, 0, s, S);
+        else PF_LAUNCH((k_quantize_step<false, false>), g, b, 0, s, S);
+    }
     return hipGetLastError();
 }
 

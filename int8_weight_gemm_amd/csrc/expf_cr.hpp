@@ -72,12 +72,10 @@ __device__ __forceinline__ dd dd_div_d(dd a, double b)
 __device__ constexpr double kLn2Hi = 0x1.62e42fefa39efp-1;
 __device__ constexpr double kLn2Lo = 0x1.abc9e3b39803fp-56;
 
-static __device__ __noinline__ float expf_cr(float xf)
+// The double-double evaluation (the rare arguments the double one below
+// cannot round with certainty).  -104 <= x <= 89, x != 0.
+static __device__ __noinline__ float expf_cr_dd(float xf)
 {
-    if (xf != xf) return xf;
-    if (xf < -104.0f) return 0.0f;    // exp(x) < 2^-150: rounds to +0
-    if (xf > 89.0f) return __builtin_huge_valf();
-    if (xf == 0.0f) return 1.0f;
     const double x = (double)xf;
     const double k = rint(x * (1.0 / kLn2Hi));
     const dd kl = dd_mul_d(dd{kLn2Hi, kLn2Lo}, k);
@@ -113,9 +111,57 @@ static __device__ __noinline__ float expf_cr(float xf)
     return f;
 }
 
+// Correctly rounded binary32 exp.  Most arguments take one double evaluation:
+//   x = k ln2 + r with ln2 split Cody-Waite style (k ln2_hi exact, |r| <= ln2/2),
+//   e^r by its Taylor polynomial of degree 13 in Horner form with fused
+//   multiply-adds (truncation below 2^-56, rounding below 2^-52 relative),
+//   e^x = 2^k e^r: relative error below 2^-51.
+// Its binary32 rounding f is the correct one unless the double lies within
+// 2^-45 (relative) of the midpoint between f and its neighbour on its side, a
+// margin of 64 times the error bound; those arguments, and those whose value
+// overflows binary32, go to the double-double evaluation.
+__device__ constexpr double kLn2CwHi = 0x1.62e42fee00000p-1;   // 32 significant bits
+__device__ constexpr double kLn2CwLo = 0x1.a39ef35793c76p-33;  // ln 2 - kLn2CwHi, rounded
+
+__device__ __forceinline__ float expf_cr(float xf)
+{
+    if (xf != xf) return xf;
+    if (xf < -104.0f) return 0.0f;    // exp(x) < 2^-150: rounds to +0
+    if (xf > 89.0f) return __builtin_huge_valf();
+    if (xf == 0.0f) return 1.0f;
+    const double x = (double)xf;
+    const double k = rint(x * 0x1.71547652b82fep0);      // x / ln 2, nearest integer
+    const double r = (x - k * kLn2CwHi) - k * kLn2CwLo;  // first difference exact
+    double p = 1.0 / 6227020800.0;                        // 1/13!
+    p = fma(p, r, 1.0 / 479001600.0);
+    p = fma(p, r, 1.0 / 39916800.0);
+    p = fma(p, r, 1.0 / 3628800.0);
+    p = fma(p, r, 1.0 / 362880.0);
+    p = fma(p, r, 1.0 / 40320.0);
+    p = fma(p, r, 1.0 / 5040.0);
+    p = fma(p, r, 1.0 / 720.0);
+    p = fma(p, r, 1.0 / 120.0);
+    p = fma(p, r, 1.0 / 24.0);
+    p = fma(p, r, 1.0 / 6.0);
+    p = fma(p, r, 0.5);
+    p = fma(p, r, 1.0);
+    p = fma(p, r, 1.0);
+    const double y = ldexp(p, (int)k);
+    const float f = (float)y;
+    if (!__builtin_isinf(f)) {
+        const double dy = y - (double)f;                  // exact
+        if (dy == 0.0) return f;
+        const float nb = dy > 0.0 ? nextafterf(f, __builtin_huge_valf()) : nextafterf(f, -__builtin_huge_valf());
+        const double mid = ((double)f + (double)nb) * 0.5; // exact
+        if (fabs(y - mid) > fabs(y) * 0x1p-45) return f;
+    }
+    return expf_cr_dd(xf);
+}
+
 // silu(g) = fl(g / fl(1 + expf_cr(-g))), each operation rounded on its own;
-// past g = -88.72 exp(-g) is +inf and the quotient -0.
-__device__ __forceinline__ float silu_cr(float g)
+// past g = -88.72 exp(-g) is +inf and the quotient -0.  Out of line: it sits
+// in the epilogues of fully unrolled product loops.
+static __device__ __noinline__ float silu_cr(float g)
 {
     const float e = expf_cr(-g);
     const float d = 1.0f + e;

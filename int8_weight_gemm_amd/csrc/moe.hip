@@ -436,7 +436,7 @@ __global__ __launch_bounds__(256) void k_expert(ExpertArgs A)
 // 64 bytes of each weight) ahead across row-block boundaries, with no barrier
 // inside the stream.  The stream is unrolled, so every ring slot and wait is
 // fixed at compile time.
-template <bool kPair, int RB, int D, int KB>
+template <bool kPair, int RB, int D, int KB, bool kSilu = false>
 __global__ __launch_bounds__(256) void k_expert_stream(ExpertArgs A)
 {
     constexpr int M = kPair ? 2 : 1;              // weights read per fragment
@@ -553,7 +553,7 @@ __global__ __launch_bounds__(256) void k_expert_stream(ExpertArgs A)
                         const float g = epilogue(acc[0][tb][q], ws0[rb][q], xsv[tb]);
                         if (kPair) {
                             const float u = epilogue(acc[M - 1][tb][q], ws1[rb][q], xsv[tb]);
-                            vp[q] = (A.act ? silu_cr(g) : g) * u;
+                            vp[q] = (kSilu ? silu_cr(g) : g) * u;
                         } else {
                             vp[q] = g;
                         }
@@ -584,7 +584,11 @@ hipError_t launch_expert(const ExpertArgs& a, hipStream_t s)
         const int rb = a.W1 ? 1 : (a.K == 2048 ? 2 : 4);
         c.tiles_n = (a.N + 64 * rb - 1) / (64 * rb);
         const dim3 g(a.E * c.tiles_n);
-        if (a.W1) {
+        if (a.W1 && a.act) {
+            if (a.K == 512) PF_LAUNCH((k_expert_stream<true, 1, 8, 8, true>), g, b, 0, s, c);
+            else if (a.K == 1024) PF_LAUNCH((k_expert_stream<true, 1, 8, 16, true>), g, b, 0, s, c);
+            else PF_LAUNCH((k_expert_stream<true, 1, 8, 32, true>), g, b, 0, s, c);
+        } else if (a.W1) {
             if (a.K == 512) PF_LAUNCH((k_expert_stream<true, 1, 8, 8>), g, b, 0, s, c);
             else if (a.K == 1024) PF_LAUNCH((k_expert_stream<true, 1, 8, 16>), g, b, 0, s, c);
             else PF_LAUNCH((k_expert_stream<true, 1, 8, 32>), g, b, 0, s, c);

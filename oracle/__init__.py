@@ -55,6 +55,7 @@ def _load():
             "or_gemv": [P, P, I64, I64, P, F, P],
             "or_linear_per_token": [P, P, I64, I64, P, P, I64, P, INT],
             "or_stack": [I64, I64, I64, P, P, P, I64, P, P, INT, INT],
+            "or_stack_attn": [I64, I64, I64, I64, P, P, P, I64, P, P, P, INT, INT],
             "or_router": [P, I64, I64, P, P],
             "or_expf_cr_array": [P, I64, P, INT],
             "or_softmax_topk": [P, I64, I64, P, P, INT],
@@ -160,6 +161,36 @@ def stack(weights, scales, x, return_proj: bool = False, threads: int | None = N
                           threads or default_threads(), int(act))
     _check(rc, "or_stack")
     return (y, proj) if return_proj else y
+
+
+def stack_attn(weights, scales, x, n_heads: int, return_proj: bool = False,
+               threads: int | None = None, act: int = ACT_NONE):
+    """The stack with causal attention (n_heads heads), layer by layer over the
+    prompt.  Returns (y [P, H], kv [L, 2, P, H]) and, with ``return_proj``, also
+    every projection output [L, P, 5H + 2F] (o from the attention)."""
+    L = len(weights)
+    x = _c(np.atleast_2d(x), np.float32)
+    P, H = x.shape
+    F = weights[0][4].shape[0]
+    keep = []
+    wp = (ctypes.c_void_p * (7 * L))()
+    sp = (ctypes.c_void_p * (7 * L))()
+    for l in range(L):
+        for j in range(7):
+            w = _c(weights[l][j], np.int8)
+            s = _c(scales[l][j], np.float32)
+            keep += [w, s]
+            wp[l * 7 + j] = w.ctypes.data
+            sp[l * 7 + j] = s.ctypes.data
+    y = np.empty((P, H), np.float32)
+    kv = np.empty((L, 2, P, H), np.float32)
+    proj = np.empty((L, P, 5 * H + 2 * F), np.float32) if return_proj else None
+    rc = _load().or_stack_attn(L, H, F, n_heads, ctypes.cast(wp, ctypes.c_void_p),
+                               ctypes.cast(sp, ctypes.c_void_p), _ptr(x), P, _ptr(y),
+                               _ptr(proj) if proj is not None else None, _ptr(kv),
+                               threads or default_threads(), int(act))
+    _check(rc, "or_stack_attn")
+    return (y, kv, proj) if return_proj else (y, kv)
 
 
 def expf_cr(x, threads: int | None = None) -> np.ndarray:

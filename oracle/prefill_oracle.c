@@ -159,6 +159,148 @@ int or_stack(int64_t L, int64_t H, int64_t F, const int8_t* const* W,
     return status;
 }
 
+/* Causal attention of one token over the K/V history of its layer ("Batched
+ * Prefill", What Stays Sequential: attention runs per position inside each
+ * chunk; "Single-pass prefill", "The fix": position t attends over
+ * kv_[layer][0..t], written before it).  For head hd (d = H / n_heads values
+ * from column hd*d): s_j = fl(dot(q, K[j]) * c) for j = 0..t, the dot an f32 sum
+ * in ascending index of separately rounded products and c = fl(1 / fl(sqrt(d)));
+ * m = max s_j; z_j = expf_cr(fl(s_j - m)); S = sum of z_j in ascending j;
+ * p_j = fl(z_j / S); out[i] = sum over j ascending of fl(p_j * V[j][i]) from +0.
+ * K and V point at position 0 of the layer's cache, rows of H values. */
+static void attend(const float* q, const float* K, const float* V, int64_t t, int64_t H,
+                   int64_t n_heads, float* z, float* out)
+{
+    const int64_t d = H / n_heads;
+    const float c = 1.0f / sqrtf((float)d);
+    for (int64_t hd = 0; hd < n_heads; ++hd) {
+        const int64_t c0 = hd * d;
+        float m = 0.0f;
+        for (int64_t j = 0; j <= t; ++j) {
+            float acc = 0.0f;
+            for (int64_t i = 0; i < d; ++i) {
+                float pr = q[c0 + i] * K[j * H + c0 + i];
+                acc = acc + pr;
+            }
+            z[j] = acc * c;
+            if (j == 0 || z[j] > m) m = z[j];
+        }
+        float S = 0.0f;
+        for (int64_t j = 0; j <= t; ++j) {
+            z[j] = or_expf_cr(z[j] - m);
+            S = S + z[j];
+        }
+        for (int64_t j = 0; j <= t; ++j) z[j] = z[j] / S;
+        for (int64_t i = 0; i < d; ++i) {
+            float o = 0.0f;
+            for (int64_t j = 0; j <= t; ++j) {
+                float pr = z[j] * V[j * H + c0 + i];
+                o = o + pr;
+            }
+            out[c0 + i] = o;
+        }
+    }
+}
+
+/* The stack with causal attention, swept the way "Single-pass prefill"
+ * describes ("The fix"): for each layer, every prompt position goes through it
+ * in order, and position t's attention reads the K/V history 0..t of that
+ * layer.  Per layer and token, with h the layer input:
+ *   (a, sa) = quantise(h); q, k, v, gate, up = gemv(., a, sa);
+ *   kv[l][0][t] = k, kv[l][1][t] = v (the cache);
+ *   att = attend(q, kv[l][0][0..t], kv[l][1][0..t]);
+ *   (ao, sao) = quantise(att); o = gemv(W_o, ao, sao);
+ *   (b, sb) = quantise(up) (or quantise(silu(gate) * up) with OR_ACT_SWIGLU);
+ *   down = gemv(W_down, b, sb); the next layer's h = down.
+ * The attention output feeds o, which, as in or_stack, feeds nothing further.
+ * Tokens of one phase are independent, so each phase runs over all tokens of
+ * the layer (threads over tokens) before the next. */
+int or_stack_attn(int64_t L, int64_t H, int64_t F, int64_t n_heads, const int8_t* const* W,
+                  const float* const* w_scale, const float* x, int64_t P, float* y,
+                  float* proj, float* kv, int threads, int act)
+{
+    if (!W || !w_scale || !x || !y || !kv || L <= 0 || H <= 0 || F <= 0 || P < 0) return -1;
+    if (H > 131072 || F > 131072 || n_heads <= 0 || H % n_heads != 0) return -1;
+    if (act != OR_ACT_NONE && act != OR_ACT_SWIGLU) return -1;
+    for (int64_t i = 0; i < 7 * L; ++i)
+        if (!W[i] || !w_scale[i]) return -1;
+    if (threads < 1) threads = 1;
+    const int64_t nrow[7] = {H, H, H, H, F, F, H};
+    int64_t off[8];
+    off[0] = 0;
+    for (int j = 0; j < 7; ++j) off[j + 1] = off[j] + nrow[j];
+    const int64_t total = off[7];
+    float* h = (float*)malloc(sizeof(float) * (size_t)(P * H + 1));
+    float* outs = (float*)malloc(sizeof(float) * (size_t)(P * total + 1));
+    if (!h || !outs) { free(h); free(outs); return -1; }
+    memcpy(h, x, sizeof(float) * (size_t)(P * H));
+    int status = 0;
+    for (int64_t l = 0; l < L && !status; ++l) {
+        float* Kc = kv + (l * 2 + 0) * P * H;
+        float* Vc = kv + (l * 2 + 1) * P * H;
+        /* projections from quantise(h) (o comes after the attention) */
+#pragma omp parallel for num_threads(threads) schedule(dynamic, 1)
+        for (int64_t t = 0; t < P; ++t) {
+            int8_t* a = (int8_t*)malloc((size_t)H);
+            float sa;
+            if (!a || quantize_row(h + t * H, H, a, &sa)) {
+#pragma omp atomic write
+                status = -2;
+                free(a);
+                continue;
+            }
+            float* ot = outs + t * total;
+            const int js[5] = {0, 1, 2, 4, 5};
+            for (int u = 0; u < 5; ++u) {
+                const int j = js[u];
+                gemv_row_block(W[l * 7 + j], w_scale[l * 7 + j], nrow[j], H, a, sa, ot + off[j]);
+            }
+            memcpy(Kc + t * H, ot + off[1], sizeof(float) * (size_t)H);
+            memcpy(Vc + t * H, ot + off[2], sizeof(float) * (size_t)H);
+            free(a);
+        }
+        if (status) break;
+        /* attention over positions 0..t, then o; the gated input of down; down */
+#pragma omp parallel for num_threads(threads) schedule(dynamic, 1)
+        for (int64_t t = 0; t < P; ++t) {
+            float* z = (float*)malloc(sizeof(float) * (size_t)(P + 1));
+            float* att = (float*)malloc(sizeof(float) * (size_t)H);
+            float* r = (float*)malloc(sizeof(float) * (size_t)F);
+            int8_t* a = (int8_t*)malloc((size_t)(F > H ? F : H));
+            float* ot = outs + t * total;
+            int bad = (!z || !att || !r || !a);
+            if (!bad) {
+                attend(ot + off[0], Kc, Vc, t, H, n_heads, z, att);
+                float so;
+                bad = quantize_row(att, H, a, &so) != 0;
+                if (!bad) gemv_row_block(W[l * 7 + 3], w_scale[l * 7 + 3], H, H, a, so, ot + off[3]);
+            }
+            if (!bad) {
+                const float* din = ot + off[5];
+                if (act == OR_ACT_SWIGLU) {
+                    for (int64_t i = 0; i < F; ++i) r[i] = or_silu(ot[off[4] + i]) * ot[off[5] + i];
+                    din = r;
+                }
+                float sb;
+                bad = quantize_row(din, F, a, &sb) != 0;
+                if (!bad) gemv_row_block(W[l * 7 + 6], w_scale[l * 7 + 6], H, F, a, sb, ot + off[6]);
+            }
+            if (bad) {
+#pragma omp atomic write
+                status = -2;
+            } else {
+                if (proj) memcpy(proj + (l * P + t) * total, ot, sizeof(float) * (size_t)total);
+                memcpy(h + t * H, ot + off[6], sizeof(float) * (size_t)H);
+            }
+            free(z); free(att); free(r); free(a);
+        }
+    }
+    if (!status) memcpy(y, h, sizeof(float) * (size_t)(P * H));
+    free(h);
+    free(outs);
+    return status;
+}
+
 /* Correctly rounded exp in binary32.  expl works in the x87 64-bit-significand
  * format with error below one unit of that format, i.e. about 2^-63 relative,
  * while rounding to binary32 needs to know on which side of the midpoint between

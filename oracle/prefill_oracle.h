@@ -75,6 +75,20 @@ int or_stack(int64_t L, int64_t H, int64_t F, const int8_t* const* W,
              const float* const* w_scale, const float* x, int64_t P, float* y,
              float* proj, int threads, int act);
 
+/* The stack with causal attention over the prompt (n_heads heads of
+ * d = H / n_heads values) [cellm §What Stays Sequential: attention runs per
+ * position; sip "The fix": position t attends over the K/V history
+ * kv_[layer][0..t]].  Per layer, each token's q, k, v, gate, up come from
+ * quantise(h); k and v are written to the cache kv [L][2][P][H] (k at [l][0],
+ * v at [l][1]); the token's attention over positions 0..t of its layer
+ * (per head: f32 scores in ascending index with c = fl(1/fl(sqrt(d))), softmax
+ * with expf_cr and an ascending sum, the probability-weighted sum of v rows in
+ * ascending position) is quantised and feeds o; down as in or_stack.  y, proj as
+ * in or_stack. */
+int or_stack_attn(int64_t L, int64_t H, int64_t F, int64_t n_heads, const int8_t* const* W,
+                  const float* const* w_scale, const float* x, int64_t P, float* y,
+                  float* proj, float* kv, int threads, int act);
+
 /* Correctly rounded binary32 exp (the exact exponential rounded to nearest,
  * ties to even).  Aborts if the long-double evaluation cannot decide the
  * rounding (never observed on the domain used; checked exhaustively by the

@@ -162,3 +162,77 @@ def softmax_topk(logits, k, renorm: bool = False) -> tuple[list[int], list[float
             T = f32_round(fr(T) + fr(v))
         w = [f32_round(fr(v) / fr(T)) for v in w]
     return order, w, p
+
+
+def dot_seq(a, b) -> float:
+    """acc = 0; for i ascending acc = RN(acc + RN(a_i * b_i))."""
+    acc = 0.0
+    for x, y in zip(a, b):
+        acc = f32_round(fr(acc) + fr(f32_round(fr(x) * fr(y))))
+    return acc
+
+
+def attend(q, K, V, t, n_heads) -> list[float]:
+    """Causal attention of one token over rows 0..t of K and V (each a list of
+    H floats): per head scores RN(dot * c), c = RN(1 / RN(sqrt(d))), softmax
+    with the correctly rounded exp and an ascending sum, then the ascending
+    sum of RN(p_j * V[j][i])."""
+    H = len(q)
+    d = H // n_heads
+    root = f32_round(_sqrt_fraction(d))
+    c = f32_round(1 / fr(root))
+    out = [0.0] * H
+    for hd in range(n_heads):
+        cols = range(hd * d, hd * d + d)
+        s = [f32_round(fr(dot_seq([q[i] for i in cols], [K[j][i] for i in cols])) * fr(c))
+             for j in range(t + 1)]
+        m = max(s)
+        z = [exp_cr(f32_round(fr(v) - fr(m))) for v in s]
+        S = 0.0
+        for v in z:
+            S = f32_round(fr(S) + fr(v))
+        p = [f32_round(fr(v) / fr(S)) for v in z]
+        for i in cols:
+            o = 0.0
+            for j in range(t + 1):
+                o = f32_round(fr(o) + fr(f32_round(fr(p[j]) * fr(V[j][i]))))
+            out[i] = o
+    return out
+
+
+def _sqrt_fraction(d: int) -> Fraction:
+    """sqrt(d) to 80 digits as an exact rational (its binary32 rounding is then
+    the correctly rounded square root)."""
+    with mpmath.workdps(80):
+        man, exp = mpmath.mpf(mpmath.sqrt(d)).man_exp
+    return Fraction(int(man)) * (Fraction(2) ** int(exp))
+
+
+def stack_attn(weights, scales, x, n_heads, act: int = 0):
+    """The stack with causal attention, layer by layer over all tokens, from the
+    brute-force pieces.  Returns (y, kv, per-layer projection rows)."""
+    P = len(x)
+    hs = [[float(v) for v in np.asarray(row, np.float32)] for row in x]
+    L = len(weights)
+    kv = [[[None] * P, [None] * P] for _ in range(L)]
+    proj = [[None] * P for _ in range(L)]
+    for l, (wl, sl) in enumerate(zip(weights, scales)):
+        outs = []
+        for t in range(P):
+            a, sa = quantize_row(np.array(hs[t], np.float32))
+            o = {j: gemv(wl[j], sl[j], a, sa) for j in (0, 1, 2, 4, 5)}
+            kv[l][0][t], kv[l][1][t] = o[1], o[2]
+            outs.append(o)
+        for t in range(P):
+            o = outs[t]
+            att = attend(o[0], kv[l][0], kv[l][1], t, n_heads)
+            ao, so = quantize_row(np.array(att, np.float32))
+            o[3] = gemv(wl[3], sl[3], ao, so)
+            din = o[5]
+            if act:
+                din = [f32_round(fr(silu(g)) * fr(u)) for g, u in zip(o[4], o[5])]
+            b, sb = quantize_row(np.array(din, np.float32))
+            o[6] = gemv(wl[6], sl[6], b, sb)
+            proj[l][t] = sum((o[j] for j in range(7)), [])
+            hs[t] = o[6]
+    return hs, kv, proj
