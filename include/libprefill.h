@@ -162,6 +162,21 @@ typedef struct {
      * the layer input, so long chains of it grow or shrink without bound: it
      * suits stacks of a few layers (the expert layer is one). */
     int64_t activation;
+    /* 0: no attention (o reads quantise(h), as q, k, v do).  n_heads > 0 adds
+     * the causal attention of "Batched Prefill" (§What Stays Sequential: it
+     * runs per position inside each chunk) over the K/V cache that the call
+     * writes ("Single-pass prefill", "The fix": position t attends over the
+     * K/V history kv_[layer][0..t]).  Per layer and token: q, k, v, gate, up
+     * from quantise(h); k and v written to the cache; per head of d = H /
+     * n_heads values, s_j = fl(dot(q, k_j) * c) over positions j = 0..t (the
+     * dot an f32 sum in ascending index of separately rounded products,
+     * c = fl(1 / fl(sqrt(d)))), m = max s_j, z_j = expf_cr(fl(s_j - m)),
+     * S = the z_j summed in ascending j, p_j = fl(z_j / S), out = the
+     * ascending-j sum of fl(p_j * v_j) from +0; then o = product of W_o with
+     * quantise(out).  o feeds nothing further, so y is the same as without
+     * attention.  Requires H % n_heads == 0, d % 4 == 0, d <= 256 and
+     * H <= 8192. */
+    int64_t n_heads;
 } pf_stack;
 
 #define PF_ACT_NONE 0
@@ -197,6 +212,9 @@ typedef struct {
     double product_busy_ms;    /* time at least one product ran (time_kernels)    */
     double quant_busy_ms;      /* time at least one quantisation ran (time_kernels) */
     double overhead_bytes;     /* split-K partials written and read back          */
+    int64_t attn_launches;     /* attention launches (stacks with n_heads > 0)    */
+    double attn_alg_bytes;     /* q rows, the K/V history once per (chunk, layer), codes */
+    double attn_ms;            /* summed device time of the attention launches    */
 } pf_stack_stats;
 
 /* Workspace bytes for pf_prefill_stack with this stack and chunk size. */
@@ -210,13 +228,15 @@ PF_API size_t pf_prefill_stack_workspace(const pf_stack* stack, int64_t chunk);
  *   (b, sb) = quantise(up); down = product with b; the next layer's h = down.
  * x [P][H] f32 -> y [P][H] f32 (the last layer's down).  proj, when not NULL,
  * receives every projection output: proj [L][P][5H + 2F] f32, each row holding
- * q, k, v, o, gate, up, down concatenated.  With the environment variable
+ * q, k, v, o, gate, up, down concatenated.  kv, required when the stack has
+ * n_heads > 0 (ignored otherwise), receives the K/V cache: kv [L][2][P][H] f32,
+ * k of layer l and position t at kv[l][0][t], v at kv[l][1][t].  With the environment variable
  * PF_BATCHED_PREFILL=0 the same call runs one GEMV per token and projection
  * instead (the per-token baseline); the bytes of y and proj are identical
  * ("Batched Prefill", §Correctness).  stats, when not NULL, is filled in and the
  * call then synchronises the stream (see pf_stack_stats). */
 PF_API pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int64_t chunk,
-                           float* y, float* proj, void* workspace, size_t ws_bytes,
+                           float* y, float* proj, float* kv, void* workspace, size_t ws_bytes,
                            pf_stack_stats* stats, void* stream);
 
 /* Mixture-of-experts layer ("Red Lite dev24", What changed):

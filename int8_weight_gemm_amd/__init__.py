@@ -43,7 +43,7 @@ class _Layer(ctypes.Structure):
 class _Stack(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int64), ("hidden", ctypes.c_int64), ("ffn", ctypes.c_int64),
                 ("layers", ctypes.POINTER(_Layer)), ("layers_alt", ctypes.POINTER(_Layer)),
-                ("activation", ctypes.c_int64)]
+                ("activation", ctypes.c_int64), ("n_heads", ctypes.c_int64)]
 
 
 class StackStats(ctypes.Structure):
@@ -54,7 +54,9 @@ class StackStats(ctypes.Structure):
                 ("quant_launches", ctypes.c_int64), ("product_alg_bytes", ctypes.c_double),
                 ("quant_alg_bytes", ctypes.c_double), ("product_ms", ctypes.c_double),
                 ("quant_ms", ctypes.c_double), ("product_busy_ms", ctypes.c_double),
-                ("quant_busy_ms", ctypes.c_double), ("overhead_bytes", ctypes.c_double)]
+                ("quant_busy_ms", ctypes.c_double), ("overhead_bytes", ctypes.c_double),
+                ("attn_launches", ctypes.c_int64), ("attn_alg_bytes", ctypes.c_double),
+                ("attn_ms", ctypes.c_double)]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -80,7 +82,7 @@ _SIGS = {
     "pf_gemm_i8_chunk_noalloc": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _P], ctypes.c_int),
     "pf_gemv_i8": ([_P, _P, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "pf_prefill_stack_workspace": ([ctypes.POINTER(_Stack), _I64], _SZ),
-    "pf_prefill_stack": ([ctypes.POINTER(_Stack), _P, _I64, _I64, _P, _P, _P, _SZ,
+    "pf_prefill_stack": ([ctypes.POINTER(_Stack), _P, _I64, _I64, _P, _P, _P, _P, _SZ,
                           ctypes.POINTER(StackStats), _P], ctypes.c_int),
     "pf_moe_chunk_workspace": ([ctypes.POINTER(_Moe), _I64], _SZ),
     "pf_moe_chunk": ([ctypes.POINTER(_Moe), _P, _I64, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
@@ -207,9 +209,10 @@ class Stack:
     """A projection stack resident in HBM: weights[l] = 7 int8 tensors (q, k, v, o,
     gate, up, down), scales[l] = 7 f32 tensors.  ``alt``, optional, is a second
     (weights, scales) copy of the same values that odd chunks read (pf_stack's
-    layers_alt); activation: ACT_NONE or ACT_SWIGLU (pf_stack's activation)."""
+    layers_alt); activation: ACT_NONE or ACT_SWIGLU (pf_stack's activation);
+    n_heads > 0: causal attention over a K/V cache (pf_stack's n_heads)."""
 
-    def __init__(self, weights, scales, alt=None, activation: int = ACT_NONE):
+    def __init__(self, weights, scales, alt=None, activation: int = ACT_NONE, n_heads: int = 0):
         self.L = len(weights)
         self.H = weights[0][0].shape[1]
         self.F = weights[0][4].shape[0]
@@ -218,7 +221,8 @@ class Stack:
         self._alt = self._table(*alt) if alt is not None else None
         self._desc = _Stack(self.L, self.H, self.F, ctypes.cast(self._layers, ctypes.POINTER(_Layer)),
                             ctypes.cast(self._alt, ctypes.POINTER(_Layer)) if self._alt is not None
-                            else None, int(activation))
+                            else None, int(activation), int(n_heads))
+        self.n_heads = int(n_heads)
 
     def _table(self, weights, scales):
         tab = (_Layer * self.L)()
@@ -238,9 +242,11 @@ class Stack:
         return int(lib().pf_prefill_stack_workspace(ctypes.byref(self._desc), chunk))
 
     def prefill(self, x: torch.Tensor, chunk: int, ws: torch.Tensor, y: torch.Tensor | None = None,
-                proj: torch.Tensor | None = None, stats: bool = False, time_kernels: bool = False):
-        """x f32 [P, H] -> y f32 [P, H]; proj (optional) f32 [L, P, 5H + 2F].
-        With stats (or time_kernels) also returns the call's statistics."""
+                proj: torch.Tensor | None = None, stats: bool = False, time_kernels: bool = False,
+                kv: torch.Tensor | None = None):
+        """x f32 [P, H] -> y f32 [P, H]; proj (optional) f32 [L, P, 5H + 2F]; kv,
+        the K/V cache f32 [L, 2, P, H], required with n_heads > 0.  With stats
+        (or time_kernels) also returns the call's statistics."""
         stats = stats or time_kernels
         _dev(x, torch.float32, "x")
         P = x.shape[0]
@@ -250,7 +256,7 @@ class Stack:
         if st is not None:
             st.time_kernels = 1 if time_kernels else 0
         _check("pf_prefill_stack", lib().pf_prefill_stack(
-            ctypes.byref(self._desc), _ptr(x), P, chunk, _ptr(y), _ptr(proj), _ptr(ws), ws.numel(),
+            ctypes.byref(self._desc), _ptr(x), P, chunk, _ptr(y), _ptr(proj), _ptr(kv), _ptr(ws), ws.numel(),
             ctypes.byref(st) if st is not None else None, _stream()))
         return (y, st.as_dict()) if stats else y
 

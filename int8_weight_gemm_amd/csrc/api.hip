@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <mutex>
 #include <cstdlib>
@@ -309,7 +310,7 @@ struct StackLayout {
     int slots;
     int dsplits;          // K splits of the down product
     int dkb;              // k-blocks per down-product split
-    size_t a, b, sa, sb, proj, part, slot_bytes, total;
+    size_t a, b, sa, sb, proj, part, ao, sao, slot_bytes, total;
 };
 
 
@@ -325,7 +326,7 @@ constexpr int kGroupSlots = 16;
 constexpr int kGroupSlotsTiled = 4;  // chunks over 64 tokens: each product fills the chip
 static_assert(kStackGroups <= kMaxGroups && kGroupSlots <= kMaxPairs, "stack sweep shape");
 
-StackLayout stack_layout(int64_t L, int64_t H, int64_t F, int64_t chunk)
+StackLayout stack_layout(int64_t L, int64_t H, int64_t F, int64_t chunk, bool attn)
 {
     StackLayout S{};
     S.groups = kStackGroups;
@@ -346,6 +347,9 @@ StackLayout stack_layout(int64_t L, int64_t H, int64_t F, int64_t chunk)
     S.sb = o; o += round_up((size_t)chunk * 4, kAlign);
     S.proj = o; o += round_up((size_t)chunk * (5 * H + 2 * F) * 4, kAlign);
     S.part = o; o += (chunk <= 64 || S.dsplits > 1) ? round_up((size_t)S.dsplits * chunk * H * 4, kAlign) : 0;
+    // attention: the quantised attention rows of the chunk and their scales
+    S.ao = o; o += attn ? round_up((size_t)chunk * H, kAlign) : 0;
+    S.sao = o; o += attn ? round_up((size_t)chunk * 4, kAlign) : 0;
     S.slot_bytes = o;
     S.total = o * S.slots;
     return S;
@@ -356,6 +360,12 @@ pf_status validate_stack(const pf_stack* st)
     if (!st || !st->layers || st->n_layers <= 0 || st->hidden <= 0 || st->ffn <= 0)
         return PF_EINVAL;
     if (st->activation != PF_ACT_NONE && st->activation != PF_ACT_SWIGLU) return PF_EINVAL;
+    if (st->n_heads < 0) return PF_EINVAL;
+    if (st->n_heads > 0) {
+        const int64_t d = st->hidden / st->n_heads;
+        if (st->hidden % st->n_heads != 0 || d % 4 != 0 || d > kAttnMaxD || st->hidden > kAttnMaxH)
+            return PF_EINVAL;
+    }
     if (!valid_k(st->hidden) || !valid_k(st->ffn)) return PF_EINVAL;
     for (const pf_layer* tab : {st->layers, st->layers_alt}) {
         if (!tab) continue;
@@ -445,6 +455,7 @@ struct DevStreams {
     hipStream_t s[kMaxGroups] = {};
     hipEvent_t fork = nullptr;
     hipEvent_t join[kMaxGroups] = {};
+    hipEvent_t kvdone[kMaxGroups][2] = {};   // a group's K/V cache rows of a step, by step parity
 };
 DevStreams g_streams[64];
 
@@ -464,6 +475,10 @@ pf_status ensure_streams(DevStreams* d)
     if (hipEventCreateWithFlags(&d->fork, hipEventDisableTiming) != hipSuccess) return PF_ELAUNCH;
     for (int i = 1; i < kStackGroups; ++i)
         if (hipEventCreateWithFlags(&d->join[i], hipEventDisableTiming) != hipSuccess) return PF_ELAUNCH;
+    for (int i = 0; i < kStackGroups; ++i)
+        for (int p = 0; p < 2; ++p)
+            if (hipEventCreateWithFlags(&d->kvdone[i][p], hipEventDisableTiming) != hipSuccess)
+                return PF_ELAUNCH;
     d->ready = true;
     return PF_OK;
 }
@@ -473,7 +488,7 @@ pf_status ensure_streams(DevStreams* d)
 // HIP events on the caller's stream to time it.
 class Recorder {
 public:
-    enum Kind { kQuant = 0, kProduct = 1 };
+    enum Kind { kQuant = 0, kProduct = 1, kAttn = 2, kKinds = 3 };
     Recorder(hipStream_t s, bool on, bool timed) : s_(s), on_(on), timed_(timed) {}
     ~Recorder()
     {
@@ -520,7 +535,7 @@ public:
         total_ms_ = ms;
         // per launch its own duration, and its interval on the call's clock
         // (launches of different chunk groups may overlap in time)
-        std::vector<std::pair<double, double>> iv[2];
+        std::vector<std::pair<double, double>> iv[kKinds];
         for (size_t i = 0; i < kinds_.size(); ++i) {
             float a = 0.0f, b = 0.0f;
             if (hipEventElapsedTime(&ms, events_[2 * i], events_[2 * i + 1]) != hipSuccess ||
@@ -531,7 +546,7 @@ public:
             iv[kinds_[i]].emplace_back(a, b);
         }
         // busy time of a kernel class: the union of its launches' intervals
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < kKinds; ++k) {
             std::sort(iv[k].begin(), iv[k].end());
             double busy = 0.0, lo = 0.0, hi = -1.0;
             for (const auto& p : iv[k]) {
@@ -550,8 +565,8 @@ public:
     }
     void fill(pf_stack_stats* st) const
     {
-        st->launches = launches_[0] + launches_[1];
-        st->alg_bytes = bytes_[0] + bytes_[1];
+        st->launches = launches_[0] + launches_[1] + launches_[2];
+        st->alg_bytes = bytes_[0] + bytes_[1] + bytes_[2];
         st->elapsed_ms = total_ms_;
         st->quant_launches = launches_[kQuant];
         st->product_launches = launches_[kProduct];
@@ -562,6 +577,9 @@ public:
         st->quant_busy_ms = timed_ ? busy_[kQuant] : 0.0;
         st->product_busy_ms = timed_ ? busy_[kProduct] : 0.0;
         st->overhead_bytes = overhead_;
+        st->attn_launches = launches_[kAttn];
+        st->attn_alg_bytes = bytes_[kAttn];
+        st->attn_ms = timed_ ? ms_[kAttn] : 0.0;
     }
 
 private:
@@ -575,10 +593,10 @@ private:
     hipEvent_t t0_ = nullptr, t1_ = nullptr;
     std::vector<hipEvent_t> events_;
     std::vector<int> kinds_;
-    int64_t launches_[2] = {0, 0};
-    double bytes_[2] = {0.0, 0.0};
-    double ms_[2] = {0.0, 0.0};
-    double busy_[2] = {0.0, 0.0};
+    int64_t launches_[kKinds] = {0, 0, 0};
+    double bytes_[kKinds] = {0.0, 0.0, 0.0};
+    double ms_[kKinds] = {0.0, 0.0, 0.0};
+    double busy_[kKinds] = {0.0, 0.0, 0.0};
     double overhead_ = 0.0;
     double total_ms_ = 0.0;
 };
@@ -599,10 +617,20 @@ struct StackRun {
     int64_t P, ch;
     float* y;
     float* proj;
+    float* kv;             // K/V cache [L][2][P][H] (attention), or null
     char* ws;
     StackLayout lay;
     hipStream_t s;
     int ng = 1;            // chunk groups, each on its own stream (chunk c in group c % ng)
+    DevStreams* ds = nullptr;
+    hipStream_t gs[kMaxGroups] = {};
+
+    bool attn() const { return st->n_heads > 0; }
+    // the cache rows of (layer l, position p0): K at half 0, V at half 1
+    float* kv_rows(int64_t l, int half, int64_t p0) const
+    {
+        return kv + (((size_t)l * 2 + half) * P + p0) * H();
+    }
 
     // the layer table chunk c reads (the second copy for odd chunks, if any)
     const pf_layer& layer(int64_t c, int64_t l) const
@@ -648,8 +676,9 @@ struct StackRun {
 
     // Chunks run in `ng` independent groups, one stream each, so that one
     // group's launches fill the start-up and tail of the other's.
-    pf_status sweep(Recorder& rec, DevStreams* ds)
+    pf_status sweep(Recorder& rec)
     {
+        gs[0] = s;
         if (ng == 1) {
             int64_t fin = -1;
             for (int64_t step = 0; step <= group_steps(0); ++step)
@@ -657,7 +686,6 @@ struct StackRun {
             return PF_OK;
         }
         // group 0 runs on the caller's stream, the others on library streams
-        hipStream_t gs[kMaxGroups] = {s};
         for (int g = 1; g < ng; ++g) gs[g] = ds->s[g];
         if (hipEventRecord(ds->fork, s) != hipSuccess) return PF_ELAUNCH;
         for (int g = 1; g < ng; ++g)
@@ -666,9 +694,14 @@ struct StackRun {
         int64_t nst = 0;
         for (int g = 0; g < ng; ++g) nst = std::max(nst, group_steps(g));
         for (int64_t step = 0; step <= nst; ++step)
-            for (int g = 0; g < ng; ++g)
-                if (step <= group_steps(g))
+            for (int g = 0; g < ng; ++g) {
+                if (step <= group_steps(g)) {
                     if (pf_status r = group_step(rec, g, step, fin[g], gs[g])) return r;
+                } else if (attn()) {
+                    // a finished group keeps its step marks current (they cover all its work)
+                    if (hipEventRecord(ds->kvdone[g][step & 1], gs[g]) != hipSuccess) return PF_ELAUNCH;
+                }
+            }
         for (int g = 1; g < ng; ++g) {
             if (hipEventRecord(ds->join[g], gs[g]) != hipSuccess) return PF_ELAUNCH;
             if (hipStreamWaitEvent(s, ds->join[g], 0) != hipSuccess) return PF_ELAUNCH;
@@ -682,23 +715,113 @@ struct StackRun {
     // quantise up, the down product.  `fin` carries the chunk whose last down
     // product ran in the previous step; its rows are rebuilt without
     // quantisation into the output.  step == group_steps(g) only finalises.
+    // chunks of group g active at `step` (each at layer step - start)
+    std::vector<int64_t> active(int g, int64_t step) const
+    {
+        std::vector<int64_t> cs;
+        const int64_t K = group_chunks(g);
+        if (step >= 0 && step < group_steps(g))
+            for (int64_t k = 0; k < K && start(k) <= step; ++k)
+                if (start(k) + L() > step) cs.push_back(g + k * ng);
+        return cs;
+    }
+
+    // The attention of the (chunk, layer) pairs group g ran at `step`: each
+    // token over the cache positions up to its own, quantised, then the o
+    // product.  Every earlier chunk's rows of the same layer are in the cache
+    // once every group has finished its step-`step` products (a chunk never
+    // reaches a layer before an earlier chunk of any group), which the
+    // per-group step marks establish.
+    pf_status attention_of(Recorder& rec, int g, int64_t step, hipStream_t sg)
+    {
+        const std::vector<int64_t> cs = active(g, step);
+        if (cs.empty()) return PF_OK;
+        if (ng > 1)
+            for (int o = 0; o < ng; ++o)
+                if (o != g && hipStreamWaitEvent(sg, ds->kvdone[o][step & 1], 0) != hipSuccess)
+                    return PF_ELAUNCH;
+        const bool skinny = ch <= 64;
+        AttnStep A;
+        std::memset(&A, 0, sizeof(A));
+        A.H = (int)H();
+        A.n_heads = (int)st->n_heads;
+        A.d = (int)(H() / st->n_heads);
+        A.scale = 1.0f / sqrtf((float)A.d);
+        A.ldq = NT();
+        A.ldkv = H();
+        StackStep O;
+        std::memset(&O, 0, sizeof(O));
+        O.nproj = 1;
+        O.K = (int)H();
+        O.rows[0] = (int)H();
+        O.yoff[0] = (int)offs(3);
+        const int tm = (int)((ch + tiled_tokens(ch) - 1) / tiled_tokens(ch));
+        O.tiles_m = tm;
+        O.tile_off[1] = (int)(skinny ? (H() + kSkinnyRows - 1) / kSkinnyRows
+                                     : ((H() + kTiledRows - 1) / kTiledRows) * tm);
+        O.splits = 1;
+        O.kb_per_split = (int)(H() / 64);
+        O.ldx = H();
+        O.ldy = NT();
+        O.kv_proj[0] = O.kv_proj[1] = -1;
+        double a_bytes = 0, o_bytes = 0;
+        for (int64_t c : cs) {
+            const int64_t l = step - start(c / ng), c0 = c * ch, M = std::min(ch, P - c0);
+            char* sl = slot(c);
+            AttnPair& ap = A.pair[A.npairs++];
+            ap.q = rows(c, l) + offs(0);
+            ap.K = kv_rows(l, 0, 0);
+            ap.V = kv_rows(l, 1, 0);
+            ap.ao = reinterpret_cast<int8_t*>(sl + lay.ao);
+            ap.sao = reinterpret_cast<float*>(sl + lay.sao);
+            ap.pos0 = (int)c0;
+            ap.M = (int)M;
+            A.max_m = std::max(A.max_m, (int)M);
+            // q read, the K/V history once, codes and scales written
+            a_bytes += (double)M * H() * 4 + 2.0 * (c0 + M) * H() * 4 + (double)M * H() + 4.0 * M;
+            StepPair& po = O.pair[O.npairs++];
+            const pf_layer& ly = layer(c, l);
+            po.W[0] = ly.W[3];
+            po.ws[0] = ly.w_scale[3];
+            po.X = ap.ao;
+            po.xs = ap.sao;
+            po.Y = rows(c, l);
+            po.M = (int)M;
+            o_bytes += product_bytes(H(), H(), M);
+        }
+        pf_status r = rec.run(Recorder::kAttn, a_bytes, [&] { return launched(launch_attention(A, sg)); });
+        if (r) return r;
+        const int tb = (int)((ch + 15) / 16);
+        return rec.run(Recorder::kProduct, o_bytes, [&] {
+            if (!skinny) return launched(launch_gemm_tiled_step(O, ch, sg));
+            return launched(H() / 64 <= 16 ? launch_gemm_xres(O, tb, sg) : launch_gemm_stream(O, tb, sg));
+        });
+    }
+
     pf_status group_step(Recorder& rec, int g, int64_t step, int64_t& fin, hipStream_t sg)
     {
-        const int64_t L = this->L(), K = group_chunks(g);
+        const int64_t L = this->L();
         const bool skinny = ch <= 64;
+        // the attention of the previous step's pairs (their q rows are intact:
+        // this step's products have not run yet on this stream)
+        if (attn())
+            if (pf_status r = attention_of(rec, g, step - 1, sg)) return r;
         // token-resident kernel for the six K = H products when a split of H fits
         const bool xres_a = skinny && H() / 64 <= 16;
         const int sd = lay.dsplits;
         // the down product leaves int32 split partials that the next
         // quantisation launch sums (always on the skinny path)
         const bool rebuild_d = skinny || sd > 1;
-        const int64_t rowsA[6] = {H(), H(), H(), H(), F(), F()};
+        // the K = H products of the step: q, k, v, o, gate, up; with attention o
+        // waits for it and the launch has five
+        const int projA6[6] = {0, 1, 2, 3, 4, 5}, projA5[6] = {0, 1, 2, 4, 5, 5};
+        const int* projA = attn() ? projA5 : projA6;
+        const int nA = attn() ? 5 : 6;
+        int64_t rowsA[6];
+        for (int j = 0; j < 6; ++j) rowsA[j] = projA[j] >= 4 ? F() : H();
         const int tm = (int)((ch + tiled_tokens(ch) - 1) / tiled_tokens(ch));
         const int tb = (int)((ch + 15) / 16);
-        std::vector<int64_t> cs;              // global chunk indices active in this step
-        if (step < group_steps(g))
-            for (int64_t k = 0; k < K && start(k) <= step; ++k)
-                if (start(k) + L > step) cs.push_back(g + k * ng);
+        const std::vector<int64_t> cs = active(g, step);   // global chunk indices active in this step
         QuantStep qa, qd;
         StackStep A, D;
         std::memset(&qa, 0, sizeof(qa));
@@ -707,7 +830,7 @@ struct StackRun {
         std::memset(&D, 0, sizeof(D));
         qa.K = (int)H();
         qd.K = (int)F();
-        A.nproj = 6;
+        A.nproj = nA;
         A.K = (int)H();
         A.splits = 1;
         A.kb_per_split = (int)(H() / 64);
@@ -723,9 +846,14 @@ struct StackRun {
         D.ldy2 = H();
         D.ldp = H();
         D.part_stride = ch * H();
-        for (int j = 0; j < 6; ++j) {
+        // with attention, k and v (slots 1 and 2 of the launch) also go to the cache
+        A.kv_proj[0] = attn() ? 1 : -1;
+        A.kv_proj[1] = attn() ? 2 : -1;
+        A.ldkv = H();
+        D.kv_proj[0] = D.kv_proj[1] = -1;
+        for (int j = 0; j < nA; ++j) {
             A.rows[j] = (int)rowsA[j];
-            A.yoff[j] = (int)offs(j);
+            A.yoff[j] = (int)offs(projA[j]);
             const int64_t t = skinny ? (rowsA[j] + kSkinnyRows - 1) / kSkinnyRows
                                      : ((rowsA[j] + kTiledRows - 1) / kTiledRows) * tm;
             A.tile_off[j + 1] = A.tile_off[j] + (int)t;
@@ -781,12 +909,16 @@ struct StackRun {
             q1.row0 = rows_d;
             rows_d += (int)M;
             StepPair& pa = A.pair[A.npairs++];
-            // the six products share one read of the quantised tokens
+            // the products share one read of the quantised tokens
             a_bytes += (double)M * H() + 4.0 * M;
-            for (int j = 0; j < 6; ++j) {
-                pa.W[j] = ly.W[j];
-                pa.ws[j] = ly.w_scale[j];
+            for (int j = 0; j < nA; ++j) {
+                pa.W[j] = ly.W[projA[j]];
+                pa.ws[j] = ly.w_scale[projA[j]];
                 a_bytes += weight_out_bytes(rowsA[j], H(), M);
+            }
+            if (attn()) {
+                pa.kv[0] = kv_rows(l, 0, c0);
+                pa.kv[1] = kv_rows(l, 1, c0);
             }
             pa.X = a;
             pa.xs = sa;
@@ -827,12 +959,17 @@ struct StackRun {
         if (r) return r;
         if (cs.empty()) {
             rec.overhead(part_bytes);
+            if (attn() && ng > 1 && hipEventRecord(ds->kvdone[g][step & 1], sg) != hipSuccess)
+                return PF_ELAUNCH;
             return PF_OK;
         }
         r = rec.run(Recorder::kProduct, a_bytes, [&] {
             if (!skinny) return launched(launch_gemm_tiled_step(A, ch, sg));
             return launched(xres_a ? launch_gemm_xres(A, tb, sg) : launch_gemm_stream(A, tb, sg));
         }, sg);
+        // this step's cache rows are written once the products above are done
+        if (!r && attn() && ng > 1 && hipEventRecord(ds->kvdone[g][step & 1], sg) != hipSuccess)
+            return PF_ELAUNCH;
         if (!r) r = rec.run(Recorder::kQuant, qd_bytes,
                             [&] { return launched(launch_quantize_step(qd, sg)); }, sg);
         if (!r) r = rec.run(Recorder::kProduct, d_bytes, [&] {
@@ -869,16 +1006,51 @@ struct StackRun {
                 if (r) return r;
                 GemmSet set;
                 std::memset(&set, 0, sizeof(set));
-                set.nprob = 6;
                 double bytes = (double)H() + 4.0;        // the token, read once
                 for (int j = 0; j < 6; ++j) {
-                    make_skinny(set.p[j], ly.W[j], ly.w_scale[j], rowsA[j], H(), a, H(), sa, 1,
+                    if (attn() && j == 3) continue;      // o waits for the attention
+                    GemmProb& gp = set.p[set.nprob++];
+                    make_skinny(gp, ly.W[j], ly.w_scale[j], rowsA[j], H(), a, H(), sa, 1,
                                 out + offs(j), NT(), unsplit(rowsA[j], H()), none, 1);
+                    if (attn() && (j == 1 || j == 2)) gp.Y2 = kv_rows(l, j - 1, t);   // the cache
                     bytes += weight_out_bytes(rowsA[j], H(), 1);
                 }
                 finish_set(set, 0);
                 r = rec.run(Recorder::kProduct, bytes, [&] { return launched(launch_gemv(set, s)); });
                 if (r) return r;
+                if (attn()) {
+                    // token t over cache positions 0 .. t of layer l, then o
+                    AttnStep A;
+                    std::memset(&A, 0, sizeof(A));
+                    A.H = (int)H();
+                    A.n_heads = (int)st->n_heads;
+                    A.d = (int)(H() / st->n_heads);
+                    A.scale = 1.0f / sqrtf((float)A.d);
+                    A.ldq = NT();
+                    A.ldkv = H();
+                    A.npairs = 1;
+                    A.max_m = 1;
+                    AttnPair& ap = A.pair[0];
+                    ap.q = out + offs(0);
+                    ap.K = kv_rows(l, 0, 0);
+                    ap.V = kv_rows(l, 1, 0);
+                    ap.ao = reinterpret_cast<int8_t*>(sl + lay.ao);
+                    ap.sao = reinterpret_cast<float*>(sl + lay.sao);
+                    ap.pos0 = (int)t;
+                    ap.M = 1;
+                    r = rec.run(Recorder::kAttn, (double)H() * 4 * (1 + 2 * (t + 1)) + H() + 4.0,
+                                [&] { return launched(launch_attention(A, s)); });
+                    if (r) return r;
+                    GemmSet os;
+                    std::memset(&os, 0, sizeof(os));
+                    os.nprob = 1;
+                    make_skinny(os.p[0], ly.W[3], ly.w_scale[3], H(), H(), ap.ao, H(), ap.sao, 1,
+                                out + offs(3), NT(), unsplit(H(), H()), none, 1);
+                    finish_set(os, 0);
+                    r = rec.run(Recorder::kProduct, product_bytes(H(), H(), 1),
+                                [&] { return launched(launch_gemv(os, s)); });
+                    if (r) return r;
+                }
                 const bool gated = st->activation == PF_ACT_SWIGLU;
                 r = rec.run(Recorder::kQuant, (double)F() * (gated ? 9 : 5) + 4, [&] {
                     if (gated)
@@ -1156,12 +1328,13 @@ size_t pf_prefill_stack_workspace(const pf_stack* stack, int64_t chunk)
     // split partials; above: fewer slots), so the largest of the two regime
     // tops covers every prompt length.
     const int64_t L = stack->n_layers, H = stack->hidden, F = stack->ffn;
-    return std::max(stack_layout(L, H, F, chunk).total,
-                    stack_layout(L, H, F, std::min<int64_t>(chunk, 64)).total);
+    const bool attn = stack->n_heads > 0;
+    return std::max(stack_layout(L, H, F, chunk, attn).total,
+                    stack_layout(L, H, F, std::min<int64_t>(chunk, 64), attn).total);
 }
 
 pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int64_t chunk,
-                           float* y, float* proj, void* workspace, size_t ws_bytes,
+                           float* y, float* proj, float* kv, void* workspace, size_t ws_bytes,
                            pf_stack_stats* stats, void* stream)
 {
     try {
@@ -1182,15 +1355,20 @@ pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int
         const size_t xb = (size_t)P * H * 4, pb = proj ? (size_t)L * P * NT * 4 : 0;
         if (overlap(x, xb, y, xb) || overlap(proj, pb, x, xb) || overlap(proj, pb, y, xb))
             return PF_EINVAL;
+        const bool attn = stack->n_heads > 0;
+        const size_t kb = attn ? (size_t)L * 2 * P * H * 4 : 0;
+        if (attn && (!kv || !aligned16(kv) || overlap(kv, kb, x, xb) || overlap(kv, kb, y, xb) ||
+                     overlap(kv, kb, proj, pb)))
+            return PF_EINVAL;
         const int64_t ch = std::min(chunk, P);
-        const StackLayout lay = stack_layout(L, H, F, ch);
+        const StackLayout lay = stack_layout(L, H, F, ch, attn);
         if (!workspace || ws_bytes < lay.total) return PF_EWORKSPACE;
         if (!aligned16(workspace)) return PF_EINVAL;
         if (overlap(workspace, ws_bytes, x, xb) || overlap(workspace, ws_bytes, y, xb) ||
-            overlap(workspace, ws_bytes, proj, pb))
+            overlap(workspace, ws_bytes, proj, pb) || overlap(workspace, ws_bytes, kv, kb))
             return PF_EINVAL;
         if (pf_status st = check_device()) return st;
-        StackRun run{stack, x, P, ch, y, proj, static_cast<char*>(workspace), lay,
+        StackRun run{stack, x, P, ch, y, proj, attn ? kv : nullptr, static_cast<char*>(workspace), lay,
                      (hipStream_t)stream};
         Recorder rec(run.s, stats != nullptr, timed);
         const bool per_token = per_token_mode();
@@ -1202,8 +1380,9 @@ pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int
             lock = std::unique_lock<std::mutex>(ds->mu);
             if (ensure_streams(ds) == PF_OK) run.ng = (int)std::min<int64_t>(lay.groups, C);
         }
+        run.ds = ds;
         pf_status st = rec.begin();
-        if (st == PF_OK) st = per_token ? run.per_token(rec) : run.sweep(rec, ds);
+        if (st == PF_OK) st = per_token ? run.per_token(rec) : run.sweep(rec);
         if (st == PF_OK) st = rec.end();
         if (st == PF_OK && stats) {
             std::memset(stats, 0, sizeof(*stats));

@@ -71,6 +71,8 @@ struct StepPair {
     float* Y;             // output rows [M][ldy]; projection j at column yoff[j]
     float* Y2;            // optional second copy [M][ldy2] (single-projection steps) or null
     int* part;            // split-K int32 partials [splits][part_stride] (rows of ldp) or null
+    float* kv[2];         // attention: the pair's K and V cache rows [M][ldkv] (projections
+                          // kv_proj[0] and kv_proj[1] also store there) or null
     int M;
 };
 struct StackStep {
@@ -88,7 +90,38 @@ struct StackStep {
     int64_t ldx, ldy, ldy2;
     int64_t ldp;          // int32 elements between token rows of the partials
     int64_t part_stride;  // int32 elements between splits of the partials
+    int kv_proj[2];       // projections whose outputs also go to the K / V cache (-1: none)
+    int64_t ldkv;         // floats between cache rows
 };
+
+// The K or V cache row base of projection j of a pair (null: none).
+__host__ __device__ inline float* step_kv(const StackStep& S, const StepPair& p, int j)
+{
+    return j == S.kv_proj[0] ? p.kv[0] : (j == S.kv_proj[1] ? p.kv[1] : nullptr);
+}
+
+// Causal attention of the tokens of up to kMaxPairs (chunk, layer) pairs, each
+// token over cache positions 0 .. its own, followed by the per-token
+// quantisation of the attention row.
+struct AttnPair {
+    const float* q;       // q rows of the pair's tokens [M][ldq]
+    const float* K;       // the layer's K cache, position 0 [P][ldkv]
+    const float* V;       // the layer's V cache, position 0
+    int8_t* ao;           // quantised attention rows [M][H]
+    float* sao;           // their scales [M]
+    int pos0;             // position of the pair's first token
+    int M;
+};
+struct AttnStep {
+    AttnPair pair[kMaxPairs];
+    int npairs;
+    int max_m;            // tokens of the largest pair (workgroups per pair)
+    int H, n_heads, d;
+    float scale;          // fl(1 / fl(sqrt(d)))
+    int64_t ldq, ldkv;
+};
+constexpr int kAttnMaxH = 8192;          // attention row held in LDS
+constexpr int kAttnMaxD = 256;           // head width: four values per lane
 
 // Per-token quantisation of several chunks' rows in one launch.  Mode 0: the
 // rows are f32 [M][ld] at src.  Mode 1 (part != null): the rows are rebuilt
@@ -171,6 +204,7 @@ hipError_t launch_expert(const ExpertArgs& a, hipStream_t s);
 hipError_t launch_combine(const float* ypair, const int* comb_row, const float* comb_w, int T,
                           int k, int H, float* out, hipStream_t s);
 hipError_t launch_expf(const float* x, int64_t n, float* y, hipStream_t s);
+hipError_t launch_attention(const AttnStep& S, hipStream_t s);
 
 // Sizes of the grouping kernel's shared bitmap.
 inline size_t group_lds_bytes(int T, int E) { return (size_t)E * ((T + 31) / 32) * 4; }

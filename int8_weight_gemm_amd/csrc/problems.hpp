@@ -36,12 +36,16 @@ __device__ __forceinline__ GemmProb step_prob(const StackStep& S, int bid, int& 
     P.xs = pp.xs;
     P.Y = pp.Y + S.yoff[j];
     P.Y2 = pp.Y2;
+    P.ldy2 = S.ldy2;
+    if (float* kv = step_kv(S, pp, j)) {
+        P.Y2 = kv;
+        P.ldy2 = S.ldkv;
+    }
     P.acc = nullptr;
     P.acc_ld = 0;
     P.acc_split = 0;
     P.ldx = S.ldx;
     P.ldy = S.ldy;
-    P.ldy2 = S.ldy2;
     P.N = S.rows[j];
     P.K = S.K;
     P.M = pp.M;

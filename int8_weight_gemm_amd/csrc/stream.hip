@@ -573,8 +573,9 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int wg_per_group
                             if (n + 1 < N) y[1] = v.y;
                             if (n + 2 < N) y[2] = v.z;
                         }
-                        if (pp.Y2) {
-                            float* y2 = pp.Y2 + (int64_t)tok * S.ldy2 + n;
+                        float* kvr = step_kv(S, pp, cur.proj);
+                        if (pp.Y2 || kvr) {
+                            float* y2 = kvr ? kvr + (int64_t)tok * S.ldkv + n : pp.Y2 + (int64_t)tok * S.ldy2 + n;
                             if (n < N) y2[0] = v.x;
                             if (n + 1 < N) y2[1] = v.y;
                             if (n + 2 < N) y2[2] = v.z;

@@ -118,16 +118,16 @@ def test_stack_validation():
     layers = (pf._Layer * 1)()
     st = pf._Stack(1, 128, 256, ctypes.cast(layers, ctypes.POINTER(pf._Layer)))
     # null weights in the layer table
-    assert lib.pf_prefill_stack(ctypes.byref(st), FAKE, 4, 32, P(0x20000), None, P(0x40000), 1 << 20,
+    assert lib.pf_prefill_stack(ctypes.byref(st), FAKE, 4, 32, P(0x20000), None, None, P(0x40000), 1 << 20,
                                 None, None) == pf.PF_EINVAL
     for j in range(7):
         layers[0].W[j] = 0x100000 + j * 0x10000
         layers[0].w_scale[j] = 0x200000 + j * 0x10000
     # workspace too small
-    assert lib.pf_prefill_stack(ctypes.byref(st), P(0x300000), 4, 32, P(0x310000), None, P(0x400000), 16,
+    assert lib.pf_prefill_stack(ctypes.byref(st), P(0x300000), 4, 32, P(0x310000), None, None, P(0x400000), 16,
                                 None, None) == pf.PF_EWORKSPACE
     # chunk must be positive
-    assert lib.pf_prefill_stack(ctypes.byref(st), P(0x300000), 4, 0, P(0x310000), None, P(0x400000), 1 << 20,
+    assert lib.pf_prefill_stack(ctypes.byref(st), P(0x300000), 4, 0, P(0x310000), None, None, P(0x400000), 1 << 20,
                                 None, None) == pf.PF_EINVAL
 
 
@@ -151,9 +151,9 @@ def test_stack_workspace_query_covers_short_prompts(L, H, F, chunk, P):
     need = lib.pf_prefill_stack_workspace(ctypes.byref(st), chunk)
     assert need > 0
     x, y, ws = P_(0x100000000), P_(0x200000000), P_(0x300000000)
-    assert lib.pf_prefill_stack(ctypes.byref(st), x, P, chunk, y, None, ws, need, None, None) == pf.PF_ENODEV
+    assert lib.pf_prefill_stack(ctypes.byref(st), x, P, chunk, y, None, None, ws, need, None, None) == pf.PF_ENODEV
     for p in range(1, chunk + 1):
-        assert lib.pf_prefill_stack(ctypes.byref(st), x, p, chunk, y, None, ws, need, None, None) == pf.PF_ENODEV
+        assert lib.pf_prefill_stack(ctypes.byref(st), x, p, chunk, y, None, None, ws, need, None, None) == pf.PF_ENODEV
 
 
 P_ = ctypes.c_void_p
