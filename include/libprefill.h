@@ -239,6 +239,43 @@ PF_API pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t
                            float* y, float* proj, float* kv, void* workspace, size_t ws_bytes,
                            pf_stack_stats* stats, void* stream);
 
+/* Statistics of one pf_prefill_stack_streamed call (filled when not NULL; the
+ * call then synchronises the stream). */
+typedef struct {
+    int64_t n_buffers;         /* device ring slots                                */
+    int64_t layers_copied;     /* host-to-device layer copies (one per layer)      */
+    int64_t prefetch_hits;     /* copies complete before the previous layer's
+                                  compute ended: the compute never waited          */
+    int64_t prefetch_misses;   /* the others (the first layer's copy always)       */
+    double bytes_copied;       /* weights and scales moved over the host link      */
+    double elapsed_ms;         /* device time of the whole call                    */
+} pf_stream_stats;
+
+/* Workspace bytes for pf_prefill_stack_streamed: the device ring of n_buffers
+ * layer slots and the activations of a P-token prompt. */
+PF_API size_t pf_prefill_stack_streamed_workspace(const pf_stack* stack, int64_t P, int64_t n_buffers);
+
+/* The stack with its weights in host memory, for models larger than device
+ * memory ("Predictive prefetch", "The fix: an async double-buffer ring": while
+ * layer L computes, layer L + 1 is materialised in the other buffer; a copy
+ * that is ready when needed is a hit, one that is not is a miss and the
+ * compute waits; "Single-pass prefill", "The fix": stream each layer once and
+ * sweep every prompt position through it).  stack->layers hold HOST pointers
+ * (pinned memory from hipHostMalloc, so the copies are asynchronous; read
+ * during the call); layers_alt must be NULL and n_heads 0.  Layer l is copied
+ * into ring slot l % n_buffers on a library-owned copy stream, at most
+ * n_buffers - 1 layers ahead; the copy into a slot waits for the compute that
+ * last used it; the compute of layer l runs every chunk of `chunk` tokens
+ * through it and waits for its copy only before its first product.  The
+ * results are those of pf_prefill_stack (the arithmetic is the same, only the
+ * schedule differs; "Predictive prefetch", "Three backends, one truth"):
+ * x [P][H] -> y [P][H].  n_buffers >= 2.  Calls that share a workspace must be
+ * ordered. */
+PF_API pf_status pf_prefill_stack_streamed(const pf_stack* stack, const float* x, int64_t P,
+                                           int64_t chunk, float* y, int64_t n_buffers,
+                                           void* workspace, size_t ws_bytes,
+                                           pf_stream_stats* stats, void* stream);
+
 /* Mixture-of-experts layer ("Red Lite dev24", What changed):
  *   W_router [E][H] f32; W_gate, W_up [E][I][H] int8; W_down [E][H][I] int8;
  *   s_gate, s_up [E][I] f32; s_down [E][H] f32. */

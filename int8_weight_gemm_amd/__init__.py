@@ -62,6 +62,15 @@ class StackStats(ctypes.Structure):
         return {n: getattr(self, n) for n, _ in self._fields_}
 
 
+class StreamStats(ctypes.Structure):
+    _fields_ = [("n_buffers", ctypes.c_int64), ("layers_copied", ctypes.c_int64),
+                ("prefetch_hits", ctypes.c_int64), ("prefetch_misses", ctypes.c_int64),
+                ("bytes_copied", ctypes.c_double), ("elapsed_ms", ctypes.c_double)]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
 class _Moe(ctypes.Structure):
     _fields_ = [("n_experts", ctypes.c_int64), ("top_k", ctypes.c_int64), ("hidden", ctypes.c_int64),
                 ("inter", ctypes.c_int64), ("W_router", ctypes.c_void_p), ("W_gate", ctypes.c_void_p),
@@ -84,6 +93,9 @@ _SIGS = {
     "pf_prefill_stack_workspace": ([ctypes.POINTER(_Stack), _I64], _SZ),
     "pf_prefill_stack": ([ctypes.POINTER(_Stack), _P, _I64, _I64, _P, _P, _P, _P, _SZ,
                           ctypes.POINTER(StackStats), _P], ctypes.c_int),
+    "pf_prefill_stack_streamed_workspace": ([ctypes.POINTER(_Stack), _I64, _I64], _SZ),
+    "pf_prefill_stack_streamed": ([ctypes.POINTER(_Stack), _P, _I64, _I64, _P, _I64, _P, _SZ,
+                                   ctypes.POINTER(StreamStats), _P], ctypes.c_int),
     "pf_moe_chunk_workspace": ([ctypes.POINTER(_Moe), _I64], _SZ),
     "pf_moe_chunk": ([ctypes.POINTER(_Moe), _P, _I64, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "pf_expf_cr": ([_P, _I64, _P, _P], ctypes.c_int),
@@ -257,6 +269,45 @@ class Stack:
             st.time_kernels = 1 if time_kernels else 0
         _check("pf_prefill_stack", lib().pf_prefill_stack(
             ctypes.byref(self._desc), _ptr(x), P, chunk, _ptr(y), _ptr(proj), _ptr(kv), _ptr(ws), ws.numel(),
+            ctypes.byref(st) if st is not None else None, _stream()))
+        return (y, st.as_dict()) if stats else y
+
+
+class HostStack:
+    """A projection stack whose weights stay in host memory (CPU tensors, pinned
+    so that the copies run asynchronously), streamed layer by layer through a
+    device ring by pf_prefill_stack_streamed."""
+
+    def __init__(self, weights, scales, activation: int = ACT_NONE):
+        self.L = len(weights)
+        self.H = weights[0][0].shape[1]
+        self.F = weights[0][4].shape[0]
+        self.weights, self.scales = weights, scales
+        self._layers = (_Layer * self.L)()
+        for l in range(self.L):
+            for j in range(NPROJ):
+                for t, dt, n in ((weights[l][j], torch.int8, "W"), (scales[l][j], torch.float32, "w_scale")):
+                    if t.is_cuda or t.dtype != dt or not t.is_contiguous():
+                        raise TypeError(f"{n}[{l}][{j}] must be a contiguous host {dt} tensor")
+                self._layers[l].W[j] = weights[l][j].data_ptr()
+                self._layers[l].w_scale[j] = scales[l][j].data_ptr()
+        self._desc = _Stack(self.L, self.H, self.F, ctypes.cast(self._layers, ctypes.POINTER(_Layer)),
+                            None, int(activation), 0)
+
+    def workspace_bytes(self, P: int, n_buffers: int = 2) -> int:
+        return int(lib().pf_prefill_stack_streamed_workspace(ctypes.byref(self._desc), P, n_buffers))
+
+    def prefill(self, x: torch.Tensor, chunk: int, ws: torch.Tensor, n_buffers: int = 2,
+                y: torch.Tensor | None = None, stats: bool = False):
+        """x f32 [P, H] on the device -> y f32 [P, H]; with stats also the ring's
+        counters (the call then synchronises)."""
+        _dev(x, torch.float32, "x")
+        P = x.shape[0]
+        if y is None:
+            y = torch.empty((P, self.H), dtype=torch.float32, device=x.device)
+        st = StreamStats() if stats else None
+        _check("pf_prefill_stack_streamed", lib().pf_prefill_stack_streamed(
+            ctypes.byref(self._desc), _ptr(x), P, chunk, _ptr(y), n_buffers, _ptr(ws), ws.numel(),
             ctypes.byref(st) if st is not None else None, _stream()))
         return (y, st.as_dict()) if stats else y
 

@@ -456,6 +456,7 @@ struct DevStreams {
     hipEvent_t fork = nullptr;
     hipEvent_t join[kMaxGroups] = {};
     hipEvent_t kvdone[kMaxGroups][2] = {};   // a group's K/V cache rows of a step, by step parity
+    hipStream_t copy = nullptr;              // host-to-device weight copies (streamed stacks)
 };
 DevStreams g_streams[64];
 
@@ -1187,6 +1188,244 @@ void* scratch_ptr()
     return p;
 }
 
+
+// ---------------------------------------------------------------------------
+// The stack with its weights in host memory ("Predictive prefetch": the
+// weights of layer L + 1 are copied into the other buffer of a ring while
+// layer L computes; "Single-pass prefill": every prompt position goes through
+// a layer while its weights are loaded, so each layer crosses the host link
+// once per prompt).  Device ring of n_buffers layer slots, fed by a copy
+// stream; the compute stream waits for layer l's copy only before its first
+// product, and the copy of layer l into a slot waits for the compute that last
+// used the slot.
+
+// One layer's weights and scales in a ring slot.
+struct SlotLayout {
+    size_t w[PF_NPROJ], s[PF_NPROJ], bytes;
+};
+
+SlotLayout slot_layout(int64_t H, int64_t F)
+{
+    const int64_t rows[PF_NPROJ] = {H, H, H, H, F, F, H};
+    const int64_t cols[PF_NPROJ] = {H, H, H, H, H, H, F};
+    SlotLayout S{};
+    size_t o = 0;
+    for (int j = 0; j < PF_NPROJ; ++j) {
+        S.w[j] = o;
+        o += round_up((size_t)rows[j] * cols[j], kAlign);
+    }
+    for (int j = 0; j < PF_NPROJ; ++j) {
+        S.s[j] = o;
+        o += round_up((size_t)rows[j] * 4, kAlign);
+    }
+    S.bytes = o;
+    return S;
+}
+
+// Workspace of the streamed stack: the ring, then the prompt's activations for
+// the layer in flight: codes a [P][H] and b [P][F] with scales, and the
+// projection rows [P][5H + 2F] (the down column is the next layer's input).
+struct StreamLayout {
+    SlotLayout sl;
+    size_t ring, a, b, sa, sb, rows, total;
+};
+
+StreamLayout stream_layout(int64_t H, int64_t F, int64_t P, int64_t nbuf)
+{
+    StreamLayout S{};
+    S.sl = slot_layout(H, F);
+    size_t o = 0;
+    S.ring = o; o += S.sl.bytes * (size_t)nbuf;
+    S.a = o; o += round_up((size_t)P * H, kAlign);
+    S.b = o; o += round_up((size_t)P * F, kAlign);
+    S.sa = o; o += round_up((size_t)P * 4, kAlign);
+    S.sb = o; o += round_up((size_t)P * 4, kAlign);
+    S.rows = o; o += round_up((size_t)P * (5 * H + 2 * F) * 4, kAlign);
+    S.total = o;
+    return S;
+}
+
+struct StreamRun {
+    const pf_stack* st;
+    const float* x;
+    int64_t P, ch, nbuf;
+    float* y;
+    char* ws;
+    StreamLayout lay;
+    hipStream_t s, cs;
+    std::vector<hipEvent_t> copied, computed;   // per layer, timing events
+
+    ~StreamRun()
+    {
+        for (hipEvent_t e : copied) if (e) (void)hipEventDestroy(e);
+        for (hipEvent_t e : computed) if (e) (void)hipEventDestroy(e);
+    }
+    int64_t H() const { return st->hidden; }
+    int64_t F() const { return st->ffn; }
+    int64_t NT() const { return 5 * st->hidden + 2 * st->ffn; }
+    int64_t offs(int j) const
+    {
+        const int64_t o[PF_NPROJ] = {0, H(), 2 * H(), 3 * H(), 4 * H(), 4 * H() + F(), 4 * H() + 2 * F()};
+        return o[j];
+    }
+    char* slot(int64_t l) const { return ws + lay.ring + (size_t)(l % nbuf) * lay.sl.bytes; }
+    float* rows() const { return reinterpret_cast<float*>(ws + lay.rows); }
+
+    // layer l's weights host -> its ring slot, on the copy stream
+    pf_status copy_layer(int64_t l)
+    {
+        const int64_t H = this->H(), F = this->F();
+        const int64_t rws[PF_NPROJ] = {H, H, H, H, F, F, H};
+        const int64_t cls[PF_NPROJ] = {H, H, H, H, H, H, F};
+        if (l >= nbuf && hipStreamWaitEvent(cs, computed[l - nbuf], 0) != hipSuccess) return PF_ELAUNCH;
+        char* sl = slot(l);
+        const pf_layer& ly = st->layers[l];
+        for (int j = 0; j < PF_NPROJ; ++j) {
+            if (hipMemcpyAsync(sl + lay.sl.w[j], ly.W[j], (size_t)rws[j] * cls[j], hipMemcpyHostToDevice, cs) !=
+                    hipSuccess ||
+                hipMemcpyAsync(sl + lay.sl.s[j], ly.w_scale[j], (size_t)rws[j] * 4, hipMemcpyHostToDevice, cs) !=
+                    hipSuccess)
+                return launched(hipGetLastError());
+        }
+        return hipEventRecord(copied[l], cs) == hipSuccess ? PF_OK : PF_ELAUNCH;
+    }
+
+    // every chunk of the prompt through layer l (weights in its slot)
+    pf_status compute_layer(int64_t l)
+    {
+        const int64_t H = this->H(), F = this->F(), L = st->n_layers;
+        char* sl = slot(l);
+        int8_t* a = reinterpret_cast<int8_t*>(ws + lay.a);
+        int8_t* b = reinterpret_cast<int8_t*>(ws + lay.b);
+        float* sa = reinterpret_cast<float*>(ws + lay.sa);
+        float* sb = reinterpret_cast<float*>(ws + lay.sb);
+        float* R = rows();
+        // quantise the layer input of every token (x, or the previous down)
+        QuantStep q;
+        std::memset(&q, 0, sizeof(q));
+        q.npairs = 1;
+        q.K = (int)H;
+        q.total_rows = (int)P;
+        q.pair[0].src = l == 0 ? x : R + offs(6);
+        q.pair[0].ld = l == 0 ? H : NT();
+        q.pair[0].q = a;
+        q.pair[0].s = sa;
+        if (pf_status r = launched(launch_quantize_step(q, s))) return r;
+        if (hipStreamWaitEvent(s, copied[l], 0) != hipSuccess) return PF_ELAUNCH;
+        const bool skinny = ch <= 64;
+        const int tb = (int)((ch + 15) / 16);
+        const int tm = (int)((ch + tiled_tokens(ch) - 1) / tiled_tokens(ch));
+        const int64_t rowsA[6] = {H, H, H, H, F, F};
+        const int64_t C = (P + ch - 1) / ch;
+        auto wptr = [&](int j) { return reinterpret_cast<const int8_t*>(sl + lay.sl.w[j]); };
+        auto sptr = [&](int j) { return reinterpret_cast<const float*>(sl + lay.sl.s[j]); };
+        // the six K = H products, chunks as the pairs of a launch
+        for (int64_t c0 = 0; c0 < C; c0 += kMaxPairs) {
+            StackStep A;
+            std::memset(&A, 0, sizeof(A));
+            A.nproj = 6;
+            A.K = (int)H;
+            A.splits = 1;
+            A.kb_per_split = (int)(H / 64);
+            A.tiles_m = tm;
+            A.ldx = H;
+            A.ldy = NT();
+            A.kv_proj[0] = A.kv_proj[1] = -1;
+            for (int j = 0; j < 6; ++j) {
+                A.rows[j] = (int)rowsA[j];
+                A.yoff[j] = (int)offs(j);
+                const int64_t t = skinny ? (rowsA[j] + kSkinnyRows - 1) / kSkinnyRows
+                                         : ((rowsA[j] + kTiledRows - 1) / kTiledRows) * tm;
+                A.tile_off[j + 1] = A.tile_off[j] + (int)t;
+            }
+            for (int64_t c = c0; c < std::min(C, c0 + kMaxPairs); ++c) {
+                const int64_t t0 = c * ch, M = std::min(ch, P - t0);
+                StepPair& p = A.pair[A.npairs++];
+                for (int j = 0; j < 6; ++j) {
+                    p.W[j] = wptr(j);
+                    p.ws[j] = sptr(j);
+                }
+                p.X = a + t0 * H;
+                p.xs = sa + t0;
+                p.Y = R + t0 * NT();
+                p.M = (int)M;
+            }
+            pf_status r;
+            if (!skinny) r = launched(launch_gemm_tiled_step(A, ch, s));
+            else r = launched(H / 64 <= 16 ? launch_gemm_xres(A, tb, s) : launch_gemm_stream(A, tb, s));
+            if (r) return r;
+        }
+        // the down product's input: up, or silu(gate) * up
+        QuantStep qd;
+        std::memset(&qd, 0, sizeof(qd));
+        qd.npairs = 1;
+        qd.K = (int)F;
+        qd.total_rows = (int)P;
+        qd.pair[0].src = R + offs(5);
+        qd.pair[0].gate = st->activation == PF_ACT_SWIGLU ? R + offs(4) : nullptr;
+        qd.pair[0].ld = NT();
+        qd.pair[0].q = b;
+        qd.pair[0].s = sb;
+        if (pf_status r = launched(launch_quantize_step(qd, s))) return r;
+        // down, whole K per tile (no split partials), the last layer also to y
+        for (int64_t c0 = 0; c0 < C; c0 += kMaxPairs) {
+            StackStep D;
+            std::memset(&D, 0, sizeof(D));
+            D.nproj = 1;
+            D.K = (int)F;
+            D.splits = 1;
+            D.kb_per_split = (int)(F / 64);
+            D.tiles_m = tm;
+            D.ldx = F;
+            D.ldy = NT();
+            D.ldy2 = H;
+            D.kv_proj[0] = D.kv_proj[1] = -1;
+            D.rows[0] = (int)H;
+            D.yoff[0] = (int)offs(6);
+            D.tile_off[1] = (int)(skinny ? (H + kSkinnyRows - 1) / kSkinnyRows
+                                         : ((H + kTiledRows - 1) / kTiledRows) * tm);
+            for (int64_t c = c0; c < std::min(C, c0 + kMaxPairs); ++c) {
+                const int64_t t0 = c * ch, M = std::min(ch, P - t0);
+                StepPair& p = D.pair[D.npairs++];
+                p.W[0] = wptr(6);
+                p.ws[0] = sptr(6);
+                p.X = b + t0 * F;
+                p.xs = sb + t0;
+                p.Y = R + t0 * NT();
+                p.Y2 = l == L - 1 ? y + t0 * H : nullptr;
+                p.M = (int)M;
+            }
+            pf_status r = launched(skinny ? launch_gemm_stream(D, tb, s) : launch_gemm_tiled_step(D, ch, s));
+            if (r) return r;
+        }
+        return hipEventRecord(computed[l], s) == hipSuccess ? PF_OK : PF_ELAUNCH;
+    }
+
+    pf_status run()
+    {
+        const int64_t L = st->n_layers;
+        copied.assign((size_t)L, nullptr);
+        computed.assign((size_t)L, nullptr);
+        for (int64_t l = 0; l < L; ++l)
+            if (hipEventCreate(&copied[l]) != hipSuccess || hipEventCreate(&computed[l]) != hipSuccess)
+                return PF_ELAUNCH;
+        // the copy stream starts after the caller's earlier work (the ring may
+        // hold a previous call's layers)
+        hipEvent_t fork = nullptr;
+        if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess) return PF_ELAUNCH;
+        pf_status r = hipEventRecord(fork, s) == hipSuccess && hipStreamWaitEvent(cs, fork, 0) == hipSuccess
+                          ? PF_OK : PF_ELAUNCH;
+        (void)hipEventDestroy(fork);
+        // copies run up to nbuf - 1 layers ahead of the compute
+        for (int64_t l = 0; l < std::min(nbuf - 1, L) && !r; ++l) r = copy_layer(l);
+        for (int64_t l = 0; l < L && !r; ++l) {
+            if (l + nbuf - 1 < L) r = copy_layer(l + nbuf - 1);
+            if (!r) r = compute_layer(l);
+        }
+        return r;
+    }
+};
+
 }  // namespace
 
 // ===========================================================================
@@ -1392,6 +1631,82 @@ pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int
             stats->tail_tokens = per_token ? 1 : P - (stats->chunks - 1) * ch;
             rec.fill(stats);
         }
+        return st;
+    } catch (...) {
+        return PF_EINTERNAL;
+    }
+}
+
+size_t pf_prefill_stack_streamed_workspace(const pf_stack* stack, int64_t P, int64_t n_buffers)
+{
+    if (!stack || stack->hidden <= 0 || stack->ffn <= 0 || P <= 0 || n_buffers < 2) return 0;
+    return stream_layout(stack->hidden, stack->ffn, P, n_buffers).total;
+}
+
+pf_status pf_prefill_stack_streamed(const pf_stack* stack, const float* x, int64_t P, int64_t chunk,
+                                    float* y, int64_t n_buffers, void* workspace, size_t ws_bytes,
+                                    pf_stream_stats* stats, void* stream)
+{
+    try {
+        if (!stack || !stack->layers || stack->n_layers <= 0 || stack->layers_alt || stack->n_heads != 0)
+            return PF_EINVAL;
+        if (!valid_k(stack->hidden) || !valid_k(stack->ffn)) return PF_EINVAL;
+        if (stack->activation != PF_ACT_NONE && stack->activation != PF_ACT_SWIGLU) return PF_EINVAL;
+        for (int64_t l = 0; l < stack->n_layers; ++l)
+            for (int j = 0; j < PF_NPROJ; ++j)
+                if (!stack->layers[l].W[j] || !stack->layers[l].w_scale[j]) return PF_EINVAL;
+        if (P < 0 || chunk <= 0 || chunk > INT32_MAX || P > INT32_MAX || n_buffers < 2 || n_buffers > 64)
+            return PF_EINVAL;
+        if (stats) {
+            std::memset(stats, 0, sizeof(*stats));
+            stats->n_buffers = n_buffers;
+        }
+        if (P == 0) return PF_OK;
+        const int64_t H = stack->hidden, F = stack->ffn;
+        if (!x || !y || !aligned16(x) || !aligned4(y)) return PF_EINVAL;
+        const size_t xb = (size_t)P * H * 4;
+        if (overlap(x, xb, y, xb)) return PF_EINVAL;
+        const StreamLayout lay = stream_layout(H, F, P, n_buffers);
+        if (!workspace || ws_bytes < lay.total) return PF_EWORKSPACE;
+        if (!aligned16(workspace) || overlap(workspace, ws_bytes, x, xb) || overlap(workspace, ws_bytes, y, xb))
+            return PF_EINVAL;
+        if (pf_status st = check_device()) return st;
+        DevStreams* ds = dev_streams();
+        if (!ds) return PF_ENODEV;
+        std::unique_lock<std::mutex> lock(ds->mu);
+        if (!ds->copy && hipStreamCreateWithFlags(&ds->copy, hipStreamNonBlocking) != hipSuccess)
+            return PF_ELAUNCH;
+        StreamRun run{stack, x, P, std::min(chunk, P), n_buffers, y, static_cast<char*>(workspace), lay,
+                      (hipStream_t)stream, ds->copy, {}, {}};
+        hipEvent_t t0 = nullptr, t1 = nullptr;
+        if (stats && (hipEventCreate(&t0) != hipSuccess || hipEventCreate(&t1) != hipSuccess ||
+                      hipEventRecord(t0, run.s) != hipSuccess))
+            return PF_ELAUNCH;
+        pf_status st = run.run();
+        if (st == PF_OK && stats) {
+            // a layer's copy is a hit when it was complete before the compute of
+            // the layer before it ended (the compute never waited on it); the
+            // first layer's copy has nothing to hide behind and counts as a miss
+            if (hipEventRecord(t1, run.s) != hipSuccess || hipEventSynchronize(t1) != hipSuccess) {
+                st = PF_ELAUNCH;
+            } else {
+                float ms = 0.0f;
+                (void)hipEventElapsedTime(&ms, t0, t1);
+                stats->elapsed_ms = ms;
+                stats->layers_copied = stack->n_layers;
+                for (int64_t l = 0; l < stack->n_layers; ++l) {
+                    bool hit = false;
+                    if (l > 0 && hipEventElapsedTime(&ms, run.computed[l - 1], run.copied[l]) == hipSuccess)
+                        hit = ms <= 0.0f;
+                    if (hit) ++stats->prefetch_hits;
+                    else ++stats->prefetch_misses;
+                }
+                const int64_t rws = 5 * H + 2 * F;
+                stats->bytes_copied = (double)stack->n_layers * ((double)(4 * H + 2 * F) * H + (double)H * F + 4.0 * rws);
+            }
+        }
+        if (t0) (void)hipEventDestroy(t0);
+        if (t1) (void)hipEventDestroy(t1);
         return st;
     } catch (...) {
         return PF_EINTERNAL;
