@@ -315,7 +315,7 @@ PF_API size_t pf_moe_chunk_workspace(const pf_moe* moe, int64_t T);
  *   out[t] = +0 then, over the selected experts in ascending id,
  *     out[t][j] = fl(out[t][j] + fl(weights_e * y_e[j])).
  * ids [T][top_k] int32, weights [T][top_k] f32, out [T][H] f32.
- * Limits: T * top_k <= 65536, E <= 1024, top_k <= 32, E * ceil(T / 32) <= 12288. */
+ * Limits: T * top_k <= 65536, E <= 1024, top_k <= 32, T <= 16384. */
 PF_API pf_status pf_moe_chunk(const pf_moe* moe, const float* x, int64_t T, int32_t* ids,
                        float* weights, float* out, void* workspace, size_t ws_bytes,
                        void* stream);

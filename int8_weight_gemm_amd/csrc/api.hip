@@ -1728,7 +1728,7 @@ pf_status pf_moe_chunk(const pf_moe* moe, const float* x, int64_t T, int32_t* id
         if (T < 0 || T * moe->top_k > 65536) return PF_EINVAL;
         if (T == 0) return PF_OK;
         const int64_t E = moe->n_experts, k = moe->top_k, H = moe->hidden, I = moe->inter;
-        if ((size_t)E * ((T + 31) / 32) > 12288) return PF_EINVAL;   // grouping bitmap in LDS
+        if (T > 16384) return PF_EINVAL;                   // a grouping workgroup's bitmap in LDS
         if (!x || !ids || !weights || !out) return PF_EINVAL;
         if (!aligned16(x) || !aligned4(ids) || !aligned4(weights) || !aligned4(out))
             return PF_EINVAL;
@@ -1758,8 +1758,8 @@ pf_status pf_moe_chunk(const pf_moe* moe, const float* x, int64_t T, int32_t* id
         float* ypair = reinterpret_cast<float*>(ws + lay.ypair);
         const int Ti = (int)T, Ei = (int)E, ki = (int)k;
 
-        pf_status st = launched(launch_quantize(x, H, Ti, (int)H, xq, xs, s));
-        if (!st) st = launched(launch_router(moe->W_router, x, Ei, (int)H, Ti, logits, s));
+        // the router launch also quantises x (its workgroups stage every token row)
+        pf_status st = launched(launch_router(moe->W_router, x, Ei, (int)H, Ti, logits, xq, xs, s));
         if (!st) st = launched(launch_softmax_topk(logits, Ei, Ti, ki, (int)moe->renormalize, ids,
                                                    weights, s));
         if (!st) st = launched(launch_group(ids, weights, Ti, ki, Ei, off, pair_tok, comb_row, comb_w, s));

@@ -194,8 +194,10 @@ hipError_t launch_split_reduce(const GemmSet& set, hipStream_t s);
 constexpr int kTiledRows = 256;
 int tiled_tokens(int64_t M);
 
+// Router logits; with xq non-null the same launch quantises x per token into
+// xq [T][H] and xs [T].
 hipError_t launch_router(const float* Wr, const float* x, int E, int H, int T, float* logits,
-                         hipStream_t s);
+                         int8_t* xq, float* xs, hipStream_t s);
 hipError_t launch_softmax_topk(const float* logits, int E, int T, int k, int renorm, int* ids,
                                float* w, hipStream_t s);
 hipError_t launch_group(const int* ids, const float* w, int T, int k, int E, int* off,

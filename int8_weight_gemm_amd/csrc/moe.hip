@@ -23,10 +23,16 @@ constexpr int kRtTile = 32;
 constexpr int kRtK = 64;
 constexpr int kRtTI = 1, kRtEJ = 2;                    // chains per thread: tokens x experts
 
+// With xq non-null the launch also quantises x per token (a1's definition): a
+// workgroup stages all H values of its 32 tokens anyway, so it keeps their exact
+// absolute maxima on the way; workgroup (bx, by) then writes the codes and
+// scales of its share of the 32 rows, re-reading them from L2.
 template <int TI, int EJ>
 __global__ __launch_bounds__(1024 / (TI * EJ)) void k_router(const float* __restrict__ Wr,
                                                              const float* __restrict__ x, int E, int H, int T,
-                                                             float* __restrict__ logits)
+                                                             float* __restrict__ logits,
+                                                             int8_t* __restrict__ xq,
+                                                             float* __restrict__ xs)
 {
     constexpr int NT = 1024 / (TI * EJ);                // threads
     constexpr int CE = kRtTile / EJ, CT = kRtTile / TI;  // thread grid: CE experts x CT tokens
@@ -46,6 +52,7 @@ __global__ __launch_bounds__(1024 / (TI * EJ)) void k_router(const float* __rest
     const float* xr[NF];
     const float* wr[NF];
     float4 px[NF], pw[NF];
+    float am[NF];                                       // running |x| maxima of the staged rows
 #pragma unroll
     for (int u = 0; u < NF; ++u) {
         const int f = ((int)threadIdx.x + NT * u) % NP;
@@ -55,6 +62,7 @@ __global__ __launch_bounds__(1024 / (TI * EJ)) void k_router(const float* __rest
         wr[u] = Wr + (int64_t)min(e0 + rr[u], E - 1) * H + cc[u];
         px[u] = *reinterpret_cast<const float4*>(xr[u]);
         pw[u] = *reinterpret_cast<const float4*>(wr[u]);
+        am[u] = fmaxf(fmaxf(fabsf(px[u].x), fabsf(px[u].y)), fmaxf(fabsf(px[u].z), fabsf(px[u].w)));
     }
     if (stager) {
 #pragma unroll
@@ -100,9 +108,40 @@ __global__ __launch_bounds__(1024 / (TI * EJ)) void k_router(const float* __rest
             for (int u = 0; u < NF; ++u) {
                 *reinterpret_cast<float4*>(&sx[b ^ 1][rr[u]][cc[u]]) = px[u];
                 *reinterpret_cast<float4*>(&sw[b ^ 1][rr[u]][cc[u]]) = pw[u];
+                am[u] = fmaxf(am[u], fmaxf(fmaxf(fabsf(px[u].x), fabsf(px[u].y)),
+                                           fmaxf(fabsf(px[u].z), fabsf(px[u].w))));
             }
         }
         __syncthreads();
+    }
+    if (xq) {
+        // the row maxima: the 16 stagers of a row are 16 consecutive lanes
+        static_assert(NF == 1 && NP == NT, "one staged piece per thread and piece");
+        __shared__ float samax[kRtTile];
+        float m = am[0];
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        if ((threadIdx.x & 15) == 0) samax[rr[0]] = m;
+        __syncthreads();
+        // this workgroup's rows of the 32: an equal share per expert tile
+        const int per = (kRtTile + gridDim.x - 1) / gridDim.x;
+        const int r0 = blockIdx.x * per, r1 = min(r0 + per, kRtTile);
+        const int n4 = H >> 2;
+        for (int r = r0; r < r1 && t0 + r < T; ++r) {
+            const float sc = samax[r] / 127.0f;
+            if (threadIdx.x == 0) xs[t0 + r] = sc;
+            const float4* row = reinterpret_cast<const float4*>(x + (int64_t)(t0 + r) * H);
+            int* qrow = reinterpret_cast<int*>(xq + (int64_t)(t0 + r) * H);
+            for (int i = threadIdx.x; i < n4; i += NT) {
+                int packed = 0;
+                if (sc != 0.0f) {
+                    const float4 v = row[i];
+                    packed = (quant_code(v.x, sc) & 0xff) | ((quant_code(v.y, sc) & 0xff) << 8) |
+                             ((quant_code(v.z, sc) & 0xff) << 16) | ((quant_code(v.w, sc) & 0xff) << 24);
+                }
+                qrow[i] = packed;
+            }
+        }
     }
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -114,11 +153,11 @@ __global__ __launch_bounds__(1024 / (TI * EJ)) void k_router(const float* __rest
 }
 
 hipError_t launch_router(const float* Wr, const float* x, int E, int H, int T, float* logits,
-                         hipStream_t s)
+                         int8_t* xq, float* xs, hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
     dim3 g((E + kRtTile - 1) / kRtTile, (T + kRtTile - 1) / kRtTile);
-    PF_LAUNCH((k_router<kRtTI, kRtEJ>), g, dim3(1024 / (kRtTI * kRtEJ)), 0, s, Wr, x, E, H, T, logits);
+    PF_LAUNCH((k_router<kRtTI, kRtEJ>), g, dim3(1024 / (kRtTI * kRtEJ)), 0, s, Wr, x, E, H, T, logits, xq, xs);
     return hipGetLastError();
 }
 
@@ -244,15 +283,18 @@ hipError_t launch_softmax_topk(const float* logits, int E, int T, int k, int ren
 }
 
 // ---------------------------------------------------------------------------
-// Grouping by the union of selected experts (one workgroup): a bitmap of
-// (expert, token) selections in LDS, per-expert counts, an exclusive scan into
-// offsets.  Then every selected pair (t, e) independently: its row in the
+// Grouping by the union of selected experts.  Workgroup g of the grid owns
+// experts [g * kGrpE, (g + 1) * kGrpE).  Every workgroup counts the pairs of
+// every expert (LDS atomics) and scans the counts into the offsets (workgroup 0
+// writes them), and keeps an (expert x token) selection bitmap of its own
+// experts.  Then every pair of its experts independently: its row in the
 // expert's group is off[e] + the number of tokens below t that chose e (a
 // popcount over e's bitmap words), so each expert lists its tokens in
 // ascending order; its rank among t's selections is the number of t's ids
-// below e, which orders the combine table by ascending expert id.
-// With kLds the ids are first copied into LDS (after the bitmap), so the
-// per-pair reads below, the rank loop's among them, do not go to memory.
+// below e, which orders the combine table by ascending expert id.  With kLds
+// the ids are first copied into LDS, so the per-pair reads do not go to memory.
+constexpr int kGrpE = 16;
+
 template <bool kLds>
 __global__ __launch_bounds__(1024) void k_group(const int* __restrict__ ids_g,
                                                 const float* __restrict__ w, int T, int k, int E,
@@ -260,14 +302,15 @@ __global__ __launch_bounds__(1024) void k_group(const int* __restrict__ ids_g,
                                                 int* __restrict__ comb_row,
                                                 float* __restrict__ comb_w)
 {
-    extern __shared__ unsigned sel[];
+    extern __shared__ unsigned sel[];                   // [kGrpE][words], then the ids (kLds)
     __shared__ int cnt[1024];
     __shared__ int scan[1024];
     __shared__ int wsum[16];
     const int words = (T + 31) >> 5;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int np = T * k;
-    int* ids_l = reinterpret_cast<int*>(sel + E * words);
+    const int e0 = (int)blockIdx.x * kGrpE, e1 = min(e0 + kGrpE, E);
+    int* ids_l = reinterpret_cast<int*>(sel + kGrpE * words);
     if (kLds) {
         for (int p0 = 0; p0 < np; p0 += 4 * 1024) {
             int v[4];
@@ -284,13 +327,13 @@ __global__ __launch_bounds__(1024) void k_group(const int* __restrict__ ids_g,
         }
     }
     const int* ids = kLds ? ids_l : ids_g;
-    for (int i = tid; i < E * words; i += 1024) sel[i] = 0;
-    for (int i = tid; i < 1024; i += 1024) cnt[i] = 0;
+    for (int i = tid; i < kGrpE * words; i += 1024) sel[i] = 0;
+    cnt[tid] = 0;
     __syncthreads();
-    for (int p = tid; p < T * k; p += 1024) {
+    for (int p = tid; p < np; p += 1024) {
         const int t = p / k, e = ids[p];
-        atomicOr(&sel[e * words + (t >> 5)], 1u << (t & 31));
         atomicAdd(&cnt[e], 1);
+        if (e >= e0 && e < e1) atomicOr(&sel[(e - e0) * words + (t >> 5)], 1u << (t & 31));
     }
     __syncthreads();
     // inclusive scan of cnt[0..1024): within each wave by lane shuffles, then
@@ -306,11 +349,15 @@ __global__ __launch_bounds__(1024) void k_group(const int* __restrict__ ids_g,
     for (int i = 0; i < wave; ++i) v += wsum[i];
     scan[tid] = v;
     __syncthreads();
-    if (tid < E) off[tid + 1] = scan[tid];
-    if (tid == 0) off[0] = 0;
-    for (int p = tid; p < T * k; p += 1024) {
-        const int t = p / k, e = ids[p];
-        const unsigned* se = sel + e * words;
+    if (blockIdx.x == 0) {
+        if (tid < E) off[tid + 1] = scan[tid];
+        if (tid == 0) off[0] = 0;
+    }
+    for (int p = tid; p < np; p += 1024) {
+        const int e = ids[p];
+        if (e < e0 || e >= e1) continue;
+        const int t = p / k;
+        const unsigned* se = sel + (e - e0) * words;
         int below = __popc(se[t >> 5] & ((1u << (t & 31)) - 1u));
         for (int wd = 0; wd < (t >> 5); ++wd) below += __popc(se[wd]);
         const int pos = scan[e] - cnt[e] + below;
@@ -326,11 +373,12 @@ hipError_t launch_group(const int* ids, const float* w, int T, int k, int E, int
                         int* pair_tok, int* comb_row, float* comb_w, hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
-    const size_t lds = group_lds_bytes(T, E), with_ids = lds + (size_t)T * k * 4;
+    const size_t lds = group_lds_bytes(T, kGrpE), with_ids = lds + (size_t)T * k * 4;
+    const dim3 g((E + kGrpE - 1) / kGrpE);
     if (with_ids <= 64 * 1024)
-        PF_LAUNCH(k_group<true>, dim3(1), dim3(1024), with_ids, s, ids, w, T, k, E, off, pair_tok, comb_row, comb_w);
+        PF_LAUNCH(k_group<true>, g, dim3(1024), with_ids, s, ids, w, T, k, E, off, pair_tok, comb_row, comb_w);
     else
-        PF_LAUNCH(k_group<false>, dim3(1), dim3(1024), lds, s, ids, w, T, k, E, off, pair_tok, comb_row, comb_w);
+        PF_LAUNCH(k_group<false>, g, dim3(1024), lds, s, ids, w, T, k, E, off, pair_tok, comb_row, comb_w);
     return hipGetLastError();
 }
 
