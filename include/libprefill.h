@@ -182,8 +182,8 @@ typedef struct {
 #define PF_ACT_NONE 0
 #define PF_ACT_SWIGLU 1
 
-/* Statistics of one pf_prefill_stack call.  time_kernels is the only input:
- * set it to 1 to give every launch a pair of HIP events stamped when the kernel
+/* Statistics of one pf_prefill_stack call.  time_kernels and max_groups are
+ * the inputs: set time_kernels to 1 to give every launch a pair of HIP events stamped when the kernel
  * itself starts and ends (hipExtLaunchKernelGGL) and get per-class device
  * times; kernels of the three chunk groups (one stream each) overlap in time,
  * so the summed launch durations (product_ms, quant_ms) can exceed the call's
@@ -197,6 +197,10 @@ typedef struct {
  * reported apart as overhead_bytes. */
 typedef struct {
     int time_kernels;          /* in: 1 = time every launch                       */
+    int max_groups;            /* in: at most this many chunk groups (0: the library's
+                                  choice, 3); 1 runs every launch in order on the
+                                  caller's stream, so no two launches overlap      */
+    int groups;                /* out: chunk groups used                          */
     int per_token_mode;        /* out: 1 if the per-token GEMV path ran           */
     int64_t chunks;            /* chunks processed (the last may be ragged)       */
     int64_t tail_tokens;       /* tokens in the last chunk                        */

@@ -47,7 +47,8 @@ class _Stack(ctypes.Structure):
 
 
 class StackStats(ctypes.Structure):
-    _fields_ = [("time_kernels", ctypes.c_int), ("per_token_mode", ctypes.c_int),
+    _fields_ = [("time_kernels", ctypes.c_int), ("max_groups", ctypes.c_int),
+                ("groups", ctypes.c_int), ("per_token_mode", ctypes.c_int),
                 ("chunks", ctypes.c_int64), ("tail_tokens", ctypes.c_int64),
                 ("launches", ctypes.c_int64), ("alg_bytes", ctypes.c_double),
                 ("elapsed_ms", ctypes.c_double), ("product_launches", ctypes.c_int64),
@@ -255,11 +256,11 @@ class Stack:
 
     def prefill(self, x: torch.Tensor, chunk: int, ws: torch.Tensor, y: torch.Tensor | None = None,
                 proj: torch.Tensor | None = None, stats: bool = False, time_kernels: bool = False,
-                kv: torch.Tensor | None = None):
+                kv: torch.Tensor | None = None, max_groups: int = 0):
         """x f32 [P, H] -> y f32 [P, H]; proj (optional) f32 [L, P, 5H + 2F]; kv,
         the K/V cache f32 [L, 2, P, H], required with n_heads > 0.  With stats
         (or time_kernels) also returns the call's statistics."""
-        stats = stats or time_kernels
+        stats = stats or time_kernels or max_groups > 0
         _dev(x, torch.float32, "x")
         P = x.shape[0]
         if y is None:
@@ -267,6 +268,7 @@ class Stack:
         st = StackStats() if stats else None
         if st is not None:
             st.time_kernels = 1 if time_kernels else 0
+            st.max_groups = int(max_groups)
         _check("pf_prefill_stack", lib().pf_prefill_stack(
             ctypes.byref(self._desc), _ptr(x), P, chunk, _ptr(y), _ptr(proj), _ptr(kv), _ptr(ws), ws.numel(),
             ctypes.byref(st) if st is not None else None, _stream()))

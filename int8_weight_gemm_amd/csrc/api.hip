@@ -1584,8 +1584,10 @@ pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int
         const bool timed = stats && stats->time_kernels;
         if (P == 0) {
             if (stats) {
+                const int max_groups = stats->max_groups;
                 std::memset(stats, 0, sizeof(*stats));
                 stats->time_kernels = timed ? 1 : 0;
+                stats->max_groups = max_groups;
             }
             return PF_OK;
         }
@@ -1618,14 +1620,18 @@ pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int
         if (!per_token && ds && C >= 2 && lay.groups >= 2) {
             lock = std::unique_lock<std::mutex>(ds->mu);
             if (ensure_streams(ds) == PF_OK) run.ng = (int)std::min<int64_t>(lay.groups, C);
+            if (stats && stats->max_groups > 0) run.ng = std::min(run.ng, stats->max_groups);
         }
         run.ds = ds;
         pf_status st = rec.begin();
         if (st == PF_OK) st = per_token ? run.per_token(rec) : run.sweep(rec);
         if (st == PF_OK) st = rec.end();
         if (st == PF_OK && stats) {
+            const int max_groups = stats->max_groups;
             std::memset(stats, 0, sizeof(*stats));
             stats->time_kernels = timed ? 1 : 0;
+            stats->max_groups = max_groups;
+            stats->groups = run.ng;
             stats->per_token_mode = per_token ? 1 : 0;
             stats->chunks = per_token ? P : (P + ch - 1) / ch;
             stats->tail_tokens = per_token ? 1 : P - (stats->chunks - 1) * ch;
