@@ -163,7 +163,8 @@ SkinnyPlan plan_tiled(int64_t N, int64_t K, int64_t M, int max_splits = 16)
         const int64_t tiles = tiles_n * ((M + tw - 1) / tw);
         const double stage_us = tw == 256 ? 1.2 : 0.85;
         for (int sp = 1; sp <= max_splits && (sp == 1 || nkb / sp >= 8); sp *= 2) {
-            const int kbs = (nkb + sp - 1) / sp;
+            int kbs = (nkb + sp - 1) / sp;
+            if (kbs > 1 && (kbs & 1)) ++kbs;   // even: a split starts on a 128-byte line
             const int splits = (nkb + kbs - 1) / kbs;
             const int64_t rounds = (tiles * splits + kComputeUnits - 1) / kComputeUnits;
             double us = (double)rounds * (kbs + 6) * stage_us;

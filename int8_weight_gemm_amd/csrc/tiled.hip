@@ -6,24 +6,22 @@
 //  * a workgroup of eight waves (two per SIMD) owns 256 weight rows x 64 WJ
 //    tokens (WJ = 4 or 2); wave (wn, wm) of the 2 x 4 grid owns 128 rows x
 //    16 WJ tokens: 4 x WJ / 2 accumulator blocks of 32 x 32;
-//  * a stage is one k-block (64 bytes of K) of the tile's weight rows and
-//    tokens in LDS as 1 KB fragments of 16 rows x 64 bytes.  A copy gives four
-//    consecutive lanes one row's 64 contiguous bytes (lane l: row l / 4), the
-//    order in which the address unit serves a fragment ~2.5x faster than one
-//    16-byte piece of each of 16 rows per lane group; lane l lands at 16 l, so
-//    piece c of row r sits at 64 r + 16 (c ^ ((r / 2) % 4)), and the MFMA
-//    operands are read with one conflict-free ds_read_b128 each; a ring of
-//    four stages, one barrier per stage, and the reads of stage g + 1 are in
-//    flight while the MFMAs of stage g run;
-//  * every fragment, weights and tokens, is copied by global_load_lds_dwordx4,
-//    three stages ahead.  These copies, 32 KB per stage and compute unit, are
-//    what holds the kernel: alone (no operand reads, no MFMAs) they take about
-//    80% of its time, while the operand reads and MFMAs alone take about 73%;
+//  * a stage is two k-blocks (128 bytes of K) of the tile's weight rows and
+//    tokens in LDS as 1 KB fragments of 8 rows x 128 bytes, copied by
+//    global_load_lds_dwordx4 with eight consecutive lanes on one row's 128
+//    bytes, so every copy instruction reads whole 128-byte lines (whose
+//    requests the memory path serves ~30% faster than 64-byte ones); pieces
+//    are swizzled so that the MFMA operand reads (one ds_read_b128 each) are
+//    conflict-free; a ring of two (256 tokens) or three (128 tokens) stages,
+//    one barrier per stage;
+//  * each k-block's LDS operand reads for the next k-block are issued between
+//    this k-block's MFMAs and waited for inside the same asm block, so no LDS
+//    load is ever in flight outside the code that issued it;
 //  * workgroups on one XCD (blockIdx % 8) take consecutive tiles, and the token
 //    tiles of one band of weight rows are consecutive, so the band is fetched
 //    from HBM once into that XCD's L2 and shared.
-// Epilogue: y[t][n] = fl(fl(acc) * fl(ws[n] * xs[t])), 16-byte stores of four
-// consecutive rows of one token where alignment allows.
+// Epilogue: y[t][n] = fl(fl(acc) * fl(ws[n] * xs[t])), written through LDS as
+// whole 512-byte token rows; split products write int32 partials instead.
 #include "device.hpp"
 #include "kernels.hpp"
 #include "lds_dma.hpp"
@@ -31,268 +29,24 @@
 
 namespace pf {
 
+// Waves per tiled workgroup.
+constexpr int kTiledWaves = 8;
 
-// One stage's MFMA operands of a wave: 8 weight operands (4 row blocks x 2 k
-// halves), WM token ones (WM / 2 token blocks x 2 k halves).
-template <int WM>
-struct TlFrags {
-    v4i a[8];
-    v4i b[WM];
-};
-
-// Issue the wave's LDS reads of one stage without waiting; tl_wait waits for
-// them.  Operand q = 2 i + kh (32-row block i, k half kh) is read at
-// a_kh + 2 KB i (weights) or b_kh + 2 KB i (tokens), a_kh and b_kh carrying
-// the lane's own offset in the block for k half kh.  The wait names every
-// destination register, so no use of one can be placed before it.
-template <int WM>
-__device__ __forceinline__ void tl_issue(TlFrags<WM>& f, uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1);
-template <int WM>
-__device__ __forceinline__ void tl_wait(TlFrags<WM>& f);
-
-template <>
-__device__ __forceinline__ void tl_issue<4>(TlFrags<4>& f, uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1)
-{
-    asm volatile(
-        "ds_read_b128 %0, %12 offset:0\n"
-        "ds_read_b128 %1, %13 offset:0\n"
-        "ds_read_b128 %2, %12 offset:2048\n"
-        "ds_read_b128 %3, %13 offset:2048\n"
-        "ds_read_b128 %4, %12 offset:4096\n"
-        "ds_read_b128 %5, %13 offset:4096\n"
-        "ds_read_b128 %6, %12 offset:6144\n"
-        "ds_read_b128 %7, %13 offset:6144\n"
-        "ds_read_b128 %8, %14 offset:0\n"
-        "ds_read_b128 %9, %15 offset:0\n"
-        "ds_read_b128 %10, %14 offset:2048\n"
-        "ds_read_b128 %11, %15 offset:2048\n"
-        : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.a[2]), "=&v"(f.a[3]),
-          "=&v"(f.a[4]), "=&v"(f.a[5]), "=&v"(f.a[6]), "=&v"(f.a[7]),
-          "=&v"(f.b[0]), "=&v"(f.b[1]), "=&v"(f.b[2]), "=&v"(f.b[3])
-        : "v"(a0), "v"(a1), "v"(b0), "v"(b1));
-}
-
-template <>
-__device__ __forceinline__ void tl_issue<2>(TlFrags<2>& f, uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1)
-{
-    asm volatile(
-        "ds_read_b128 %0, %10 offset:0\n"
-        "ds_read_b128 %1, %11 offset:0\n"
-        "ds_read_b128 %2, %10 offset:2048\n"
-        "ds_read_b128 %3, %11 offset:2048\n"
-        "ds_read_b128 %4, %10 offset:4096\n"
-        "ds_read_b128 %5, %11 offset:4096\n"
-        "ds_read_b128 %6, %10 offset:6144\n"
-        "ds_read_b128 %7, %11 offset:6144\n"
-        "ds_read_b128 %8, %12 offset:0\n"
-        "ds_read_b128 %9, %13 offset:0\n"
-        : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.a[2]), "=&v"(f.a[3]),
-          "=&v"(f.a[4]), "=&v"(f.a[5]), "=&v"(f.a[6]), "=&v"(f.a[7]),
-          "=&v"(f.b[0]), "=&v"(f.b[1])
-        : "v"(a0), "v"(a1), "v"(b0), "v"(b1));
-}
-
-template <>
-__device__ __forceinline__ void tl_wait<2>(TlFrags<2>& f)
-{
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]),
-                 "+v"(f.a[4]), "+v"(f.a[5]), "+v"(f.a[6]), "+v"(f.a[7]),
-                 "+v"(f.b[0]), "+v"(f.b[1]));
-}
-
-template <>
-__device__ __forceinline__ void tl_wait<4>(TlFrags<4>& f)
-{
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]),
-                 "+v"(f.a[4]), "+v"(f.a[5]), "+v"(f.a[6]), "+v"(f.a[7]),
-                 "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]));
-}
-
-template <>
-__device__ __forceinline__ void tl_issue<8>(TlFrags<8>& f, uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1)
-{
-    asm volatile(
-        "ds_read_b128 %0, %16 offset:0\n"
-        "ds_read_b128 %1, %17 offset:0\n"
-        "ds_read_b128 %2, %16 offset:2048\n"
-        "ds_read_b128 %3, %17 offset:2048\n"
-        "ds_read_b128 %4, %16 offset:4096\n"
-        "ds_read_b128 %5, %17 offset:4096\n"
-        "ds_read_b128 %6, %16 offset:6144\n"
-        "ds_read_b128 %7, %17 offset:6144\n"
-        "ds_read_b128 %8, %18 offset:0\n"
-        "ds_read_b128 %9, %19 offset:0\n"
-        "ds_read_b128 %10, %18 offset:2048\n"
-        "ds_read_b128 %11, %19 offset:2048\n"
-        "ds_read_b128 %12, %18 offset:4096\n"
-        "ds_read_b128 %13, %19 offset:4096\n"
-        "ds_read_b128 %14, %18 offset:6144\n"
-        "ds_read_b128 %15, %19 offset:6144\n"
-        : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.a[2]), "=&v"(f.a[3]),
-          "=&v"(f.a[4]), "=&v"(f.a[5]), "=&v"(f.a[6]), "=&v"(f.a[7]),
-          "=&v"(f.b[0]), "=&v"(f.b[1]), "=&v"(f.b[2]), "=&v"(f.b[3]),
-          "=&v"(f.b[4]), "=&v"(f.b[5]), "=&v"(f.b[6]), "=&v"(f.b[7])
-        : "v"(a0), "v"(a1), "v"(b0), "v"(b1));
-}
-
-template <>
-__device__ __forceinline__ void tl_wait<8>(TlFrags<8>& f)
-{
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]),
-                 "+v"(f.a[4]), "+v"(f.a[5]), "+v"(f.a[6]), "+v"(f.a[7]),
-                 "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]),
-                 "+v"(f.b[4]), "+v"(f.b[5]), "+v"(f.b[6]), "+v"(f.b[7]));
-}
-
-// One 256 x 64 WJ output tile of problem P (tile index `local`, token tiles
-// fastest), by NW waves (4: one per SIMD; 8: two per SIMD) in a 2 x NW/2 grid:
-// wave (wn, wm) owns rows 128 wn .. + 127 and JB = 4 WJ / NW token blocks of
-// 32 from token 32 JB wm: 4 x JB accumulator blocks of 32 x 32.  Stage s (one
-// k-block) sits in ring slot s % 4: weight fragments 0 .. 15 (16 rows x 64
-// bytes each), then token fragments 0 .. 4 WJ - 1; wave w copies fragments
-// w + NW h of each by DMA.  Iteration g:
-//   wait for stage g's fragments (read in iteration g - 1) and this wave's
-//   copies of stage g + 1; barrier (stage g + 1 published, stage g read by
-//   all); copy stage g + 4 into the slot of stage g; issue the reads of stage
-//   g + 1; the MFMAs of stage g.
-// With two waves per SIMD, the waves of the second row half copy after their
-// first k half of MFMAs instead: a wave issuing copies issues no MFMA, and
-// its SIMD's other wave then does.
-// Every iteration issues the same copies (k-blocks past the end are clamped
-// to the last one and land in free slots, never read), so every wait is a
-// constant.
+// The epilogue of a tile: lane l, register 4 q + r of a 32 x 32 block holds
+// token l % 32, row 8 q + 4 (l / 32) + r.  Split: this split's int32
+// partials; unsplit: y = fl(fl(acc) * fl(ws * xs)) with the tile's scales
+// staged once in LDS.  The tile leaves through the (now idle) ring in two
+// passes, rows 128 h .. + 127 in pass h: the waves of that row half write
+// their values as [token][128 rows], the 16-byte piece of rows 4 g .. 4 g + 3
+// of token u at 512 u + 16 (g ^ (u % 32)), then every thread stores whole
+// 512-byte token rows, 32 lanes per token.  (Each lane storing its own 16-byte
+// pieces, 64 tokens per instruction, cost ~20% of the 7B prompt's time.)
 template <int WJ, int NW>
-__device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int kidx)
+__device__ __forceinline__ void tiled_store(const GemmProb& P, int8_t* ring, int n0, int t0,
+                                            int kidx, v16i (&acc)[4][2 * WJ / (NW / 2)], int wn, int wm, int lane)
 {
-    constexpr int NS = 4;
-    constexpr int WMT = NW / 2;                          // token parts of the wave grid
-    constexpr int JB = 2 * WJ / WMT;                     // 32-token blocks per wave
-    constexpr int WB = 2 * JB;                           // token operands per wave per stage
-    constexpr int kFa = 16, kFb = 4 * WJ;                // fragments per stage
-    constexpr int kStage = (kFa + kFb) * 1024;
-    constexpr int ka = kFa / NW, kb = kFb / NW;          // copies per wave per stage
-    constexpr int kOps = ka + kb;                        // vector-memory ops per wave per stage
-    static_assert(NW == 4 || NW == 8, "four or eight waves");
-    static_assert(kb * NW == kFb && JB >= 1, "tile shape");
-    static_assert(3 * kOps <= 63, "vmcnt range");
-    __shared__ __attribute__((aligned(16))) int8_t ring[NS * kStage];
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int tm = local % P.tiles_m, tn = local / P.tiles_m;
-    const int n0 = tn * 256, t0 = tm * 64 * WJ;
-    // this split's k-blocks: kb0 .. kb0 + nkb - 1 (all of K when unsplit)
-    const int kb0 = kidx * P.kb_per_split;
-    const int nkb = min(P.kb_per_split, (P.K >> 6) - kb0);
-    // fragment f: rows (or tokens) 16 f .. + 15 of the k-block; lane l copies
-    // row l / 4, piece (l % 4) ^ ((l / 8) % 4), to 16 l.  Rows and tokens past
-    // the end repeat the last one; their results are never stored.
+    constexpr int JB = 2 * WJ / (NW / 2);
     const int lrow = lane & 31;
-    const int crow = lane >> 2;                          // row this lane copies
-    const int kof = ((lane & 3) ^ ((lane >> 3) & 3)) << 4;
-    const int8_t* asrc[ka];
-#pragma unroll
-    for (int h = 0; h < ka; ++h) {
-        const int f = wave + NW * h;
-        asrc[h] = P.W + (int64_t)min(n0 + 16 * f + crow, P.N - 1) * P.K + kof;
-    }
-    const int8_t* bsrc[kb];
-#pragma unroll
-    for (int h = 0; h < kb; ++h) {
-        const int f = wave + NW * h;
-        bsrc[h] = P.X + (int64_t)min(t0 + 16 * f + crow, P.M - 1) * P.ldx + kof;
-    }
-    const uint32_t ring0 = lds_addr(ring);
-
-    auto kbo = [&](int s) { return (int64_t)(kb0 + min(s, nkb - 1)) * 64; };
-    // stage s into its slot: this wave's weight fragments w + NW h and token
-    // fragments kFa + w + NW h, all by DMA (kOps copies)
-    auto put = [&](int s) {
-        int8_t* slot = ring + (s % NS) * kStage;
-#pragma unroll
-        for (int h = 0; h < ka; ++h) dma16(asrc[h] + kbo(s), slot + (wave + NW * h) * 1024);
-#pragma unroll
-        for (int h = 0; h < kb; ++h) dma16(bsrc[h] + kbo(s), slot + (kFa + wave + NW * h) * 1024);
-    };
-
-    // The 32 x 32 x 32 operand of rows 32 i .. + 31, k half kh: lane l needs
-    // row r = l % 32, piece c = 2 kh + l / 32, which sits in fragment
-    // 2 i + r / 16 at 64 (r % 16) + 16 (c ^ ((r % 16 / 2) % 4)); for k half 1
-    // that is the half-0 offset with bit 5 flipped.  Any 8 consecutive lanes
-    // read 8 different 16-byte bank groups.
-    const uint32_t lofs = (uint32_t)(((lane >> 4) & 1) * 1024 + 64 * (lane & 15) +
-                                     16 * ((lane >> 5) ^ ((lane >> 1) & 3)));   // k half 0; half 1: ^ 32
-    const int wn = wave / WMT, wm = wave % WMT;
-    const uint32_t ra0 = ring0 + wn * 8 * 1024 + lofs, ra1 = ring0 + wn * 8 * 1024 + (lofs ^ 32);
-    const uint32_t rb0 = ring0 + (kFa + wm * WB) * 1024 + lofs, rb1 = ring0 + (kFa + wm * WB) * 1024 + (lofs ^ 32);
-    const bool late_copy = NW == 8 && wn == 1;           // copies after the first k half
-
-    v16i acc[4][JB];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < JB; ++j) acc[i][j] = v16i{};
-
-    // stages 0 .. NS - 1 into the ring, one stage per fenced group
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        put(s);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    }
-    wait_vmcnt<(NS - 1) * kOps>();                       // own copies of stage 0
-    stage_barrier();
-    TlFrags<WB> fr[2];
-    tl_issue<WB>(fr[0], ra0, ra1, rb0, rb1);
-
-    // Iteration g: wait for stage g's operands (read in iteration g - 1) and
-    // this wave's copies of stage g + 1; barrier (stage g + 1 published, stage
-    // g read by all); copy stage g + NS into the slot of stage g; issue the
-    // reads of stage g + 1; the MFMAs of stage g.  A tail step is the last
-    // stage (g = nkb - 1) and reads and copies nothing.
-    auto step = [&](int g, TlFrags<WB>& cur, TlFrags<WB>& nxt, bool tail) {
-        tl_wait<WB>(cur);
-        const bool more = !tail && g + 1 < nkb;
-        if (more) {
-            wait_vmcnt<(NS - 2) * kOps>();               // own copies of stage g + 1
-            stage_barrier();                             // stage g + 1 published; stage g read by all
-            if (!late_copy) put(g + NS);                 // into the slot of stage g
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);     // this stage's copies stay in it
-            const uint32_t so = (uint32_t)(((g + 1) % NS) * kStage);
-            tl_issue<WB>(nxt, ra0 + so, ra1 + so, rb0 + so, rb1 + so);
-        }
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            if (kh == 1 && more && late_copy) put(g + NS);
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < JB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[2 * i + kh], cur.b[2 * j + kh],
-                                                                     acc[i][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    int g = 0;
-    for (; g + 1 < nkb; g += 2) {                        // the same registers every pass
-        step(g, fr[0], fr[1], false);
-        step(g + 1, fr[1], fr[0], false);
-    }
-    if (g < nkb) step(g, fr[0], fr[1], true);
-    wait_vmcnt<0>();                                     // no copy outlives the workgroup's LDS
-
-    // Lane l, register 4 q + r of a 32 x 32 block: token l % 32, row
-    // 8 q + 4 (l / 32) + r.  Split: this split's int32 partials; unsplit: the
-    // epilogue with the tile's scales staged once in LDS.  The tile leaves
-    // through the ring in two passes, rows 128 h .. + 127 in pass h: the waves
-    // of that row half write their values as [token][128 rows], the 16-byte
-    // piece of rows 4 g .. 4 g + 3 of token u at 512 u + 16 (g ^ (u % 32)), then
-    // every thread stores whole 512-byte token rows, 32 lanes per token.  (Each
-    // lane storing its own 16-byte pieces, 64 tokens per instruction, cost
-    // ~20% of the 7B prompt's time.)
     const bool split = P.splits > 1;
     int* const part = split ? P.acc + (int64_t)kidx * P.acc_split : nullptr;
     __shared__ float sws[256], sxs[256];
@@ -306,7 +60,6 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
                            : (((uintptr_t)P.Y & 15) == 0 && (P.ldy & 3) == 0 &&
                               (!P.Y2 || (((uintptr_t)P.Y2 & 15) == 0 && (P.ldy2 & 3) == 0)));
     constexpr int kPieces = 64 * WJ * 32;                // 16-byte pieces per pass
-    static_assert(64 * WJ * 512 <= NS * kStage, "a pass fits in the ring");
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         if (wn == h) {
@@ -365,6 +118,270 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
     }
 }
 
+// ---------------------------------------------------------------------------
+// Stages of two k-blocks.  A stage is 128 bytes of K of the tile's 256 weight
+// rows and 64 WJ tokens in LDS as 1 KB fragments of 8 rows x 128 bytes, so
+// every copy instruction reads whole 128-byte lines: eight consecutive lanes
+// take one row's 128 bytes (lane l: row l / 8 of the fragment, landing at
+// 16 l), with piece c of row r (r counted in the stage) at
+// 128 r + 16 (c ^ s(r)), s(r) = (r % 8) ^ ((r / 8) % 2), so that any 16
+// consecutive lanes of an operand read touch 16 different 16-byte bank groups
+// of a 256-byte span.  A ring of NS stages (two of 64 KB at 256 tokens, three
+// of 48 KB at 128), copied NS - 1 stages ahead, one barrier per stage.
+//
+// Each k-block of a stage is one asm block that issues the LDS reads of the
+// next k-block's operands, runs this k-block's MFMAs from registers and waits
+// for the reads before it ends, so no load is in flight outside the block
+// that issued it.
+
+// One k-block's MFMA operands of a wave: a[2 i + kh] for row block i (32 rows)
+// and k half kh (32 bytes), b[2 j + kh] for token block j.
+template <int JB>
+struct KbOps {
+    v4i a[8];
+    v4i b[2 * JB];
+};
+
+#define PF_RD(dst, adr, off) "ds_read_b128 %[" #dst "], %[" #adr "] offset:" #off "\n"
+#define PF_MF(c, a, b) "v_mfma_i32_32x32x32_i8 %[" #c "], %[" #a "], %[" #b "], %[" #c "]\n"
+
+// kb_half<JB, KH>: n's k half KH <- the operands at ra (row block i at
+// + 4096 i) and rb (token block j at + 4096 j), acc += the products of c's k
+// half KH, then wait for the reads.  A k-block is two of these, so that c's
+// half 0 is dead before n's half 1 is read into its registers.  The compiler
+// cannot see the MFMAs inside, so each block first gives the two wait states
+// an MFMA needs after a vector ALU write of its sources (the accumulators are
+// cleared that way): one s_nop, one read.
+template <int JB, int KH>
+__device__ __forceinline__ void kb_half(KbOps<JB>& n, const KbOps<JB>& c, v16i (&acc)[4][JB],
+                                        uint32_t ra, uint32_t rb)
+{
+    if constexpr (JB == 2) {
+        asm volatile(
+            "s_nop 0\n"
+            PF_RD(na0, ra, 0) PF_MF(c00, a0, b0)
+            PF_RD(nb0, rb, 0) PF_MF(c01, a0, b1)
+            PF_RD(na1, ra, 4096) PF_MF(c10, a1, b0)
+            PF_RD(nb1, rb, 4096) PF_MF(c11, a1, b1)
+            PF_RD(na2, ra, 8192) PF_MF(c20, a2, b0)
+            PF_RD(na3, ra, 12288) PF_MF(c21, a2, b1)
+            PF_MF(c30, a3, b0)
+            PF_MF(c31, a3, b1)
+            "s_waitcnt lgkmcnt(0)"
+            : [na0] "=&v"(n.a[KH]), [na1] "=&v"(n.a[2 + KH]), [na2] "=&v"(n.a[4 + KH]), [na3] "=&v"(n.a[6 + KH]),
+              [nb0] "=&v"(n.b[KH]), [nb1] "=&v"(n.b[2 + KH]),
+              [c00] "+v"(acc[0][0]), [c01] "+v"(acc[0][1]), [c10] "+v"(acc[1][0]), [c11] "+v"(acc[1][1]),
+              [c20] "+v"(acc[2][0]), [c21] "+v"(acc[2][1]), [c30] "+v"(acc[3][0]), [c31] "+v"(acc[3][1])
+            : [a0] "v"(c.a[KH]), [a1] "v"(c.a[2 + KH]), [a2] "v"(c.a[4 + KH]), [a3] "v"(c.a[6 + KH]),
+              [b0] "v"(c.b[KH]), [b1] "v"(c.b[2 + KH]), [ra] "v"(ra), [rb] "v"(rb));
+    } else {
+        asm volatile(
+            "s_nop 0\n"
+            PF_RD(na0, ra, 0) PF_MF(c0, a0, b0)
+            PF_RD(nb0, rb, 0) PF_MF(c1, a1, b0)
+            PF_RD(na1, ra, 4096) PF_MF(c2, a2, b0)
+            PF_RD(na2, ra, 8192) PF_MF(c3, a3, b0)
+            PF_RD(na3, ra, 12288)
+            "s_waitcnt lgkmcnt(0)"
+            : [na0] "=&v"(n.a[KH]), [na1] "=&v"(n.a[2 + KH]), [na2] "=&v"(n.a[4 + KH]), [na3] "=&v"(n.a[6 + KH]),
+              [nb0] "=&v"(n.b[KH]),
+              [c0] "+v"(acc[0][0]), [c1] "+v"(acc[1][0]), [c2] "+v"(acc[2][0]), [c3] "+v"(acc[3][0])
+            : [a0] "v"(c.a[KH]), [a1] "v"(c.a[2 + KH]), [a2] "v"(c.a[4 + KH]), [a3] "v"(c.a[6 + KH]),
+              [b0] "v"(c.b[KH]), [ra] "v"(ra), [rb] "v"(rb));
+    }
+}
+
+// kb_step: n <- the next k-block's operands (k half kh at ra_kh, rb_kh),
+// acc += the products of c.
+template <int JB>
+__device__ __forceinline__ void kb_step(KbOps<JB>& n, const KbOps<JB>& c, v16i (&acc)[4][JB],
+                                        uint32_t ra0, uint32_t ra1, uint32_t rb0, uint32_t rb1)
+{
+    kb_half<JB, 0>(n, c, acc, ra0, rb0);
+    kb_half<JB, 1>(n, c, acc, ra1, rb1);
+}
+
+// kb_read: n <- the operands at (ra0, ra1, rb0, rb1), waited for.
+template <int JB>
+__device__ __forceinline__ void kb_read(KbOps<JB>& n, uint32_t ra0, uint32_t ra1, uint32_t rb0, uint32_t rb1)
+{
+    if constexpr (JB == 2) {
+        asm volatile(
+            PF_RD(na0, ra0, 0) PF_RD(na1, ra1, 0) PF_RD(na2, ra0, 4096) PF_RD(na3, ra1, 4096)
+            PF_RD(na4, ra0, 8192) PF_RD(na5, ra1, 8192) PF_RD(na6, ra0, 12288) PF_RD(na7, ra1, 12288)
+            PF_RD(nb0, rb0, 0) PF_RD(nb1, rb1, 0) PF_RD(nb2, rb0, 4096) PF_RD(nb3, rb1, 4096)
+            "s_waitcnt lgkmcnt(0)"
+            : [na0] "=&v"(n.a[0]), [na1] "=&v"(n.a[1]), [na2] "=&v"(n.a[2]), [na3] "=&v"(n.a[3]),
+              [na4] "=&v"(n.a[4]), [na5] "=&v"(n.a[5]), [na6] "=&v"(n.a[6]), [na7] "=&v"(n.a[7]),
+              [nb0] "=&v"(n.b[0]), [nb1] "=&v"(n.b[1]), [nb2] "=&v"(n.b[2]), [nb3] "=&v"(n.b[3])
+            : [ra0] "v"(ra0), [ra1] "v"(ra1), [rb0] "v"(rb0), [rb1] "v"(rb1));
+    } else {
+        asm volatile(
+            PF_RD(na0, ra0, 0) PF_RD(na1, ra1, 0) PF_RD(na2, ra0, 4096) PF_RD(na3, ra1, 4096)
+            PF_RD(na4, ra0, 8192) PF_RD(na5, ra1, 8192) PF_RD(na6, ra0, 12288) PF_RD(na7, ra1, 12288)
+            PF_RD(nb0, rb0, 0) PF_RD(nb1, rb1, 0)
+            "s_waitcnt lgkmcnt(0)"
+            : [na0] "=&v"(n.a[0]), [na1] "=&v"(n.a[1]), [na2] "=&v"(n.a[2]), [na3] "=&v"(n.a[3]),
+              [na4] "=&v"(n.a[4]), [na5] "=&v"(n.a[5]), [na6] "=&v"(n.a[6]), [na7] "=&v"(n.a[7]),
+              [nb0] "=&v"(n.b[0]), [nb1] "=&v"(n.b[1])
+            : [ra0] "v"(ra0), [ra1] "v"(ra1), [rb0] "v"(rb0), [rb1] "v"(rb1));
+    }
+}
+
+
+// kb_last: acc += the products of c (the last k-block: nothing to read).  It
+// ends with 20 wait states, more than a 16-pass MFMA needs before a vector
+// ALU instruction may read its result, since the compiler does not see these
+// MFMAs when it places the epilogue's reads of acc.
+template <int JB>
+__device__ __forceinline__ void kb_last(const KbOps<JB>& c, v16i (&acc)[4][JB])
+{
+    if constexpr (JB == 2) {
+        asm volatile(
+            "s_nop 1\n"
+            PF_MF(c00, a0, b0) PF_MF(c01, a0, b2) PF_MF(c10, a2, b0) PF_MF(c11, a2, b2)
+            PF_MF(c20, a4, b0) PF_MF(c21, a4, b2) PF_MF(c30, a6, b0) PF_MF(c31, a6, b2)
+            PF_MF(c00, a1, b1) PF_MF(c01, a1, b3) PF_MF(c10, a3, b1) PF_MF(c11, a3, b3)
+            PF_MF(c20, a5, b1) PF_MF(c21, a5, b3) PF_MF(c30, a7, b1) PF_MF(c31, a7, b3)
+            "s_nop 7\n s_nop 7\n s_nop 3"
+            : [c00] "+v"(acc[0][0]), [c01] "+v"(acc[0][1]), [c10] "+v"(acc[1][0]), [c11] "+v"(acc[1][1]),
+              [c20] "+v"(acc[2][0]), [c21] "+v"(acc[2][1]), [c30] "+v"(acc[3][0]), [c31] "+v"(acc[3][1])
+            : [a0] "v"(c.a[0]), [a1] "v"(c.a[1]), [a2] "v"(c.a[2]), [a3] "v"(c.a[3]),
+              [a4] "v"(c.a[4]), [a5] "v"(c.a[5]), [a6] "v"(c.a[6]), [a7] "v"(c.a[7]),
+              [b0] "v"(c.b[0]), [b1] "v"(c.b[1]), [b2] "v"(c.b[2]), [b3] "v"(c.b[3]));
+    } else {
+        asm volatile(
+            "s_nop 1\n"
+            PF_MF(c0, a0, b0) PF_MF(c1, a2, b0) PF_MF(c2, a4, b0) PF_MF(c3, a6, b0)
+            PF_MF(c0, a1, b1) PF_MF(c1, a3, b1) PF_MF(c2, a5, b1) PF_MF(c3, a7, b1)
+            "s_nop 7\n s_nop 7\n s_nop 3"
+            : [c0] "+v"(acc[0][0]), [c1] "+v"(acc[1][0]), [c2] "+v"(acc[2][0]), [c3] "+v"(acc[3][0])
+            : [a0] "v"(c.a[0]), [a1] "v"(c.a[1]), [a2] "v"(c.a[2]), [a3] "v"(c.a[3]),
+              [a4] "v"(c.a[4]), [a5] "v"(c.a[5]), [a6] "v"(c.a[6]), [a7] "v"(c.a[7]),
+              [b0] "v"(c.b[0]), [b1] "v"(c.b[1]));
+    }
+}
+
+#undef PF_RD
+#undef PF_MF
+
+// One 256 x 64 WJ output tile of problem P (tile `local`, token tiles fastest)
+// by eight waves in a 2 x 4 grid: wave (wn, wm) owns rows 128 wn .. + 127 and
+// tokens 32 JB wm .. + 32 JB - 1 (JB = WJ / 2 blocks of 32): 4 x JB
+// accumulator blocks of 32 x 32.  Stage s (k-blocks 2 s, 2 s + 1 of this
+// split) sits in ring slot s % NS: weight fragments 0 .. 31, then token
+// fragments 0 .. 8 WJ - 1; wave w copies fragments w + 8 h of each.
+// Iteration g:
+//   k-block 2 g: read k-block 2 g + 1 from stage g, MFMAs of 2 g;
+//   wait for this wave's copies of stage g + 1; barrier (stage g + 1
+//   published, stage g read by all); copy stage g + NS into stage g's slot;
+//   k-block 2 g + 1: read k-block 2 g + 2 from stage g + 1, MFMAs of 2 g + 1.
+// Every iteration issues the same copies (k-blocks past the end are clamped
+// to the last one and land in free slots, never read), so every wait is a
+// constant.  An odd k-block count leaves the last stage one k-block.
+template <int WJ>
+__device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int kidx)
+{
+    constexpr int NW = kTiledWaves;
+    constexpr int NS = WJ == 4 ? 2 : 3;                 // ring stages: 128 or 144 KB
+    constexpr int JB = WJ / 2;
+    constexpr int kFa = 32, kFb = 8 * WJ;                // fragments per stage
+    constexpr int kStage = (kFa + kFb) * 1024;
+    constexpr int ka = kFa / NW, kb = kFb / NW;          // copies per wave per stage
+    constexpr int kOps = ka + kb;
+    static_assert(WJ == 2 || WJ == 4, "tile width");
+    static_assert((NS - 1) * kOps <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) int8_t ring[NS * kStage];
+    __shared__ __attribute__((aligned(16))) int8_t zero_b[JB * 32 * 128];   // the wave's token blocks, zeros
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tm = local % P.tiles_m, tn = local / P.tiles_m;
+    const int n0 = tn * 256, t0 = tm * 64 * WJ;
+    const int kb0 = kidx * P.kb_per_split;
+    const int nkb = min(P.kb_per_split, (P.K >> 6) - kb0);
+    const int nst = (nkb + 1) >> 1;
+    if (threadIdx.x < JB * 256) reinterpret_cast<v4i*>(zero_b)[threadIdx.x] = v4i{};   // 16 bytes each
+    __syncthreads();
+    // copies: lane l of fragment f takes row 8 f + l / 8 and the piece that
+    // belongs at position l % 8: p = (l % 8) ^ (l / 8) ^ (f % 2), f % 2 being
+    // the wave's parity for all of its fragments; piece p is byte 16 (p % 4) of
+    // k-block p / 4 of the stage
+    const int crow = lane >> 3;
+    const int pc = (lane & 7) ^ crow ^ (wave & 1);
+    const int phalf = pc >> 2;
+    const int pof = (pc & 3) << 4;
+    const int8_t* asrc[ka];
+#pragma unroll
+    for (int h = 0; h < ka; ++h)
+        asrc[h] = P.W + (int64_t)min(n0 + 8 * (wave + NW * h) + crow, P.N - 1) * P.K + (int64_t)kb0 * 64 + pof;
+    const int8_t* bsrc[kb];
+#pragma unroll
+    for (int h = 0; h < kb; ++h)
+        bsrc[h] = P.X + (int64_t)min(t0 + 8 * (wave + NW * h) + crow, P.M - 1) * P.ldx + (int64_t)kb0 * 64 + pof;
+    const uint32_t ring0 = lds_addr(ring);
+
+    auto put = [&](int s) {
+        int8_t* slot = ring + (s % NS) * kStage;
+        const int64_t ko = (int64_t)min(2 * s + phalf, nkb - 1) * 64;
+#pragma unroll
+        for (int h = 0; h < ka; ++h) dma16(asrc[h] + ko, slot + (wave + NW * h) * 1024);
+#pragma unroll
+        for (int h = 0; h < kb; ++h) dma16(bsrc[h] + ko, slot + (kFa + wave + NW * h) * 1024);
+    };
+
+    // operand reads: lane l, row (or token) r = l % 32 of a 32-row block and
+    // half h = l / 32 reads piece 2 q + h of k quarter q (0 .. 3 over the
+    // stage) at 128 r + 16 ((2 q + h) ^ s(r)) = 128 r + (16 (h ^ s(r)) ^ 32 q)
+    const int r = lane & 31;
+    const int sr = (r & 7) ^ ((r >> 3) & 1);
+    const uint32_t lo = (uint32_t)(128 * r + 16 * ((lane >> 5) ^ sr));
+    const int wn = wave >> 2, wm = wave & 3;
+    // the wave's weight rows start at 128 wn rows, its tokens at token block
+    // JB wm; both offsets keep bits 5 and 6 clear, so quarter q is x ^ 32 q
+    const uint32_t xa = (uint32_t)(wn * 128 * 128) + lo;
+    const uint32_t xb = (uint32_t)(kFa * 1024 + wm * JB * 32 * 128) + lo;
+    auto ra = [&](uint32_t so, int q) { return ring0 + so + (xa ^ (uint32_t)(32 * q)); };
+    auto rb = [&](uint32_t so, int q) { return ring0 + so + (xb ^ (uint32_t)(32 * q)); };
+
+    v16i acc[4][JB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < JB; ++j) acc[i][j] = v16i{};
+
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        put(s);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+    wait_vmcnt<(NS - 1) * kOps>();                       // own copies of stage 0
+    stage_barrier();
+    KbOps<JB> c0, c1;
+    kb_read<JB>(c0, ra(0, 0), ra(0, 1), rb(0, 0), rb(0, 1));
+
+    for (int g = 0; g + 1 < nst; ++g) {
+        const uint32_t so = (uint32_t)((g % NS) * kStage), sn = (uint32_t)(((g + 1) % NS) * kStage);
+        kb_step<JB>(c1, c0, acc, ra(so, 2), ra(so, 3), rb(so, 2), rb(so, 3));
+        wait_vmcnt<(NS - 2) * kOps>();                   // own copies of stage g + 1
+        stage_barrier();                                 // stage g + 1 published; stage g read by all
+        put(g + NS);                                     // into the slot of stage g
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        kb_step<JB>(c0, c1, acc, ra(sn, 0), ra(sn, 1), rb(sn, 0), rb(sn, 1));
+    }
+    // the last stage: with an odd k-block count its second k-block reads
+    // the token operands from a zeroed block, so it adds nothing
+    {
+        const uint32_t so = (uint32_t)(((nst - 1) % NS) * kStage);
+        const bool two = 2 * nst == nkb;
+        const uint32_t z = lds_addr(zero_b) + lo;
+        kb_step<JB>(c1, c0, acc, ra(so, 2), ra(so, 3), two ? rb(so, 2) : z, two ? rb(so, 3) : z);
+        kb_last<JB>(c1, acc);
+    }
+    wait_vmcnt<0>();                                     // no copy outlives the workgroup's LDS
+    static_assert(64 * WJ * 512 <= NS * kStage, "a pass fits in the ring");
+    tiled_store<WJ, NW>(P, ring, n0, t0, kidx, acc, wn, wm, lane);
+}
+
 // Workgroup b -> tile (b % 8) * per_xcd + b / 8: the workgroups of one XCD take
 // a contiguous range of tiles.  The grid is 8 per_xcd; indices past the last
 // tile return at once.
@@ -372,9 +389,6 @@ __device__ __forceinline__ int xcd_tile(int per_xcd)
 {
     return ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
 }
-
-// Waves per tiled workgroup (see tiled_block).
-constexpr int kTiledWaves = 8;
 
 // A work unit is (tile, K split), splits fastest.
 template <int WJ>
@@ -385,7 +399,7 @@ void k_gemm_tiled(GemmSet set, int per_xcd)
     if (j >= set.total_tiles) return;
     const GemmProb P = find_prob(set, j);
     const int u = j - P.tile_begin;
-    tiled_block<WJ, kTiledWaves>(P, u / P.splits, u % P.splits);
+    tiled_block<WJ>(P, u / P.splits, u % P.splits);
 }
 
 // Stack step: with S.partials the K range is split S.splits ways and each unit
@@ -405,7 +419,7 @@ void k_gemm_tiled_step(StackStep S, int per_xcd)
         P.acc_ld = S.ldp;
         P.acc_split = S.part_stride;
     }
-    tiled_block<WJ, kTiledWaves>(P, local, j % S.splits);
+    tiled_block<WJ>(P, local, j % S.splits);
 }
 
 int tiled_tokens(int64_t M) { return M > 128 ? 256 : 128; }
