@@ -198,8 +198,9 @@ typedef struct {
 typedef struct {
     int time_kernels;          /* in: 1 = time every launch                       */
     int max_groups;            /* in: at most this many chunk groups (0: the library's
-                                  choice, 3); 1 runs every launch in order on the
-                                  caller's stream, so no two launches overlap      */
+                                  choice: 3 for chunks of up to 64 tokens, 1 above);
+                                  1 runs every launch in order on the caller's
+                                  stream, so no two launches overlap               */
     int groups;                /* out: chunk groups used                          */
     int per_token_mode;        /* out: 1 if the per-token GEMV path ran           */
     int64_t chunks;            /* chunks processed (the last may be ragged)       */
