@@ -46,6 +46,11 @@
  *     reentrant.
  *   - K of every product must be a positive multiple of 64 and at most 131072,
  *     which keeps every int32 accumulator exact (131072 * 127 * 127 < 2^31).
+ *   - A weight matrix (N x K) and a chunk of quantised tokens (M x K) must each
+ *     hold fewer than 2^32 bytes (the product kernels address them by 32-bit
+ *     offsets): pf_gemm_i8_chunk checks N * K and M * K, pf_prefill_stack
+ *     hidden * ffn and chunk * max(hidden, ffn); larger ones are rejected with
+ *     PF_EINVAL.
  *
  * Arithmetic (bit-exact with the plain per-token CPU definition):
  *   quantise:  amax = max_k |x_k|; s = fl(amax / 127); q_k = clamp(roundf(fl(x_k / s)),

@@ -374,6 +374,7 @@ pf_status validate_stack(const pf_stack* st)
             return PF_EINVAL;
     }
     if (!valid_k(st->hidden) || !valid_k(st->ffn)) return PF_EINVAL;
+    if ((uint64_t)st->hidden * (uint64_t)st->ffn >= (1ull << 32)) return PF_EINVAL;   // 32-bit offsets
     for (const pf_layer* tab : {st->layers, st->layers_alt}) {
         if (!tab) continue;
         for (int64_t l = 0; l < st->n_layers; ++l)
@@ -1111,6 +1112,8 @@ pf_status check_chunk_args(const int8_t* W, const float* w_scale, int64_t N, int
                            const int8_t* xq, const float* a_scale, int64_t M, const float* y)
 {
     if (N <= 0 || N > INT32_MAX || !valid_k(K) || M < 0 || M > INT32_MAX) return PF_EINVAL;
+    // the tiled kernel addresses a matrix by 32-bit offsets
+    if ((uint64_t)N * (uint64_t)K >= (1ull << 32) || (uint64_t)M * (uint64_t)K >= (1ull << 32)) return PF_EINVAL;
     if (M == 0) return PF_OK;
     if (!W || !w_scale || !xq || !a_scale || !y) return PF_EINVAL;
     if (!aligned16(W) || !aligned4(w_scale) || !aligned16(xq) || !aligned4(a_scale) || !aligned4(y))
@@ -1609,6 +1612,7 @@ pf_status pf_prefill_stack(const pf_stack* stack, const float* x, int64_t P, int
                      overlap(kv, kb, proj, pb)))
             return PF_EINVAL;
         const int64_t ch = std::min(chunk, P);
+        if ((uint64_t)ch * (uint64_t)std::max(H, F) >= (1ull << 32)) return PF_EINVAL;   // 32-bit offsets
         const StackLayout lay = stack_layout(L, H, F, ch, attn);
         if (!workspace || ws_bytes < lay.total) return PF_EWORKSPACE;
         if (!aligned16(workspace)) return PF_EINVAL;

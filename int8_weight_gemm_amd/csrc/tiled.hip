@@ -12,8 +12,9 @@
 //    bytes, so every copy instruction reads whole 128-byte lines (whose
 //    requests the memory path serves ~30% faster than 64-byte ones); pieces
 //    are swizzled so that the MFMA operand reads (one ds_read_b128 each) are
-//    conflict-free; a ring of two (256 tokens) or three (128 tokens) stages,
-//    one barrier per stage;
+//    conflict-free; the weights sit in a ring of three (256 tokens) or four
+//    (128 tokens) stage slots, the tokens in a ring of two, 160 KB in all, one
+//    barrier per stage;
 //  * each k-block's LDS operand reads for the next k-block are issued between
 //    this k-block's MFMAs and waited for inside the same asm block, so no LDS
 //    load is ever in flight outside the code that issued it;
@@ -42,14 +43,13 @@ constexpr int kTiledWaves = 8;
 // 512-byte token rows, 32 lanes per token.  (Each lane storing its own 16-byte
 // pieces, 64 tokens per instruction, cost ~20% of the 7B prompt's time.)
 template <int WJ, int NW>
-__device__ __forceinline__ void tiled_store(const GemmProb& P, int8_t* ring, int n0, int t0,
+__device__ __forceinline__ void tiled_store(const GemmProb& P, int8_t* ring, float* sws, float* sxs, int n0, int t0,
                                             int kidx, v16i (&acc)[4][2 * WJ / (NW / 2)], int wn, int wm, int lane)
 {
     constexpr int JB = 2 * WJ / (NW / 2);
     const int lrow = lane & 31;
     const bool split = P.splits > 1;
     int* const part = split ? P.acc + (int64_t)kidx * P.acc_split : nullptr;
-    __shared__ float sws[256], sxs[256];
     if (!split) {
         const int t = (int)threadIdx.x;
         if (t < 256) sws[t] = P.ws[min(n0 + t, P.N - 1)];
@@ -268,31 +268,38 @@ __device__ __forceinline__ void kb_last(const KbOps<JB>& c, v16i (&acc)[4][JB])
 // One 256 x 64 WJ output tile of problem P (tile `local`, token tiles fastest)
 // by eight waves in a 2 x 4 grid: wave (wn, wm) owns rows 128 wn .. + 127 and
 // tokens 32 JB wm .. + 32 JB - 1 (JB = WJ / 2 blocks of 32): 4 x JB
-// accumulator blocks of 32 x 32.  Stage s (k-blocks 2 s, 2 s + 1 of this
-// split) sits in ring slot s % NS: weight fragments 0 .. 31, then token
-// fragments 0 .. 8 WJ - 1; wave w copies fragments w + 8 h of each.
-// Iteration g:
-//   k-block 2 g: read k-block 2 g + 1 from stage g, MFMAs of 2 g;
+// accumulator blocks of 32 x 32.  Stage s is k-blocks 2 s, 2 s + 1 of this
+// split, held in two rings: the weights in NSW slots of 32 KB (fragments
+// 0 .. 31), copied NSW - 1 stages ahead, the tokens in NST slots of 8 WJ KB
+// (fragments 0 .. 8 WJ - 1), copied NST - 1 ahead, 160 KB in all; wave w
+// copies fragments w + 8 h of each.  The weights come from HBM or the
+// Infinity Cache, the tokens mostly from L2, so the weights get the longer
+// lead (three weight slots against two: the 7B prompt 16.7 -> 16.2 ms,
+// 38400 x 4096 x 512 143 -> 134 us).  Iteration g:
+//   k-block 2 g: read k-block 2 g + 1 of stage g, MFMAs of 2 g;
 //   wait for this wave's copies of stage g + 1; barrier (stage g + 1
-//   published, stage g read by all); copy stage g + NS into stage g's slot;
-//   k-block 2 g + 1: read k-block 2 g + 2 from stage g + 1, MFMAs of 2 g + 1.
-// Every iteration issues the same copies (k-blocks past the end are clamped
-// to the last one and land in free slots, never read), so every wait is a
-// constant.  An odd k-block count leaves the last stage one k-block.
+//   published, stage g read by all); copy the tokens of stage g + NST, then
+//   the weights of stage g + NSW, into stage g's slots;
+//   k-block 2 g + 1: read k-block 2 g + 2 of stage g + 1, MFMAs of 2 g + 1.
+// Tokens before weights: waiting for the tokens of stage g + 1 leaves only
+// the newest weights in flight, and the weights of stage g + 1, copied
+// earlier, have landed too.  Every iteration issues the same copies (k-blocks
+// past the end are clamped to the last one and land in free slots, never
+// read), so every wait is a constant.
 template <int WJ>
 __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int kidx)
 {
     constexpr int NW = kTiledWaves;
-    constexpr int NS = WJ == 4 ? 2 : 3;                 // ring stages: 128 or 144 KB
+    constexpr int NSW = WJ == 4 ? 3 : 4, NST = 2;
     constexpr int JB = WJ / 2;
     constexpr int kFa = 32, kFb = 8 * WJ;                // fragments per stage
-    constexpr int kStage = (kFa + kFb) * 1024;
+    constexpr int kWst = kFa * 1024, kTst = kFb * 1024;
     constexpr int ka = kFa / NW, kb = kFb / NW;          // copies per wave per stage
-    constexpr int kOps = ka + kb;
-    static_assert(WJ == 2 || WJ == 4, "tile width");
-    static_assert((NS - 1) * kOps <= 63, "vmcnt range");
-    __shared__ __attribute__((aligned(16))) int8_t ring[NS * kStage];
-    __shared__ __attribute__((aligned(16))) int8_t zero_b[JB * 32 * 128];   // the wave's token blocks, zeros
+    constexpr int kRing = NSW * kWst + NST * kTst;
+    static_assert(kRing <= 160 * 1024, "LDS");
+    static_assert(ka + (NST - 1) * (ka + kb) <= 63, "vmcnt range");
+    static_assert(64 * WJ * 512 + 2048 <= kRing, "a pass and the scales fit in the ring");
+    __shared__ __attribute__((aligned(16))) int8_t ring[kRing];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int tm = local % P.tiles_m, tn = local / P.tiles_m;
@@ -300,48 +307,43 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
     const int kb0 = kidx * P.kb_per_split;
     const int nkb = min(P.kb_per_split, (P.K >> 6) - kb0);
     const int nst = (nkb + 1) >> 1;
-    if (threadIdx.x < JB * 256) reinterpret_cast<v4i*>(zero_b)[threadIdx.x] = v4i{};   // 16 bytes each
-    __syncthreads();
-    // copies: lane l of fragment f takes row 8 f + l / 8 and the piece that
-    // belongs at position l % 8: p = (l % 8) ^ (l / 8) ^ (f % 2), f % 2 being
-    // the wave's parity for all of its fragments; piece p is byte 16 (p % 4) of
-    // k-block p / 4 of the stage
     const int crow = lane >> 3;
     const int pc = (lane & 7) ^ crow ^ (wave & 1);
     const int phalf = pc >> 2;
     const int pof = (pc & 3) << 4;
-    const int8_t* asrc[ka];
+    // 32-bit offsets from the matrices' bases (weights and tokens are each
+    // under 2 GiB), so a copy's address is one register plus a uniform base
+    uint32_t aoff[ka], boff[kb];
 #pragma unroll
     for (int h = 0; h < ka; ++h)
-        asrc[h] = P.W + (int64_t)min(n0 + 8 * (wave + NW * h) + crow, P.N - 1) * P.K + (int64_t)kb0 * 64 + pof;
-    const int8_t* bsrc[kb];
+        aoff[h] = (uint32_t)min(n0 + 8 * (wave + NW * h) + crow, P.N - 1) * (uint32_t)P.K + (uint32_t)(kb0 * 64 + pof);
 #pragma unroll
     for (int h = 0; h < kb; ++h)
-        bsrc[h] = P.X + (int64_t)min(t0 + 8 * (wave + NW * h) + crow, P.M - 1) * P.ldx + (int64_t)kb0 * 64 + pof;
+        boff[h] = (uint32_t)min(t0 + 8 * (wave + NW * h) + crow, P.M - 1) * (uint32_t)P.ldx + (uint32_t)(kb0 * 64 + pof);
     const uint32_t ring0 = lds_addr(ring);
+    int8_t* const tring = ring + NSW * kWst;
 
-    auto put = [&](int s) {
-        int8_t* slot = ring + (s % NS) * kStage;
-        const int64_t ko = (int64_t)min(2 * s + phalf, nkb - 1) * 64;
+    auto put_w = [&](int s) {
+        int8_t* slot = ring + (s % NSW) * kWst;
+        const uint32_t ko = (uint32_t)min(2 * s + phalf, nkb - 1) * 64u;
 #pragma unroll
-        for (int h = 0; h < ka; ++h) dma16(asrc[h] + ko, slot + (wave + NW * h) * 1024);
+        for (int h = 0; h < ka; ++h) dma16(P.W + (aoff[h] + ko), slot + (wave + NW * h) * 1024);
+    };
+    auto put_t = [&](int s) {
+        int8_t* slot = tring + (s % NST) * kTst;
+        const uint32_t ko = (uint32_t)min(2 * s + phalf, nkb - 1) * 64u;
 #pragma unroll
-        for (int h = 0; h < kb; ++h) dma16(bsrc[h] + ko, slot + (kFa + wave + NW * h) * 1024);
+        for (int h = 0; h < kb; ++h) dma16(P.X + (boff[h] + ko), slot + (wave + NW * h) * 1024);
     };
 
-    // operand reads: lane l, row (or token) r = l % 32 of a 32-row block and
-    // half h = l / 32 reads piece 2 q + h of k quarter q (0 .. 3 over the
-    // stage) at 128 r + 16 ((2 q + h) ^ s(r)) = 128 r + (16 (h ^ s(r)) ^ 32 q)
     const int r = lane & 31;
     const int sr = (r & 7) ^ ((r >> 3) & 1);
     const uint32_t lo = (uint32_t)(128 * r + 16 * ((lane >> 5) ^ sr));
     const int wn = wave >> 2, wm = wave & 3;
-    // the wave's weight rows start at 128 wn rows, its tokens at token block
-    // JB wm; both offsets keep bits 5 and 6 clear, so quarter q is x ^ 32 q
     const uint32_t xa = (uint32_t)(wn * 128 * 128) + lo;
-    const uint32_t xb = (uint32_t)(kFa * 1024 + wm * JB * 32 * 128) + lo;
-    auto ra = [&](uint32_t so, int q) { return ring0 + so + (xa ^ (uint32_t)(32 * q)); };
-    auto rb = [&](uint32_t so, int q) { return ring0 + so + (xb ^ (uint32_t)(32 * q)); };
+    const uint32_t xb = (uint32_t)(NSW * kWst + wm * JB * 32 * 128) + lo;
+    auto ra = [&](int s, int q) { return ring0 + (uint32_t)((s % NSW) * kWst) + (xa ^ (uint32_t)(32 * q)); };
+    auto rb = [&](int s, int q) { return ring0 + (uint32_t)((s % NST) * kTst) + (xb ^ (uint32_t)(32 * q)); };
 
     v16i acc[4][JB];
 #pragma unroll
@@ -349,37 +351,44 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
 #pragma unroll
         for (int j = 0; j < JB; ++j) acc[i][j] = v16i{};
 
+    // the copies of iterations -NSW .. -1
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        put(s);
+    for (int g = -NSW; g < 0; ++g) {
+        if (g + NST >= 0) put_t(g + NST);
+        put_w(g + NSW);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
-    wait_vmcnt<(NS - 1) * kOps>();                       // own copies of stage 0
+    wait_vmcnt<ka + (NST - 1) * (ka + kb)>();            // own copies of stage 0
     stage_barrier();
     KbOps<JB> c0, c1;
     kb_read<JB>(c0, ra(0, 0), ra(0, 1), rb(0, 0), rb(0, 1));
 
     for (int g = 0; g + 1 < nst; ++g) {
-        const uint32_t so = (uint32_t)((g % NS) * kStage), sn = (uint32_t)(((g + 1) % NS) * kStage);
-        kb_step<JB>(c1, c0, acc, ra(so, 2), ra(so, 3), rb(so, 2), rb(so, 3));
-        wait_vmcnt<(NS - 2) * kOps>();                   // own copies of stage g + 1
+        kb_step<JB>(c1, c0, acc, ra(g, 2), ra(g, 3), rb(g, 2), rb(g, 3));
+        wait_vmcnt<ka + (NST - 2) * (ka + kb)>();        // own copies of stage g + 1
         stage_barrier();                                 // stage g + 1 published; stage g read by all
-        put(g + NS);                                     // into the slot of stage g
+        put_t(g + NST);                                  // into the slots of stage g
+        put_w(g + NSW);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        kb_step<JB>(c0, c1, acc, ra(sn, 0), ra(sn, 1), rb(sn, 0), rb(sn, 1));
+        kb_step<JB>(c0, c1, acc, ra(g + 1, 0), ra(g + 1, 1), rb(g + 1, 0), rb(g + 1, 1));
     }
-    // the last stage: with an odd k-block count its second k-block reads
-    // the token operands from a zeroed block, so it adds nothing
+    // the last stage: with an odd k-block count its second k-block's token
+    // operands are replaced by zeros, so it adds nothing
     {
-        const uint32_t so = (uint32_t)(((nst - 1) % NS) * kStage);
-        const bool two = 2 * nst == nkb;
-        const uint32_t z = lds_addr(zero_b) + lo;
-        kb_step<JB>(c1, c0, acc, ra(so, 2), ra(so, 3), two ? rb(so, 2) : z, two ? rb(so, 3) : z);
+        const int g = nst - 1;
+        kb_step<JB>(c1, c0, acc, ra(g, 2), ra(g, 3), rb(g, 2), rb(g, 3));
+        if (2 * nst != nkb) {
+#pragma unroll
+            for (int j = 0; j < 2 * JB; ++j) c1.b[j] = v4i{0, 0, 0, 0};
+        }
         kb_last<JB>(c1, acc);
     }
     wait_vmcnt<0>();                                     // no copy outlives the workgroup's LDS
-    static_assert(64 * WJ * 512 <= NS * kStage, "a pass fits in the ring");
-    tiled_store<WJ, NW>(P, ring, n0, t0, kidx, acc, wn, wm, lane);
+    // the scales go into the token ring: every wave's copies have landed and
+    // every wave has read its last operands before any wave writes there
+    __syncthreads();
+    float* sws = reinterpret_cast<float*>(ring + 64 * WJ * 512);
+    tiled_store<WJ, NW>(P, ring, sws, sws + 256, n0, t0, kidx, acc, wn, wm, lane);
 }
 
 // Workgroup b -> tile (b % 8) * per_xcd + b / 8: the workgroups of one XCD take
@@ -428,6 +437,10 @@ hipError_t launch_gemm_tiled(const GemmSet& set, int tile_tokens, hipStream_t s)
 {
     if (set.total_tiles <= 0) return hipSuccess;
     if (tile_tokens != 256 && tile_tokens != 128) return hipErrorInvalidValue;
+    for (int i = 0; i < set.nprob; ++i)                  // 32-bit copy offsets
+        if ((uint64_t)set.p[i].N * (uint64_t)set.p[i].K >= (1ull << 32) ||
+            (uint64_t)set.p[i].M * (uint64_t)set.p[i].ldx >= (1ull << 32))
+            return hipErrorInvalidValue;
     const int per_xcd = (set.total_tiles + 7) / 8;
     const dim3 g(8 * per_xcd), b(64 * kTiledWaves);
     if (tile_tokens == 256) PF_LAUNCH((k_gemm_tiled<4>), g, b, 0, s, set, per_xcd);
@@ -440,6 +453,9 @@ hipError_t launch_gemm_tiled(const GemmSet& set, int tile_tokens, hipStream_t s)
 hipError_t launch_gemm_tiled_step(const StackStep& S, int64_t M, hipStream_t s)
 {
     if (S.splits < 1 || (S.splits > 1 && !S.partials)) return hipErrorInvalidValue;
+    for (int j = 0; j < S.nproj; ++j)                    // 32-bit copy offsets
+        if ((uint64_t)S.rows[j] * (uint64_t)S.K >= (1ull << 32)) return hipErrorInvalidValue;
+    if ((uint64_t)M * (uint64_t)S.ldx >= (1ull << 32)) return hipErrorInvalidValue;
     const int tiles = S.npairs * S.tile_off[S.nproj] * S.splits;
     if (tiles <= 0) return hipSuccess;
     const int per_xcd = (tiles + 7) / 8;

@@ -248,6 +248,34 @@ def test_sweep4096_chunks_match_oracle_and_each_other():
         np.testing.assert_array_equal(host(y), ref[:M])
 
 
+@pytest.mark.parametrize("N,K,M", [(38400, 4096, 512), (16384, 16384, 320), (11008, 4096, 200)])
+def test_large_tiled_products_equal_per_token_gemvs(N, K, M):
+    """Products of hundreds of tiles (several rounds of workgroups per compute
+    unit): every output of the chunk product equals the per-token GEMV's
+    (both bit-exact definitions of the same arithmetic, "Batched Prefill",
+    §Correctness), and sampled rows equal the oracle's."""
+    say("large tiled", N, K, M)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(N + K + M)
+    W = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+    ws = torch.rand(N, device="cuda", generator=g) * 0.009 + 0.001
+    x = torch.randn(M, K, device="cuda", generator=g)
+    q, s = pf.quantize_act(x)
+    wsp = pf.workspace(max(1, pf.gemm_i8_chunk_workspace(N, K, M)))
+    y = pf.gemm_i8_chunk(W, ws, q, s, ws=wsp)
+    y2 = pf.gemm_i8_chunk(W, ws, q, s, ws=wsp)            # the same call again
+    per = torch.empty_like(y)
+    for t in range(M):
+        pf.gemv_i8(W, ws, q[t].contiguous(), s[t:t + 1].contiguous(), out=per[t])
+    torch.cuda.synchronize()
+    assert torch.equal(y, per)
+    assert torch.equal(y, y2)
+    rows = np.unique(np.concatenate([np.arange(0, N, 997), [N - 1]]))
+    Wh = host(W)[rows]
+    ref = oracle.linear(Wh, host(ws)[rows], host(q), host(s))
+    np.testing.assert_array_equal(host(y)[:, rows], ref)
+
+
 def test_rejects_bad_arguments_without_launch():
     W = torch.zeros((64, 100), dtype=torch.int8, device="cuda")
     with pytest.raises(pf.PrefillError) as e:
