@@ -203,7 +203,7 @@ typedef struct {
 typedef struct {
     int time_kernels;          /* in: 1 = time every launch                       */
     int max_groups;            /* in: at most this many chunk groups (0: the library's
-                                  choice: 3 for chunks of up to 64 tokens, 1 above);
+                                  choice: 3 for chunks of up to 64 tokens, 2 above);
                                   1 runs every launch in order on the caller's
                                   stream, so no two launches overlap               */
     int groups;                /* out: chunk groups used                          */

@@ -325,22 +325,28 @@ constexpr int kMaxGroups = 4;
 constexpr int kStackGroups = 3;
 constexpr int kGroupSlots = 16;
 constexpr int kGroupSlotsTiled = 4;  // chunks over 64 tokens: each product fills the chip
+constexpr int kTiledGroups = 2;      // chunk groups over 64 tokens
 static_assert(kStackGroups <= kMaxGroups && kGroupSlots <= kMaxPairs, "stack sweep shape");
+static_assert(kTiledGroups <= kStackGroups, "a stream per group");
 
 StackLayout stack_layout(int64_t L, int64_t H, int64_t F, int64_t chunk, bool attn)
 {
     StackLayout S{};
-    // chunks over 64 tokens: one group, whose launches then carry up to four
-    // chunks' tiles (the 7B-class prompt at 512 tokens: 16.5 ms against 16.9 ms
-    // in three groups, whose launches carry one or two)
-    S.groups = chunk <= 64 ? kStackGroups : 1;
+    // chunks over 64 tokens: two groups, whose launches each carry up to two of
+    // the 7B-class prompt's four 512-token chunks.  Every tile of a launch ends
+    // at about the same time and then stores its 256 KB of outputs, so in one
+    // group all compute units wait on the same burst of stores; two groups on
+    // two streams run their launches out of phase (the prompt in 15.65 ms
+    // against 16.25 ms in one group and 16.36 ms in three, on one box).
+    S.groups = chunk <= 64 ? kStackGroups : kTiledGroups;
     S.gslots = (int)std::min<int64_t>(L, chunk <= 64 ? kGroupSlots : kGroupSlotsTiled);
     S.slots = S.groups * S.gslots;
     // down-product K splits: on the skinny path at most 16 k-blocks (the
     // token slice in LDS) each.  On the tiled path two, when a group's down
     // launch (gslots chunks of 256-row x tile-width tiles) would leave compute
-    // units idle: the 7B-class stack at 512 tokens, 128 tiles, ran its prompt
-    // in 16.9 ms split in two against 17.2 ms unsplit and 17.9 ms in four.
+    // units idle: the 7B-class stack at 512 tokens in two groups ran its
+    // prompt in 15.65 ms split in two against 16.26 ms unsplit and 16.64 ms
+    // in four.
     const int nkb = (int)(F / 64);
     const int64_t down_tiles = S.gslots * ((H + kTiledRows - 1) / kTiledRows) *
                                ((chunk + tiled_tokens(chunk) - 1) / tiled_tokens(chunk));
