@@ -28,6 +28,13 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt with only the LDS counter limited to 0 (vmcnt and expcnt at their
+// maxima): this wave's LDS reads and writes have completed.
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
 // Workgroup barrier without the memory fence of __syncthreads (which would wait
 // for every outstanding load, draining the DMA pipeline).  Completion of this
 // wave's DMAs is established by wait_vmcnt before it; the signal fences keep

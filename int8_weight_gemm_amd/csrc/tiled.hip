@@ -22,7 +22,7 @@
 //    tiles of one band of weight rows are consecutive, so the band is fetched
 //    from HBM once into that XCD's L2 and shared.
 // Epilogue: y[t][n] = fl(fl(acc) * fl(ws[n] * xs[t])), written through LDS as
-// whole 512-byte token rows; split products write int32 partials instead.
+// 256-byte runs of token rows; split products write int32 partials instead.
 #include "device.hpp"
 #include "kernels.hpp"
 #include "lds_dma.hpp"
@@ -37,11 +37,15 @@ constexpr int kTiledWaves = 8;
 // token l % 32, row 8 q + 4 (l / 32) + r.  Split: this split's int32
 // partials; unsplit: y = fl(fl(acc) * fl(ws * xs)) with the tile's scales
 // staged once in LDS.  The tile leaves through the (now idle) ring in two
-// passes, rows 128 h .. + 127 in pass h: the waves of that row half write
-// their values as [token][128 rows], the 16-byte piece of rows 4 g .. 4 g + 3
-// of token u at 512 u + 16 (g ^ (u % 32)), then every thread stores whole
-// 512-byte token rows, 32 lanes per token.  (Each lane storing its own 16-byte
-// pieces, 64 tokens per instruction, cost ~20% of the 7B prompt's time.)
+// passes of 128 rows; in pass h every wave writes its row blocks 2 h and
+// 2 h + 1 (rows 128 wn + 64 h .. + 63), so all the waves work in both passes
+// (passes by row half, which left half the waves idle, took 12.9 against
+// 10.3 us per tile).  LDS row of token u: pass row rr = 64 wn + 32 (i - 2 h) +
+// 8 q + 4 (l / 32) + r, its 16-byte piece g = rr / 4 at 512 u + 16 (g ^ (u % 32));
+// pass row rr is weight row n0 + 128 (rr / 64) + 64 h + rr % 64.  Then every
+// thread stores 16-byte pieces of two 256-byte row runs per token, 16 lanes
+// per run.  (Each lane storing its own 16-byte pieces, 64 tokens per
+// instruction, cost ~20% of the 7B prompt's time.)
 template <int WJ, int NW>
 __device__ __forceinline__ void tiled_store(const GemmProb& P, int8_t* ring, float* sws, float* sxs, int n0, int t0,
                                             int kidx, v16i (&acc)[4][2 * WJ / (NW / 2)], int wn, int wm, int lane)
@@ -62,31 +66,32 @@ __device__ __forceinline__ void tiled_store(const GemmProb& P, int8_t* ring, flo
     constexpr int kPieces = 64 * WJ * 32;                // 16-byte pieces per pass
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        if (wn == h) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * h + ii;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+            for (int j = 0; j < JB; ++j) {
+                const int tl = wm * 32 * JB + 32 * j + lrow;         // token in the tile
+                const float xs = sxs[tl];
 #pragma unroll
-                    for (int j = 0; j < JB; ++j) {
-                        const int g4 = 8 * i + 2 * q + (lane >> 5);          // rows 4 g4 .. + 3 of the half
-                        const int tl = wm * 32 * JB + 32 * j + lrow;         // token in the tile
-                        v4i val = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                        if (!split) {
-                            const float4 w4 = *reinterpret_cast<const float4*>(sws + 128 * h + 4 * g4);
-                            const float xs = sxs[tl];
-                            val = v4i{__float_as_int(epilogue(val[0], w4.x, xs)), __float_as_int(epilogue(val[1], w4.y, xs)),
-                                      __float_as_int(epilogue(val[2], w4.z, xs)), __float_as_int(epilogue(val[3], w4.w, xs))};
-                        }
-                        *reinterpret_cast<v4i*>(ring + tl * 512 + 16 * (g4 ^ (tl & 31))) = val;
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    const int g4 = 16 * wn + 8 * ii + 2 * q + (lane >> 5);
+                    const int nl = 128 * wn + 32 * i + 8 * q + 4 * (lane >> 5);   // row in the tile
+                    const float4 w4 = *reinterpret_cast<const float4*>(sws + nl);
+                    const v4i a = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    const v4i f = v4i{__float_as_int(epilogue(a[0], w4.x, xs)), __float_as_int(epilogue(a[1], w4.y, xs)),
+                                      __float_as_int(epilogue(a[2], w4.z, xs)), __float_as_int(epilogue(a[3], w4.w, xs))};
+                    *reinterpret_cast<v4i*>(ring + tl * 512 + 16 * (g4 ^ (tl & 31))) = split ? a : f;
+                }
+            }
         }
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < kPieces / (64 * NW); ++u) {
             const int idx = (int)threadIdx.x + 64 * NW * u;
             const int tl = idx >> 5, g4 = idx & 31;
-            const int t = t0 + tl, n = n0 + 128 * h + 4 * g4;
+            const int rr = 4 * g4;
+            const int t = t0 + tl, n = n0 + 128 * (rr >> 6) + 64 * h + (rr & 63);
             if (t >= P.M || n >= P.N) continue;
             const v4i val = *reinterpret_cast<const v4i*>(ring + tl * 512 + 16 * (g4 ^ (tl & 31)));
             if (split) {
@@ -114,7 +119,12 @@ __device__ __forceinline__ void tiled_store(const GemmProb& P, int8_t* ring, flo
                     }
             }
         }
-        if (h == 0) __syncthreads();                     // pass 1 overwrites the ring
+        if (h == 0) {
+            // pass 1 overwrites the ring once every wave's LDS reads of pass 0
+            // are done; the pass's global stores need not have completed
+            wait_lgkmcnt0();
+            stage_barrier();
+        }
     }
 }
 
