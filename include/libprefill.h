@@ -324,6 +324,10 @@ PF_API size_t pf_moe_chunk_workspace(const pf_moe* moe, int64_t T);
  *     (token, expert) row, y_e = down(hq);
  *   out[t] = +0 then, over the selected experts in ascending id,
  *     out[t][j] = fl(out[t][j] + fl(weights_e * y_e[j])).
+ * With the environment variable PF_MOE_FUSED=1 and hidden and inter each 512,
+ * 1024 or 2048, gate/up, quantise(r) and down run as one launch with one
+ * workgroup per expert ("Red Lite dev24", Scope boundary); the outputs are
+ * identical.
  * ids [T][top_k] int32, weights [T][top_k] f32, out [T][H] f32.
  * Limits: T * top_k <= 65536, E <= 1024, top_k <= 32, T <= 16384. */
 PF_API pf_status pf_moe_chunk(const pf_moe* moe, const float* x, int64_t T, int32_t* ids,

@@ -399,6 +399,14 @@ bool per_token_mode()
     return v && v[0] == '0' && v[1] == '\0';
 }
 
+// PF_MOE_FUSED=1: the experts of pf_moe_chunk as one fused launch (measured a
+// little slower than the three launches it replaces, so not the default).
+bool moe_fused_mode()
+{
+    const char* v = std::getenv("PF_MOE_FUSED");
+    return v && v[0] == '1' && v[1] == '\0';
+}
+
 // ---------------------------------------------------------------------------
 // MoE workspace layout.
 struct MoeLayout {
@@ -1794,16 +1802,20 @@ pf_status pf_moe_chunk(const pf_moe* moe, const float* x, int64_t T, int32_t* id
         gu.ldx = H; gu.ldy = I; gu.N = (int)I; gu.K = (int)H; gu.E = Ei;
         gu.tiles_n = (int)((I + 63) / 64);
         gu.act = (int)moe->activation;
-        st = launched(launch_expert(gu, s));
-        if (!st) st = launched(launch_quantize(r, I, Ti * ki, (int)I, hq, hs, s));
-        if (st) return st;
         ExpertArgs dn;
         std::memset(&dn, 0, sizeof(dn));
         dn.W0 = moe->W_down; dn.s0 = moe->s_down;
         dn.off = off; dn.gather = nullptr; dn.X = hq; dn.xs = hs; dn.Y = ypair;
         dn.ldx = I; dn.ldy = H; dn.N = (int)H; dn.K = (int)I; dn.E = Ei;
         dn.tiles_n = (int)((H + 63) / 64);
-        st = launched(launch_expert(dn, s));
+        if (moe_fused_mode() && expert_fused_shape(H, I)) {
+            // gate/up, quantise(r) and down in one launch, one workgroup per expert
+            st = launched(launch_expert_fused(gu, dn, s));
+        } else {
+            st = launched(launch_expert(gu, s));
+            if (!st) st = launched(launch_quantize(r, I, Ti * ki, (int)I, hq, hs, s));
+            if (!st) st = launched(launch_expert(dn, s));
+        }
         if (!st) st = launched(launch_combine(ypair, comb_row, comb_w, Ti, ki, (int)H, out, s));
         return st;
     } catch (...) {

@@ -203,6 +203,11 @@ hipError_t launch_softmax_topk(const float* logits, int E, int T, int k, int ren
 hipError_t launch_group(const int* ids, const float* w, int T, int k, int E, int* off,
                         int* pair_tok, int* comb_row, float* comb_w, hipStream_t s);
 hipError_t launch_expert(const ExpertArgs& a, hipStream_t s);
+// gate/up, the per-row quantisation of r and down of every expert in one
+// launch (one workgroup per expert); G.Y receives r, Dn.Y the pairs' outputs.
+// For hidden and inter sizes of 512, 1024 or 2048 (expert_fused_shape).
+bool expert_fused_shape(int64_t H, int64_t I);
+hipError_t launch_expert_fused(const ExpertArgs& G, const ExpertArgs& Dn, hipStream_t s);
 hipError_t launch_combine(const float* ypair, const int* comb_row, const float* comb_w, int T,
                           int k, int H, float* out, hipStream_t s);
 hipError_t launch_expf(const float* x, int64_t n, float* y, hipStream_t s);

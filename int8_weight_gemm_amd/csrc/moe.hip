@@ -619,6 +619,262 @@ __global__ __launch_bounds__(256) void k_expert_stream(ExpertArgs A)
     }
 }
 
+// ---------------------------------------------------------------------------
+// The whole expert pipeline in one workgroup per expert ("Red Lite dev24",
+// Scope boundary: the gate/up/down expert kernel).  Over each group of up to
+// 32 of the expert's (token, expert) pairs: gate/up over every 64-row band
+// (r = fl(g u), or fl(silu(g) u), to the pairs' rows of G.Y, and each row's
+// |r| maximum into LDS by integer atomics on its binary32 bits, exact for
+// non-negative values); then the rows' codes, quantise(r) per pair row with
+// the same arithmetic as k_quantize_rows, written straight into LDS as the
+// down product's B fragments; then down over every band of 64 RBD rows to the
+// pairs' rows of Dn.Y.  r is read back by the workgroup that wrote it, and
+// neither the quantisation nor down waits for another launch.  Each wave
+// streams its weight rows into registers D fragments ahead, across band
+// boundaries, as k_expert_stream does within one band.
+template <int KBG, int KBD, bool kSilu>
+__global__ __launch_bounds__(256) void k_expert_fused(ExpertArgs G, ExpertArgs Dn)
+{
+    constexpr int DG = 8, DD = 16;                // fragments ahead: gate/up, down
+    constexpr int RBD = KBD == 32 ? 2 : 4;        // down row blocks of 16 per wave and band
+    constexpr int NFG = KBG, NFD = RBD * KBD;     // fragments per wave and band
+    static_assert(NFG % DG == 0 && NFD % DD == 0, "ring slots the same in every band");
+    constexpr int KX = KBG > KBD ? KBG : KBD;
+    __shared__ __attribute__((aligned(16))) int8_t xl[2 * KX * 1024];
+    __shared__ int rows[32];
+    __shared__ unsigned int rmax[32];
+    __shared__ float rsc[32];
+    const int e = blockIdx.x;
+    const int p0 = G.off[e], p1 = G.off[e + 1];
+    if (p0 == p1) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int koff = (lane >> 4) << 4;
+    const int I = G.N, H = Dn.N;                  // gate/up rows (K = H); down rows (K = I)
+    const int tiles_g = (I + 63) / 64, tiles_d = (H + 64 * RBD - 1) / (64 * RBD);
+    const int8_t* wg = G.W0 + (int64_t)e * I * H + koff;
+    const int8_t* wu = G.W1 + (int64_t)e * I * H + koff;
+    const int8_t* wd = Dn.W0 + (int64_t)e * H * I + koff;
+    auto gfrag = [&](const int8_t* w, int tn, int kb) {   // band tn, k-block kb (16 rows per wave)
+        const int row = min(tn * 64 + wave * 16 + (lane & 15), I - 1);
+        return ld16(w + (int64_t)row * H + kb * 64);
+    };
+    auto dfrag = [&](int tn, int f) {                    // band tn, fragment (rb, kb)
+        const int rb = f / KBD, kb = f % KBD;
+        const int row = min(tn * 64 * RBD + wave * 16 * RBD + rb * 16 + (lane & 15), H - 1);
+        return ld16(wd + (int64_t)row * I + kb * 64);
+    };
+
+    for (int g0 = p0; g0 < p1; g0 += 32) {
+        const int gm = min(32, p1 - g0);
+        __syncthreads();                           // the previous group's LDS reads are done
+        if (threadIdx.x < 32) {
+            rows[threadIdx.x] = (int)threadIdx.x < gm ? G.gather[g0 + threadIdx.x] : -1;
+            rmax[threadIdx.x] = 0u;
+        }
+        __syncthreads();
+        float xsv[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const int j = tb * 16 + (lane & 15);
+            xsv[tb] = G.xs[rows[j] >= 0 ? rows[j] : rows[0]];
+        }
+        // token fragments (tb, kb) at (tb * KBG + kb) KB, loaded into registers,
+        // then the first weight fragments, so both are in flight together
+        v4i ring[DG][2];
+        {
+            v4i xv[2 * KBG / 4];
+            const int rl = rows[lane & 15], rh = rows[16 + (lane & 15)];
+            const int8_t* x0 = G.X + (int64_t)(rl >= 0 ? rl : rows[0]) * G.ldx + koff;
+            const int8_t* x1 = G.X + (int64_t)(rh >= 0 ? rh : rows[0]) * G.ldx + koff;
+#pragma unroll
+            for (int i = 0; i < 2 * KBG / 4; ++i) {
+                const int f = wave + 4 * i;
+                xv[i] = ld16(f < KBG ? x0 + (int64_t)f * 64 : x1 + (int64_t)(f - KBG) * 64);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int f = 0; f < DG; ++f) {
+                ring[f][0] = gfrag(wg, 0, f);
+                ring[f][1] = gfrag(wu, 0, f);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 2 * KBG / 4; ++i) st16(xl + (wave + 4 * i) * 1024 + lane * 16, xv[i]);
+            __builtin_amdgcn_s_waitcnt(0xC07F);    // LDS writes done, the loads stay in flight
+            stage_barrier();
+        }
+        // gate/up, band by band
+        for (int tn = 0; tn < tiles_g; ++tn) {
+            const int nr = tn * 64 + wave * 16 + ((lane >> 4) << 2);
+            float ws0[4], ws1[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = min(nr + q, I - 1);
+                ws0[q] = G.s0[(int64_t)e * I + n];
+                ws1[q] = G.s1[(int64_t)e * I + n];
+            }
+            v4i acc[2][2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) acc[m][0] = acc[m][1] = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int f = 0; f < NFG; ++f) {
+                const v4i b0 = *reinterpret_cast<const v4i*>(xl + f * 1024 + lane * 16);
+                const v4i b1 = *reinterpret_cast<const v4i*>(xl + (KBG + f) * 1024 + lane * 16);
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    acc[m][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ring[f % DG][m], b0, acc[m][0], 0, 0, 0);
+                    acc[m][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ring[f % DG][m], b1, acc[m][1], 0, 0, 0);
+                }
+                if (f + DG < NFG) {
+                    ring[f % DG][0] = gfrag(wg, tn, f + DG);
+                    ring[f % DG][1] = gfrag(wu, tn, f + DG);
+                } else if (tn + 1 < tiles_g) {             // the next band's first fragments
+                    ring[f % DG][0] = gfrag(wg, tn + 1, f + DG - NFG);
+                    ring[f % DG][1] = gfrag(wu, tn + 1, f + DG - NFG);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // acc[m][tb][q]: row nr + q, pair tb * 16 + (lane & 15)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                const int j = tb * 16 + (lane & 15);
+                float4 v;
+                float* vp = &v.x;
+                float m = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float g = epilogue(acc[0][tb][q], ws0[q], xsv[tb]);
+                    const float u = epilogue(acc[1][tb][q], ws1[q], xsv[tb]);
+                    vp[q] = (kSilu ? silu_cr(g) : g) * u;
+                    if (nr + q < I) m = fmaxf(m, fabsf(vp[q]));
+                }
+                m = fmaxf(m, __shfl_xor(m, 16));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                if (j < gm) {
+                    float* yrow = G.Y + (int64_t)(g0 + j) * G.ldy;
+                    if (nr + 3 < I) {
+                        *reinterpret_cast<float4*>(yrow + nr) = v;
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 3; ++q)
+                            if (nr + q < I) yrow[nr + q] = vp[q];
+                    }
+                    if ((lane >> 4) == 0) atomicMax(&rmax[j], __float_as_uint(m));
+                }
+            }
+        }
+        __syncthreads();                           // r in memory, the row maxima in LDS
+        if (threadIdx.x < 32) rsc[threadIdx.x] = __uint_as_float(rmax[threadIdx.x]) / 127.0f;
+        __syncthreads();
+        // the codes: fragment (tb, kb) at (tb * KBD + kb) KB; lane l holds pair
+        // tb * 16 + (l & 15), bytes (l >> 4) * 16 .. + 15 of k-block kb
+#pragma unroll
+        for (int i = 0; i < 2 * KBD / 4; ++i) {
+            const int f = wave + 4 * i;
+            const int tb = f / KBD, kb = f % KBD;
+            const int j = tb * 16 + (lane & 15);
+            v4i packed = v4i{0, 0, 0, 0};
+            const float s = j < gm ? rsc[j] : 0.0f;
+            if (s != 0.0f) {
+                const float4* src =
+                    reinterpret_cast<const float4*>(G.Y + (int64_t)(g0 + j) * G.ldy + kb * 64 + koff);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float4 x = src[w];
+                    packed[w] = (quant_code(x.x, s) & 0xff) | ((quant_code(x.y, s) & 0xff) << 8) |
+                                ((quant_code(x.z, s) & 0xff) << 16) | ((quant_code(x.w, s) & 0xff) << 24);
+                }
+            }
+            st16(xl + f * 1024 + lane * 16, packed);
+        }
+        float xsd[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) xsd[tb] = rsc[tb * 16 + (lane & 15)];
+        // the first down fragments travel across the barrier
+        v4i dring[DD];
+#pragma unroll
+        for (int f = 0; f < DD; ++f) dring[f] = dfrag(0, f);
+        __builtin_amdgcn_s_waitcnt(0xC07F);        // the codes are in LDS
+        stage_barrier();
+        // down, band by band
+        for (int tn = 0; tn < tiles_d; ++tn) {
+            const int r0 = tn * 64 * RBD + wave * 16 * RBD;
+            float ws[RBD][4];
+#pragma unroll
+            for (int rb = 0; rb < RBD; ++rb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    ws[rb][q] = Dn.s0[(int64_t)e * H + min(r0 + rb * 16 + ((lane >> 4) << 2) + q, H - 1)];
+            v4i acc[2];
+#pragma unroll
+            for (int f = 0; f < NFD; ++f) {
+                const int rb = f / KBD, kb = f % KBD;
+                if (kb == 0) acc[0] = acc[1] = v4i{0, 0, 0, 0};
+                const v4i b0 = *reinterpret_cast<const v4i*>(xl + kb * 1024 + lane * 16);
+                const v4i b1 = *reinterpret_cast<const v4i*>(xl + (KBD + kb) * 1024 + lane * 16);
+                acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(dring[f % DD], b0, acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(dring[f % DD], b1, acc[1], 0, 0, 0);
+                if (f + DD < NFD) dring[f % DD] = dfrag(tn, f + DD);
+                else if (tn + 1 < tiles_d) dring[f % DD] = dfrag(tn + 1, f + DD - NFD);
+                __builtin_amdgcn_sched_barrier(0);
+                if (kb == KBD - 1) {
+                    const int nr = r0 + rb * 16 + ((lane >> 4) << 2);
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb) {
+                        const int j = tb * 16 + (lane & 15);
+                        if (j >= gm) continue;
+                        float* yrow = Dn.Y + (int64_t)(g0 + j) * Dn.ldy;
+                        float4 v;
+                        float* vp = &v.x;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) vp[q] = epilogue(acc[tb][q], ws[rb][q], xsd[tb]);
+                        if (nr + 3 < H) {
+                            *reinterpret_cast<float4*>(yrow + nr) = v;
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < 3; ++q)
+                                if (nr + q < H) yrow[nr + q] = vp[q];
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+bool expert_fused_shape(int64_t H, int64_t I)
+{
+    auto ok = [](int64_t k) { return k == 512 || k == 1024 || k == 2048; };
+    return ok(H) && ok(I);
+}
+
+template <int KBG, bool kSilu>
+static void fused_for_kbd(int kbd, dim3 g, hipStream_t s, const ExpertArgs& G, const ExpertArgs& Dn)
+{
+    const dim3 b(256);
+    if (kbd == 8) PF_LAUNCH((k_expert_fused<KBG, 8, kSilu>), g, b, 0, s, G, Dn);
+    else if (kbd == 16) PF_LAUNCH((k_expert_fused<KBG, 16, kSilu>), g, b, 0, s, G, Dn);
+    else PF_LAUNCH((k_expert_fused<KBG, 32, kSilu>), g, b, 0, s, G, Dn);
+}
+
+template <bool kSilu>
+static void fused_for_kbg(int kbg, int kbd, dim3 g, hipStream_t s, const ExpertArgs& G, const ExpertArgs& Dn)
+{
+    if (kbg == 8) fused_for_kbd<8, kSilu>(kbd, g, s, G, Dn);
+    else if (kbg == 16) fused_for_kbd<16, kSilu>(kbd, g, s, G, Dn);
+    else fused_for_kbd<32, kSilu>(kbd, g, s, G, Dn);
+}
+
+hipError_t launch_expert_fused(const ExpertArgs& G, const ExpertArgs& Dn, hipStream_t s)
+{
+    if (!expert_fused_shape(G.K, G.N) || Dn.K != G.N || Dn.N != G.K || !G.W1 || !G.gather)
+        return hipErrorInvalidValue;
+    const dim3 g(G.E);
+    if (G.act) fused_for_kbg<true>(G.K / 64, G.N / 64, g, s, G, Dn);
+    else fused_for_kbg<false>(G.K / 64, G.N / 64, g, s, G, Dn);
+    return hipGetLastError();
+}
+
 // The streaming form for K of 512, 1024 or 2048 and 16-byte aligned output
 // rows; the piecewise form otherwise.
 hipError_t launch_expert(const ExpertArgs& a, hipStream_t s)

@@ -128,3 +128,30 @@ def test_expf_cr_positive_domain():
             np.testing.assert_array_equal(g[close], oracle.expf_cr(x[close]))
     extra = np.float32([89.5, 100.0, 1e30, np.inf, 88.72283, 88.72284])
     np.testing.assert_array_equal(host(pf.expf_cr(dev(extra))), oracle.expf_cr(extra))
+
+
+@pytest.fixture
+def fused_experts(monkeypatch):
+    """PF_MOE_FUSED=1: gate/up, quantise(r) and down as one launch."""
+    monkeypatch.setenv("PF_MOE_FUSED", "1")
+
+
+# the fused expert kernel (hidden and inter of 512, 1024 or 2048): groups of up
+# to 32 pairs (E = 8, top-2 of 150 tokens: over 32 per expert), both orders of
+# H and I, gated SiLU, and an all-zero token (its r rows are zero: scale 0)
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("E,k,H,I,T", [(16, 4, 512, 1024, 70), (8, 2, 1024, 512, 150),
+                                       (4, 1, 2048, 2048, 33), (32, 4, 2048, 512, 64)])
+def test_moe_fused_experts_match_oracle(fused_experts, act, E, k, H, I, T):
+    say(f"fused experts E={E} k={k} H={H} I={I} T={T} act={act}")
+    m = prefill_inputs.moe(E, k, H, I, T, seed=400 + E + T)
+    m["activation"] = act
+    x = m["x"].copy()
+    x[2] = 0.0
+    check_moe(m, x)
+
+
+def test_moe512_fused_experts_match_oracle(fused_experts):
+    say("moe512 with the fused expert kernel")
+    m = prefill_inputs.workload("moe512")
+    check_moe(m, m["x"])
