@@ -21,8 +21,9 @@
 //  * workgroups on one XCD (blockIdx % 8) take consecutive tiles, and the token
 //    tiles of one band of weight rows are consecutive, so the band is fetched
 //    from HBM once into that XCD's L2 and shared.
-// Epilogue: y[t][n] = fl(fl(acc) * fl(ws[n] * xs[t])), written through LDS as
-// 256-byte runs of token rows; split products write int32 partials instead.
+// Epilogue: y[t][n] = fl(fl(acc) * fl(ws[n] * xs[t])), stored from the
+// accumulators as whole 128-byte lines; split products write int32 partials
+// instead.
 #include "device.hpp"
 #include "kernels.hpp"
 #include "lds_dma.hpp"
@@ -33,98 +34,95 @@ namespace pf {
 // Waves per tiled workgroup.
 constexpr int kTiledWaves = 8;
 
-// The epilogue of a tile: lane l, register 4 q + r of a 32 x 32 block holds
-// token l % 32, row 8 q + 4 (l / 32) + r.  Split: this split's int32
-// partials; unsplit: y = fl(fl(acc) * fl(ws * xs)) with the tile's scales
-// staged once in LDS.  The tile leaves through the (now idle) ring in two
-// passes of 128 rows; in pass h every wave writes its row blocks 2 h and
-// 2 h + 1 (rows 128 wn + 64 h .. + 63), so all the waves work in both passes
-// (passes by row half, which left half the waves idle, took 12.9 against
-// 10.3 us per tile).  LDS row of token u: pass row rr = 64 wn + 32 (i - 2 h) +
-// 8 q + 4 (l / 32) + r, its 16-byte piece g = rr / 4 at 512 u + 16 (g ^ (u % 32));
-// pass row rr is weight row n0 + 128 (rr / 64) + 64 h + rr % 64.  Then every
-// thread stores 16-byte pieces of two 256-byte row runs per token, 16 lanes
-// per run.  (Each lane storing its own 16-byte pieces, 64 tokens per
-// instruction, cost ~20% of the 7B prompt's time.)
+// The epilogue of a tile.  The MFMAs take the tokens as their first operand
+// and the weights as their second, so a 32 x 32 accumulator block is indexed
+// [token][row]: lane l, register 4 q + r holds token 8 q + 4 (l / 32) + r of
+// the block and weight row l % 32.  Output rows are token-major with the
+// weight rows contiguous, so each register goes out as one 4-byte store per
+// lane that fills two whole 128-byte lines (32 consecutive rows of two
+// tokens), straight from the accumulators: no LDS, no barrier.  (Through LDS
+// as 256-byte runs, with the weight rows as the first operand, a 256 x 256
+// tile took ~10.3 us to leave.)  Split: this split's int32 partials; unsplit:
+// y = fl(fl(acc) * fl(ws * xs)).
 template <int WJ, int NW>
-__device__ __forceinline__ void tiled_store(const GemmProb& P, int8_t* ring, float* sws, float* sxs, int n0, int t0,
-                                            int kidx, v16i (&acc)[4][2 * WJ / (NW / 2)], int wn, int wm, int lane)
+__device__ __forceinline__ void tiled_store(const GemmProb& P, int n0, int t0, int kidx,
+                                            v16i (&acc)[4][2 * WJ / (NW / 2)])
 {
     constexpr int JB = 2 * WJ / (NW / 2);
-    const int lrow = lane & 31;
-    const bool split = P.splits > 1;
-    int* const part = split ? P.acc + (int64_t)kidx * P.acc_split : nullptr;
-    if (!split) {
-        const int t = (int)threadIdx.x;
-        if (t < 256) sws[t] = P.ws[min(n0 + t, P.N - 1)];
-        if (t < 64 * WJ) sxs[t] = P.xs[min(t0 + t, P.M - 1)];
-    }
-    __syncthreads();                                     // every wave is done with the ring
-    const bool vec = split ? ((P.acc_ld & 3) == 0 && (P.acc_split & 3) == 0 && ((uintptr_t)P.acc & 15) == 0)
-                           : (((uintptr_t)P.Y & 15) == 0 && (P.ldy & 3) == 0 &&
-                              (!P.Y2 || (((uintptr_t)P.Y2 & 15) == 0 && (P.ldy2 & 3) == 0)));
-    constexpr int kPieces = 64 * WJ * 32;                // 16-byte pieces per pass
+    const bool is_split = P.splits > 1;
+    // the lane's place, derived here from the thread index rather than kept
+    // live through the main loop
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int col = tid & 31, hi = (tid >> 5) & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nw = n0 + 128 * (wave >> 2);               // the wave's first weight row
+    const int tw = t0 + 32 * JB * (wave & 3);            // the wave's first token
+    // element e of block (i, j): token tw + 32 j + 8 (e / 4) + 4 hi + e % 4,
+    // row nw + 32 i + col.  A full tile (no output past M or N, no second
+    // copy) takes its scales and stores at constant offsets from one address.
+    const bool full = tw + 32 * JB <= P.M && nw + 128 <= P.N && (is_split || !P.Y2);
+    auto tile = [&](auto full_c, auto split_c) {
+        constexpr bool F = decltype(full_c)::value, split = decltype(split_c)::value;
+        const float* const wp = P.ws + nw + col;
+        const float* const xp = P.xs + tw + 4 * hi;
+        float ws[4];
+        if constexpr (!split) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-            const int i = 2 * h + ii;
-#pragma unroll
-            for (int j = 0; j < JB; ++j) {
-                const int tl = wm * 32 * JB + 32 * j + lrow;         // token in the tile
-                const float xs = sxs[tl];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int g4 = 16 * wn + 8 * ii + 2 * q + (lane >> 5);
-                    const int nl = 128 * wn + 32 * i + 8 * q + 4 * (lane >> 5);   // row in the tile
-                    const float4 w4 = *reinterpret_cast<const float4*>(sws + nl);
-                    const v4i a = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    const v4i f = v4i{__float_as_int(epilogue(a[0], w4.x, xs)), __float_as_int(epilogue(a[1], w4.y, xs)),
-                                      __float_as_int(epilogue(a[2], w4.z, xs)), __float_as_int(epilogue(a[3], w4.w, xs))};
-                    *reinterpret_cast<v4i*>(ring + tl * 512 + 16 * (g4 ^ (tl & 31))) = split ? a : f;
-                }
-            }
+            for (int i = 0; i < 4; ++i) ws[i] = F ? wp[32 * i] : P.ws[min(nw + 32 * i + col, P.N - 1)];
         }
-        __syncthreads();
+        int* const out = split ? P.acc + (int64_t)kidx * P.acc_split : reinterpret_cast<int*>(P.Y);
+        const int64_t ld = split ? P.acc_ld : P.ldy;
+        int* const ow = out + (int64_t)(tw + 4 * hi) * ld + nw + col;
+        // every scale is loaded before the first store: the memory counter
+        // also counts stores, so a later load's wait would wait for them
+        float xs[JB][16];
+        if constexpr (!split) {
 #pragma unroll
-        for (int u = 0; u < kPieces / (64 * NW); ++u) {
-            const int idx = (int)threadIdx.x + 64 * NW * u;
-            const int tl = idx >> 5, g4 = idx & 31;
-            const int rr = 4 * g4;
-            const int t = t0 + tl, n = n0 + 128 * (rr >> 6) + 64 * h + (rr & 63);
-            if (t >= P.M || n >= P.N) continue;
-            const v4i val = *reinterpret_cast<const v4i*>(ring + tl * 512 + 16 * (g4 ^ (tl & 31)));
-            if (split) {
-                int* p = part + (int64_t)t * P.acc_ld + n;
-                if (vec && n + 3 < P.N) {
-                    *reinterpret_cast<v4i*>(p) = val;
+            for (int j = 0; j < JB; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int dt = 32 * j + 8 * (e >> 2) + (e & 3);
+                    xs[j][e] = F ? xp[dt] : P.xs[min(tw + 4 * hi + dt, P.M - 1)];
+                }
+        }
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int dt = 32 * j + 8 * (e >> 2) + (e & 3);
+                const int t = tw + 4 * hi + dt;
+                int* const o = ow + (int64_t)dt * ld;
+                int v[4];
+                if constexpr (split) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = acc[i][j][e];
                 } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n + r < P.N) p[r] = val[r];
+                    for (int i = 0; i < 4; ++i) v[i] = __float_as_int(epilogue(acc[i][j][e], ws[i], xs[j][e]));
                 }
-                continue;
-            }
-            float* y = P.Y + (int64_t)t * P.ldy + n;
-            float* y2 = P.Y2 ? P.Y2 + (int64_t)t * P.ldy2 + n : nullptr;
-            if (vec && n + 3 < P.N) {
-                *reinterpret_cast<v4i*>(y) = val;
-                if (y2) *reinterpret_cast<v4i*>(y2) = val;
-            } else {
+                if constexpr (F) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (n + r < P.N) {
-                        y[r] = __int_as_float(val[r]);
-                        if (y2) y2[r] = __int_as_float(val[r]);
+                    for (int i = 0; i < 4; ++i) o[32 * i] = v[i];
+                } else {
+                    if (t >= P.M) continue;
+                    int* const o2 = (!split && P.Y2) ? reinterpret_cast<int*>(P.Y2) + (int64_t)t * P.ldy2 + nw + col : nullptr;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (nw + 32 * i + col >= P.N) continue;
+                        o[32 * i] = v[i];
+                        if (o2) o2[32 * i] = v[i];
                     }
+                }
             }
         }
-        if (h == 0) {
-            // pass 1 overwrites the ring once every wave's LDS reads of pass 0
-            // are done; the pass's global stores need not have completed
-            wait_lgkmcnt0();
-            stage_barrier();
-        }
+    };
+    if (is_split) {
+        if (full) tile(std::true_type{}, std::true_type{});
+        else tile(std::false_type{}, std::true_type{});
+    } else {
+        if (full) tile(std::true_type{}, std::false_type{});
+        else tile(std::false_type{}, std::false_type{});
     }
 }
 
@@ -153,7 +151,8 @@ struct KbOps {
 };
 
 #define PF_RD(dst, adr, off) "ds_read_b128 %[" #dst "], %[" #adr "] offset:" #off "\n"
-#define PF_MF(c, a, b) "v_mfma_i32_32x32x32_i8 %[" #c "], %[" #a "], %[" #b "], %[" #c "]\n"
+// the tokens (b) are the first operand, so the result block is [token][row]
+#define PF_MF(c, a, b) "v_mfma_i32_32x32x32_i8 %[" #c "], %[" #b "], %[" #a "], %[" #c "]\n"
 
 // kb_half<JB, KH>: n's k half KH <- the operands at ra (row block i at
 // + 4096 i) and rb (token block j at + 4096 j), acc += the products of c's k
@@ -308,8 +307,7 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
     constexpr int kRing = NSW * kWst + NST * kTst;
     static_assert(kRing <= 160 * 1024, "LDS");
     static_assert(ka + (NST - 1) * (ka + kb) <= 63, "vmcnt range");
-    static_assert(64 * WJ * 512 + 2048 <= kRing, "a pass and the scales fit in the ring");
-    __shared__ __attribute__((aligned(16))) int8_t ring[kRing];
+        __shared__ __attribute__((aligned(16))) int8_t ring[kRing];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int tm = local % P.tiles_m, tn = local / P.tiles_m;
@@ -394,11 +392,7 @@ __device__ __forceinline__ void tiled_block(const GemmProb& P, int local, int ki
         kb_last<JB>(c1, acc);
     }
     wait_vmcnt<0>();                                     // no copy outlives the workgroup's LDS
-    // the scales go into the token ring: every wave's copies have landed and
-    // every wave has read its last operands before any wave writes there
-    __syncthreads();
-    float* sws = reinterpret_cast<float*>(ring + 64 * WJ * 512);
-    tiled_store<WJ, NW>(P, ring, sws, sws + 256, n0, t0, kidx, acc, wn, wm, lane);
+    tiled_store<WJ, NW>(P, n0, t0, kidx, acc);
 }
 
 // Workgroup b -> tile (b % 8) * per_xcd + b / 8: the workgroups of one XCD take
