@@ -168,7 +168,8 @@ def test_tiled_k_blocks_around_ring_depth(M, K):
 
 @pytest.mark.parametrize("M", [100, 200])
 def test_tiled_unaligned_output(M):
-    """An output that is only 4-byte aligned takes the scalar stores."""
+    """An output that is only 4-byte aligned (the epilogue's 4-byte stores need no
+    more) and whose rows are not a multiple of four floats apart."""
     N, K = 300, 512
     W, ws, q, s = _proj(N, K, M, 700 + M)
     buf = torch.full((M * N + 1,), -1.0, dtype=torch.float32, device="cuda")
