@@ -79,6 +79,8 @@ def test_gemm_rejects_bad_k_and_alignment():
     assert lib.pf_gemm_i8_chunk(FAKE, FAKE, 64, 128, FAKE, FAKE, 0, P(0x20000), None, 0, None) == pf.PF_OK
     # a weight matrix or token chunk of 2^32 bytes or more (32-bit offsets in the kernels)
     assert lib.pf_gemm_i8_chunk(FAKE, FAKE, 1 << 20, 4096, FAKE, FAKE, 4, P(0x20000), None, 0, None) == pf.PF_EINVAL
+    # exactly 2^32 bytes at the largest K (one row fewer is the largest product taken)
+    assert lib.pf_gemm_i8_chunk(FAKE, FAKE, 32768, 131072, FAKE, FAKE, 4, P(0x20000), None, 0, None) == pf.PF_EINVAL
     assert lib.pf_gemm_i8_chunk(FAKE, FAKE, 64, 4096, FAKE, FAKE, 1 << 20, P(0x20000), None, 0, None) == pf.PF_EINVAL
 
 

@@ -277,6 +277,33 @@ def test_large_tiled_products_equal_per_token_gemvs(N, K, M):
     np.testing.assert_array_equal(host(y)[:, rows], ref)
 
 
+@pytest.mark.parametrize("M", [1, 32, 100])
+def test_largest_accepted_product(M):
+    """The largest weight matrix the entry points take: K at its maximum (131072)
+    and N * K one row short of 2^32 bytes (the tiled copies address a matrix by
+    32-bit offsets), through the GEMV (M = 1), the skinny path (32) and the tiled
+    path (100); sampled rows, the last included, equal the oracle's.  (One row
+    more is refused before any launch: test_abi.)"""
+    K = 131072
+    N = (1 << 32) // K - 1
+    say("largest product", N, K, M)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(M)
+    W = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+    ws = torch.rand(N, device="cuda", generator=g) * 0.009 + 0.001
+    q, s = pf.quantize_act(torch.randn(M, K, device="cuda", generator=g))
+    if M == 1:
+        y = pf.gemv_i8(W, ws, q[0].contiguous(), s[:1].contiguous())[None, :]
+    else:
+        wsp = pf.workspace(max(1, pf.gemm_i8_chunk_workspace(N, K, M)))
+        y = pf.gemm_i8_chunk(W, ws, q, s, ws=wsp)
+    rows = np.array([0, 1, 4097, N // 2, N - 2, N - 1])
+    ref = oracle.linear(host(W[torch.from_numpy(rows).cuda()]), host(ws)[rows], host(q), host(s))
+    np.testing.assert_array_equal(host(y)[:, rows], ref)
+    del W
+    torch.cuda.empty_cache()
+
+
 def test_rejects_bad_arguments_without_launch():
     W = torch.zeros((64, 100), dtype=torch.int8, device="cuda")
     with pytest.raises(pf.PrefillError) as e:
