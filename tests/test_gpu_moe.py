@@ -71,6 +71,15 @@ def test_moe_concentrated_routing():
     check(m)
 
 
+# The limits pf_moe_chunk takes: 1024 experts with top-32 over 2048 tokens
+# (65536 pairs, the most a call may route), and 16384 tokens (the grouping
+# bitmap's largest) with top-4; small experts keep the oracle quick.
+@pytest.mark.parametrize("E,k,T", [(1024, 32, 2048), (16, 4, 16384)])
+def test_moe_at_its_limits(E, k, T):
+    print(f"moe limits E={E} k={k} T={T}", file=sys.stderr, flush=True)
+    check(prefill_inputs.moe(E, k, 64, 64, T, seed=300 + E + k))
+
+
 def test_moe512_matches_oracle():
     print("moe512: 512 experts, top-10, 512 tokens", file=sys.stderr, flush=True)
     m = prefill_inputs.workload("moe512")
