@@ -348,7 +348,10 @@ hipError_t launch_quantize_step(const QuantStep& S, hipStream_t s)
 // Per-token GEMV (M = 1): a workgroup owns 16 weight rows, NW waves of 16 / NW
 // rows each; each lane streams 16-byte pieces of its wave's rows, multiplies
 // with v_dot4_i32_i8 and the wave reduces the int32 sums.  The token's 16-byte
-// pieces are re-read from L1/L2 per row group.
+// pieces are re-read from L1/L2 per row group.  The weights are loaded as
+// non-temporal (each byte is used once per token): 4096 x 4096 kernel 6.2 ->
+// 5.3 us, the 350M stack's per-token mode 219.7 -> 215.7 ms; a copy of the
+// token per workgroup in LDS was slower.
 constexpr int kGemvTile = 16;
 
 template <int NW>
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv(GemmSet set)
         const v4i qv = ld16(P.X + c * 16);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const v4i wv = ld16(wrow[r] + c * 16);
+            const v4i wv = ld16_nt(wrow[r] + c * 16);
             acc[r] = __builtin_amdgcn_sdot4(wv.x, qv.x, acc[r], false);
             acc[r] = __builtin_amdgcn_sdot4(wv.y, qv.y, acc[r], false);
             acc[r] = __builtin_amdgcn_sdot4(wv.z, qv.z, acc[r], false);

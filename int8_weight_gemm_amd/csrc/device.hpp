@@ -19,6 +19,11 @@ constexpr int kWave = 64;
 // One 128-bit load / store.
 __device__ __forceinline__ v4i ld16(const int8_t* p) { return *reinterpret_cast<const v4i*>(p); }
 __device__ __forceinline__ void st16(int8_t* p, v4i v) { *reinterpret_cast<v4i*>(p) = v; }
+// A 128-bit load marked non-temporal: weights streamed once per use.
+__device__ __forceinline__ v4i ld16_nt(const int8_t* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+}
 
 // Epilogue of one output: fl( fl((float)acc) * fl(w_scale * a_scale) ), the
 // scale product taken first.
