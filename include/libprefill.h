@@ -238,7 +238,10 @@ PF_API size_t pf_prefill_stack_workspace(const pf_stack* stack, int64_t chunk);
  *   (b, sb) = quantise(up); down = product with b; the next layer's h = down.
  * x [P][H] f32 -> y [P][H] f32 (the last layer's down).  proj, when not NULL,
  * receives every projection output: proj [L][P][5H + 2F] f32, each row holding
- * q, k, v, o, gate, up, down concatenated.  kv, required when the stack has
+ * q, k, v, o, gate, up, down concatenated.  When NULL, the outputs nothing
+ * reads are computed but not stored: q (unless the attention reads it), k and
+ * v (the attention reads the cache), o, and gate without the gated SiLU; y
+ * and kv are the same, with fewer bytes written.  kv, required when the stack has
  * n_heads > 0 (ignored otherwise), receives the K/V cache: kv [L][2][P][H] f32,
  * k of layer l and position t at kv[l][0][t], v at kv[l][1][t].  With the environment variable
  * PF_BATCHED_PREFILL=0 the same call runs one GEMV per token and projection

@@ -677,6 +677,22 @@ struct StackRun {
         if (proj) return proj + ((size_t)l * P + (size_t)c * ch) * NT();
         return reinterpret_cast<float*>(slot(c) + lay.proj);
     }
+    // Launch slots whose projection rows nothing reads when the caller keeps
+    // none: q (unless the attention reads it), k and v (the attention reads
+    // the cache), o, and gate without the gated SiLU; up feeds the down
+    // product.  Those rows are not stored (the same bits come out in y and
+    // the cache, with fewer bytes written).
+    unsigned unread_rows(const int* projs, int n) const
+    {
+        if (proj) return 0u;
+        unsigned m = 0;
+        for (int j = 0; j < n; ++j) {
+            const int p = projs[j];
+            const bool read = p == 5 || (p == 4 && st->activation == PF_ACT_SWIGLU) || (p == 0 && attn());
+            if (!read) m |= 1u << j;
+        }
+        return m;
+    }
     int64_t offs(int j) const
     {
         const int64_t o[PF_NPROJ] = {0, H(), 2 * H(), 3 * H(), 4 * H(), 4 * H() + F(), 4 * H() + 2 * F()};
@@ -787,6 +803,7 @@ struct StackRun {
         O.ldx = H();
         O.ldy = NT();
         O.kv_proj[0] = O.kv_proj[1] = -1;
+        O.nostore = proj ? 0u : 1u;                      // o's rows feed nothing further
         double a_bytes = 0, o_bytes = 0;
         for (int64_t c : cs) {
             const int64_t l = step - start(c / ng), c0 = c * ch, M = std::min(ch, P - c0);
@@ -873,6 +890,7 @@ struct StackRun {
         A.kv_proj[0] = attn() ? 1 : -1;
         A.kv_proj[1] = attn() ? 2 : -1;
         A.ldkv = H();
+        A.nostore = unread_rows(projA, nA);
         D.kv_proj[0] = D.kv_proj[1] = -1;
         for (int j = 0; j < nA; ++j) {
             A.rows[j] = (int)rowsA[j];
@@ -1355,6 +1373,9 @@ struct StreamRun {
             A.ldx = H;
             A.ldy = NT();
             A.kv_proj[0] = A.kv_proj[1] = -1;
+            // q, k, v and o feed nothing here, gate only the gated SiLU: their
+            // rows are not stored
+            A.nostore = st->activation == PF_ACT_SWIGLU ? 0x0fu : 0x1fu;
             for (int j = 0; j < 6; ++j) {
                 A.rows[j] = (int)rowsA[j];
                 A.yoff[j] = (int)offs(j);

@@ -92,6 +92,8 @@ struct StackStep {
     int64_t part_stride;  // int32 elements between splits of the partials
     int kv_proj[2];       // projections whose outputs also go to the K / V cache (-1: none)
     int64_t ldkv;         // floats between cache rows
+    unsigned nostore;     // bit j: projection j's rows are not stored (nothing reads them);
+                          // its cache rows still are
 };
 
 // The K or V cache row base of projection j of a pair (null: none).

@@ -34,7 +34,7 @@ __device__ __forceinline__ GemmProb step_prob(const StackStep& S, int bid, int& 
     P.ws = pp.ws[j];
     P.X = pp.X;
     P.xs = pp.xs;
-    P.Y = pp.Y + S.yoff[j];
+    P.Y = ((S.nostore >> j) & 1u) ? nullptr : pp.Y + S.yoff[j];
     P.Y2 = pp.Y2;
     P.ldy2 = S.ldy2;
     if (float* kv = step_kv(S, pp, j)) {
@@ -59,7 +59,7 @@ __device__ __forceinline__ GemmProb step_prob(const StackStep& S, int bid, int& 
 
 __device__ __forceinline__ void store_out(const GemmProb& P, int t, int n, float v)
 {
-    P.Y[(int64_t)t * P.ldy + n] = v;
+    if (P.Y) P.Y[(int64_t)t * P.ldy + n] = v;
     if (P.Y2) P.Y2[(int64_t)t * P.ldy2 + n] = v;
 }
 

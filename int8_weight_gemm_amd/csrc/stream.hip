@@ -565,13 +565,15 @@ __global__ __launch_bounds__(256) void k_gemm_xres(StackStep S, int wg_per_group
                         v.y = epilogue(acc[tb][1], wsl[1], xs);
                         v.z = epilogue(acc[tb][2], wsl[2], xs);
                         v.w = epilogue(acc[tb][3], wsl[3], xs);
-                        float* y = pp.Y + S.yoff[cur.proj] + (int64_t)tok * S.ldy + n;
-                        if (n + 3 < N) {
-                            *reinterpret_cast<float4*>(y) = v;   // rows n..n+3: 16 bytes
-                        } else {
-                            if (n < N) y[0] = v.x;
-                            if (n + 1 < N) y[1] = v.y;
-                            if (n + 2 < N) y[2] = v.z;
+                        if (!((S.nostore >> cur.proj) & 1u)) {
+                            float* y = pp.Y + S.yoff[cur.proj] + (int64_t)tok * S.ldy + n;
+                            if (n + 3 < N) {
+                                *reinterpret_cast<float4*>(y) = v;   // rows n..n+3: 16 bytes
+                            } else {
+                                if (n < N) y[0] = v.x;
+                                if (n + 1 < N) y[1] = v.y;
+                                if (n + 2 < N) y[2] = v.z;
+                            }
                         }
                         float* kvr = step_kv(S, pp, cur.proj);
                         if (pp.Y2 || kvr) {

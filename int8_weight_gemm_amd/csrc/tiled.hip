@@ -58,10 +58,21 @@ __device__ __forceinline__ void tiled_store(const GemmProb& P, int n0, int t0, i
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nw = n0 + 128 * (wave >> 2);               // the wave's first weight row
     const int tw = t0 + 32 * JB * (wave & 3);            // the wave's first token
+    // the outputs: the split's partials, or the rows and their second copy
+    // (without rows to keep, the copy alone; with neither, nothing to store)
+    float* y1 = P.Y;
+    int64_t ld1 = P.ldy;
+    float* y2 = P.Y2;
+    if (!is_split && !y1) {
+        if (!y2) return;
+        y1 = y2;
+        ld1 = P.ldy2;
+        y2 = nullptr;
+    }
     // element e of block (i, j): token tw + 32 j + 8 (e / 4) + 4 hi + e % 4,
     // row nw + 32 i + col.  A full tile (no output past M or N, no second
     // copy) takes its scales and stores at constant offsets from one address.
-    const bool full = tw + 32 * JB <= P.M && nw + 128 <= P.N && (is_split || !P.Y2);
+    const bool full = tw + 32 * JB <= P.M && nw + 128 <= P.N && (is_split || !y2);
     auto tile = [&](auto full_c, auto split_c) {
         constexpr bool F = decltype(full_c)::value, split = decltype(split_c)::value;
         const float* const wp = P.ws + nw + col;
@@ -71,8 +82,8 @@ __device__ __forceinline__ void tiled_store(const GemmProb& P, int n0, int t0, i
 #pragma unroll
             for (int i = 0; i < 4; ++i) ws[i] = F ? wp[32 * i] : P.ws[min(nw + 32 * i + col, P.N - 1)];
         }
-        int* const out = split ? P.acc + (int64_t)kidx * P.acc_split : reinterpret_cast<int*>(P.Y);
-        const int64_t ld = split ? P.acc_ld : P.ldy;
+        int* const out = split ? P.acc + (int64_t)kidx * P.acc_split : reinterpret_cast<int*>(y1);
+        const int64_t ld = split ? P.acc_ld : ld1;
         int* const ow = out + (int64_t)(tw + 4 * hi) * ld + nw + col;
         // every scale is loaded before the first store: the memory counter
         // also counts stores, so a later load's wait would wait for them
@@ -106,7 +117,7 @@ __device__ __forceinline__ void tiled_store(const GemmProb& P, int n0, int t0, i
                     for (int i = 0; i < 4; ++i) o[32 * i] = v[i];
                 } else {
                     if (t >= P.M) continue;
-                    int* const o2 = (!split && P.Y2) ? reinterpret_cast<int*>(P.Y2) + (int64_t)t * P.ldy2 + nw + col : nullptr;
+                    int* const o2 = (!split && y2) ? reinterpret_cast<int*>(y2) + (int64_t)t * P.ldy2 + nw + col : nullptr;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         if (nw + 32 * i + col >= P.N) continue;

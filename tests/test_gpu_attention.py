@@ -30,13 +30,13 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def run(st, n_heads, chunk, act=0, per_token=False, alt=False):
+def run(st, n_heads, chunk, act=0, per_token=False, alt=False, keep_proj=True):
     wd = [[dev(w) for w in wl] for wl in st["weights"]]
     sd = [[dev(s) for s in sl] for sl in st["scales"]]
     altc = ([[w.clone() for w in wl] for wl in wd], [[s.clone() for s in sl] for sl in sd]) if alt else None
     stack = pf.Stack(wd, sd, alt=altc, activation=act, n_heads=n_heads)
     L, P, H = len(wd), st["x"].shape[0], stack.H
-    proj = torch.empty((L, P, 5 * H + 2 * stack.F), dtype=torch.float32, device="cuda")
+    proj = torch.empty((L, P, 5 * H + 2 * stack.F), dtype=torch.float32, device="cuda") if keep_proj else None
     kv = torch.full((L, 2, P, H), float("nan"), dtype=torch.float32, device="cuda")
     if per_token:
         os.environ["PF_BATCHED_PREFILL"] = "0"
@@ -45,7 +45,7 @@ def run(st, n_heads, chunk, act=0, per_token=False, alt=False):
     finally:
         if per_token:
             del os.environ["PF_BATCHED_PREFILL"]
-    return host(y), host(proj), host(kv)
+    return host(y), (host(proj) if keep_proj else None), host(kv)
 
 
 @pytest.fixture(scope="module")
@@ -61,6 +61,17 @@ def test_attention_stack_matches_oracle(small, chunk):
     y, proj, kv = run(st, 4, chunk)
     np.testing.assert_array_equal(kv, kv_ref)
     np.testing.assert_array_equal(proj, proj_ref)
+    np.testing.assert_array_equal(y, y_ref)
+
+
+@pytest.mark.parametrize("chunk", [32, 96, 150])
+def test_attention_without_projection_rows(small, chunk):
+    """No projection rows kept: only q (read by the attention) and up (read by
+    the down product's quantisation) are stored besides the cache; y and the
+    cache are the same."""
+    st, (y_ref, kv_ref, _) = small
+    y, _, kv = run(st, 4, chunk, keep_proj=False)
+    np.testing.assert_array_equal(kv, kv_ref)
     np.testing.assert_array_equal(y, y_ref)
 
 

@@ -52,6 +52,15 @@ def test_stack_swiglu_full_compare(swiglu_stack, chunk):
     assert np.all(np.isfinite(y_ref))
 
 
+@pytest.mark.parametrize("chunk", [32, 96, 200])
+def test_stack_swiglu_without_projection_rows(swiglu_stack, chunk):
+    """No projection rows kept: q, k, v and o are not stored, gate is (the gated
+    SiLU reads it); y is the same."""
+    st, y_ref, _, stack = swiglu_stack
+    y = stack.prefill(dev(st["x"]), chunk, pf.workspace(stack.workspace_bytes(chunk)))
+    np.testing.assert_array_equal(host(y), y_ref)
+
+
 def test_stack_swiglu_per_token_mode(swiglu_stack):
     st, y_ref, _, stack = swiglu_stack
     os.environ["PF_BATCHED_PREFILL"] = "0"
