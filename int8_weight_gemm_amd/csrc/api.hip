@@ -912,7 +912,10 @@ struct StackRun {
             q.splits = sd;
             q.ws = layer(c, l_prev).w_scale[6];
             q.as = reinterpret_cast<const float*>(sl + lay.sb);
-            q.h = rows(c, l_prev) + offs(6);
+            // the rebuilt f32 rows: kept only for the caller's projection rows
+            // (the codes come from registers), or where the quantisation reads
+            // them back (rows of more than 16384 values)
+            q.h = (proj || H() > 16384) ? rows(c, l_prev) + offs(6) : nullptr;
             q.ldh = NT();
             q.y = last ? y + c * ch * H() : nullptr;
         };

@@ -218,7 +218,7 @@ __device__ __forceinline__ void quant_row_regs(const QuantPair& P, int t, int K)
                     }
         }
         const float as = P.as[t];
-        float4* hrow = reinterpret_cast<float4*>(P.h + (int64_t)t * P.ldh);
+        float4* hrow = P.h ? reinterpret_cast<float4*>(P.h + (int64_t)t * P.ldh) : nullptr;
         float* yrow = P.y ? P.y + (int64_t)t * K : nullptr;    // 4-byte aligned only
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -229,7 +229,7 @@ __device__ __forceinline__ void quant_row_regs(const QuantPair& P, int t, int K)
             v[u].z = epilogue(a[u].z, ws[2], as);
             v[u].w = epilogue(a[u].w, ws[3], as);
             if (i < n4) {
-                hrow[i] = v[u];
+                if (hrow) hrow[i] = v[u];
                 if (yrow) {
                     yrow[4 * i] = v[u].x;
                     yrow[4 * i + 1] = v[u].y;

@@ -144,7 +144,8 @@ struct QuantPair {
     int splits;
     const float* ws;      // mode 1: weight-row scales [K]
     const float* as;      // mode 1: token scales [M]
-    float* h;             // mode 1: rebuilt rows [M][ldh]
+    float* h;             // mode 1: rebuilt rows [M][ldh] (null: not stored; rows of at
+                          // most 16384 values only)
     int64_t ldh;
     float* y;             // mode 1: optional copy [M][K]
 };
